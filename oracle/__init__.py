@@ -1,0 +1,229 @@
+"""CPU oracle for the sparse MoE FFN layer forward (ctypes wrapper of ``libmoe_oracle.so``).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It never imports the HIP library and the HIP library
+never imports it. The arithmetic is in ``moe_oracle.cpp``; this file only marshals numpy
+arrays (bf16 tensors are ``uint16`` bit patterns, row-major).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with g++ (OpenMP, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "moe_oracle.h"))
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+               _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = ctypes.CDLL(_LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_D = ctypes.c_double
+
+
+def _declare(L):
+    L.oracle_bf16_from_double.argtypes = [_D]
+    L.oracle_bf16_from_double.restype = ctypes.c_uint16
+    L.oracle_double_from_bf16.argtypes = [ctypes.c_uint16]
+    L.oracle_double_from_bf16.restype = _D
+    L.oracle_router_logits.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I, _P]
+    L.oracle_route_from_logits.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _P]
+    L.oracle_dispatch.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
+    L.oracle_gateup_rows.argtypes = [_I, _I, _I, _D, _P, _P, _P, _P]
+    L.oracle_down_rows.argtypes = [_I, _I, _I, _P, _P, _P]
+    L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P]
+    L.oracle_layer_forward.argtypes = [_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 9 + [_I] + [_P] * 12
+    L.oracle_layer_dense.argtypes = [_I, _I, _I, _I, _I, _D] + [_P] * 11
+    L.oracle_num_threads.restype = _I
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _u16(a):
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def bf16_from_double(v: float) -> int:
+    return int(lib().oracle_bf16_from_double(float(v)))
+
+
+def double_from_bf16(b: int) -> float:
+    return float(lib().oracle_double_from_bf16(int(b)))
+
+
+def bf16_round_array(a: np.ndarray) -> np.ndarray:
+    """Element-wise oracle bf16 rounding of a float64 array (slow; for small arrays)."""
+    f = lib().oracle_bf16_from_double
+    flat = np.asarray(a, dtype=np.float64).ravel()
+    return np.array([f(float(v)) for v in flat], dtype=np.uint16).reshape(np.shape(a))
+
+
+def router_logits(x, wr, bias=None, tokens=None):
+    x, wr = _u16(x), _u16(wr)
+    T, H = x.shape
+    E = wr.shape[0]
+    logits = np.zeros((T, E), dtype=np.float32)
+    tok = None if tokens is None else _i32(tokens)
+    lib().oracle_router_logits(T, H, E, _ptr(x), _ptr(wr), _ptr(_f32(bias)), _ptr(tok),
+                               0 if tok is None else len(tok), _ptr(logits))
+    return logits
+
+
+def route_from_logits(logits, K, scale=1.0, norm_topk=True, want_probs=False):
+    logits = _f32(logits)
+    T, E = logits.shape
+    idx = np.zeros((T, K), dtype=np.int32)
+    w = np.zeros((T, K), dtype=np.float32)
+    probs = np.zeros((T, E), dtype=np.float64) if want_probs else None
+    lib().oracle_route_from_logits(T, E, K, int(bool(norm_topk)), float(scale), _ptr(logits),
+                                   _ptr(idx), _ptr(w), _ptr(probs))
+    return (idx, w, probs) if want_probs else (idx, w)
+
+
+def dispatch(topk_idx, E, capacity=0):
+    topk_idx = _i32(topk_idx)
+    T, K = topk_idx.shape
+    counts = np.zeros(E, dtype=np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int32)
+    r2s = np.zeros(T * K, dtype=np.int32)
+    s2r = np.zeros(T * K, dtype=np.int32)
+    lib().oracle_dispatch(T, K, E, int(capacity), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                          _ptr(r2s), _ptr(s2r))
+    return counts, offsets, r2s, s2r
+
+
+def gateup_rows(x_rows, wg, wu, limit):
+    x_rows, wg, wu = _u16(x_rows), _u16(wg), _u16(wu)
+    n, H = x_rows.shape
+    I = wg.shape[0]
+    h = np.zeros((n, I), dtype=np.uint16)
+    if n:
+        lib().oracle_gateup_rows(n, H, I, float(limit), _ptr(x_rows), _ptr(wg), _ptr(wu), _ptr(h))
+    return h
+
+
+def down_rows(h, wd):
+    h, wd = _u16(h), _u16(wd)
+    n, I = h.shape
+    H = wd.shape[0]
+    y = np.zeros((n, H), dtype=np.uint16)
+    if n:
+        lib().oracle_down_rows(n, H, I, _ptr(h), _ptr(wd), _ptr(y))
+    return y
+
+
+def expert_ffn_rows(x_rows, wg, wu, wd, limit):
+    h = gateup_rows(x_rows, wg, wu, limit)
+    return h, down_rows(h, wd)
+
+
+def combine(topk_w, slot_to_row, y_routed, y_shared=None):
+    topk_w, slot_to_row, y_routed = _f32(topk_w), _i32(slot_to_row), _u16(y_routed)
+    T, K = topk_w.shape
+    H = y_routed.shape[1]
+    out = np.zeros((T, H), dtype=np.uint16)
+    ys = None if y_shared is None else _u16(y_shared)
+    lib().oracle_combine(T, K, H, _ptr(topk_w), _ptr(slot_to_row), _ptr(y_routed), _ptr(ys),
+                         _ptr(out))
+    return out
+
+
+def layer_forward(x, wr, wg, wu, wd, K, *, bias=None, sg=None, su=None, sd=None, scale=1.0,
+                  limit=10.0, capacity=0, norm_topk=True, logits=None):
+    """Sparse evaluation of the whole layer; returns a dict of every intermediate.
+
+    When ``logits`` is given the router projection is skipped and those fp32 logits are used
+    (the "same logits" mode)."""
+    x, wr, wg, wu, wd = _u16(x), _u16(wr), _u16(wg), _u16(wu), _u16(wd)
+    T, H = x.shape
+    E, I = wg.shape[0], wg.shape[1]
+    use_logits = logits is not None
+    lg = _f32(logits).copy() if use_logits else np.zeros((T, E), dtype=np.float32)
+    r = dict(
+        logits=lg,
+        topk_idx=np.zeros((T, K), dtype=np.int32),
+        topk_w=np.zeros((T, K), dtype=np.float32),
+        counts=np.zeros(E, dtype=np.int32),
+        offsets=np.zeros(E + 1, dtype=np.int32),
+        row_to_slot=np.zeros(T * K, dtype=np.int32),
+        slot_to_row=np.zeros(T * K, dtype=np.int32),
+        h_routed=np.zeros((T * K, I), dtype=np.uint16),
+        y_routed=np.zeros((T * K, H), dtype=np.uint16),
+        out=np.zeros((T, H), dtype=np.uint16),
+    )
+    has_shared = sg is not None
+    if has_shared:
+        sg, su, sd = _u16(sg), _u16(su), _u16(sd)
+        r["h_shared"] = np.zeros((T, I), dtype=np.uint16)
+        r["y_shared"] = np.zeros((T, H), dtype=np.uint16)
+    lib().oracle_layer_forward(
+        T, H, E, K, I, int(bool(norm_topk)), float(scale), float(limit), int(capacity),
+        _ptr(x), _ptr(wr), _ptr(_f32(bias)), _ptr(wg), _ptr(wu), _ptr(wd),
+        _ptr(sg), _ptr(su), _ptr(sd), int(use_logits), _ptr(lg),
+        _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+        _ptr(r["row_to_slot"]), _ptr(r["slot_to_row"]), _ptr(r["h_routed"]), _ptr(r["y_routed"]),
+        _ptr(r.get("h_shared")), _ptr(r.get("y_shared")), _ptr(r["out"]))
+    return r
+
+
+def layer_dense(x, wg, wu, wd, topk_idx, topk_w, slot_to_row, *, sg=None, su=None, sd=None,
+                limit=10.0):
+    x, wg, wu, wd = _u16(x), _u16(wg), _u16(wu), _u16(wd)
+    topk_idx, topk_w, slot_to_row = _i32(topk_idx), _f32(topk_w), _i32(slot_to_row)
+    T, H = x.shape
+    E, I = wg.shape[0], wg.shape[1]
+    K = topk_idx.shape[1]
+    out = np.zeros((T, H), dtype=np.uint16)
+    if sg is not None:
+        sg, su, sd = _u16(sg), _u16(su), _u16(sd)
+    lib().oracle_layer_dense(T, H, E, K, I, float(limit), _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd),
+                             _ptr(sg), _ptr(su), _ptr(sd), _ptr(topk_idx), _ptr(topk_w),
+                             _ptr(slot_to_row), _ptr(out))
+    return out
+
+
+def bf16_to_f64(a: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns (numpy bit shift; used by tests for comparisons)."""
+    return (np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,115 @@
+/*
+ * moe_oracle.h -- plain, slow CPU reference for the sparse MoE FFN layer forward.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark may load this library. It shares no code, header, table or helper with the
+ * HIP library: it has its own bf16 rounding, its own loops, and accumulates every dot
+ * product sequentially in double precision.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [Hy4-deep-dive]  "Tencent Hunyuan Hy4 Preview deep technical analysis" (happyrock.cloud blog),
+ *                   code sketches `MoERouter` and `MoELayer`.
+ *  [Hy3-deep-dive]  "Tencent Hunyuan Hy3 official release deep analysis" (happyrock.cloud blog),
+ *                   `SparseMoERouter.forward`, `MoEFeedForward.forward`, Go `computeConfidence`.
+ *  [Hy4-config]     "Hy4 preview config.json deep interpretation" (lshu.cn), sections
+ *                   "MoE routed experts: 256 choose 8" and "length, vocabulary and training details".
+ *  [Hy3-explainer]  Hy3 sparse-MoE explainer (tqpw.cn), section 2.1 "basic working principle of MoE".
+ *
+ * Conventions: bf16 tensors are passed as raw uint16 bit patterns, row-major, host memory.
+ * Every function is deterministic for any OpenMP thread count (each output element is
+ * produced by one thread with a fixed sequential summation order).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Round a double to the nearest bf16 value, ties to even (IEEE RNE); overflow -> inf,
+ * NaN -> canonical quiet NaN 0x7FC0. Single rounding from the double value. */
+uint16_t oracle_bf16_from_double(double v);
+/* Exact widening of a bf16 bit pattern. */
+double oracle_double_from_bf16(uint16_t b);
+
+/* Router projection, [Hy4-deep-dive] `MoERouter.gate` (a bias-free linear map hidden -> experts)
+ * and [Hy3-deep-dive] `self.gate(x_flat)`. logits[t,e] = fp32( sum_h x[t,h]*wr[e,h] + bias[e] ),
+ * the sum taken in double in ascending h. bias may be NULL (the pages' router has none).
+ * Only tokens listed in `tokens` (n_tok entries) are computed when tokens != NULL; their rows
+ * of `logits` (full [T,E] array) are written, the rest are untouched. */
+void oracle_router_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
+                          const float* bias, const int32_t* tokens, int n_tok, float* logits);
+
+/* Softmax over the experts, top-k, optional renormalisation, routed scaling.
+ * [Hy4-deep-dive] `torch.topk(F.softmax(scores), k)`; [Hy3-deep-dive] renormalisation of the
+ * selected probabilities; [Hy4-config] `norm_topk_prob: true`, `routed_scaling_factor: 2.827`.
+ * Selection takes the k largest fp32 logits (softmax is strictly increasing, so this is the
+ * same set as the k largest probabilities), ordered by value descending and, for equal values,
+ * by expert index ascending; -0.0 and +0.0 are equal. Logits must be finite.
+ * w[t,j] = fp32( scale * p_j / sum_{i in top-k} p_i ) when norm_topk != 0, else fp32(scale*p_j).
+ * probs (may be NULL) receives the full double softmax [T,E]. */
+void oracle_route_from_logits(int T, int E, int K, int norm_topk, double scale,
+                              const float* logits, int32_t* topk_idx, float* topk_w,
+                              double* probs);
+
+/* Token-to-expert dispatch: a stable counting sort of slot ids s = t*K + j by expert,
+ * [Hy3-explainer] 2.1 (per-expert gather `x[expert_mask]`). capacity > 0 keeps the first
+ * `capacity` slots of each expert in ascending slot order and drops the rest.
+ * counts[E] kept per expert, offsets[E+1] exclusive scan, row_to_slot[T*K] (rows >= offsets[E]
+ * are set to -1), slot_to_row[T*K] (-1 for dropped slots). */
+void oracle_dispatch(int T, int K, int E, int capacity, const int32_t* topk_idx,
+                     int32_t* counts, int32_t* offsets, int32_t* row_to_slot,
+                     int32_t* slot_to_row);
+
+/* SwiGLU gate/up half of one expert on n gathered rows, [Hy3-deep-dive] `MoEFeedForward`
+ * (gate_proj, up_proj, silu) with the [Hy4-config] `swiglu_limit` clamp of both pre-activations:
+ * g = sum_h x*wg[i,h], u = sum_h x*wu[i,h] (double), g,u clamped to [-limit, limit] when
+ * limit > 0, h[r,i] = bf16( g/(1+exp(-g)) * u ). wg, wu are [I,H]; x_rows is [n,H]. */
+void oracle_gateup_rows(int n, int H, int I, double limit, const uint16_t* x_rows,
+                        const uint16_t* wg, const uint16_t* wu, uint16_t* h);
+
+/* Down projection of one expert, [Hy3-deep-dive] `down_proj`: y[r,c] = bf16( sum_i h[r,i]*wd[c,i] ),
+ * wd is [H,I], h is [n,I]. */
+void oracle_down_rows(int n, int H, int I, const uint16_t* h, const uint16_t* wd, uint16_t* y);
+
+/* Weighted combine, [Hy4-deep-dive] `MoELayer.forward` (routed sum plus shared expert output):
+ * out[t,c] = bf16( sum_{j<K, slot_to_row[t*K+j] >= 0} w[t,j]*y[row,c] + y_shared[t,c] ), summed in
+ * double in slot order, the shared term last. y_shared may be NULL. */
+void oracle_combine(int T, int K, int H, const float* topk_w, const int32_t* slot_to_row,
+                    const uint16_t* y_routed, const uint16_t* y_shared, uint16_t* out);
+
+/* Whole layer, sparse evaluation (steps above in order). The routed expert weights are
+ * wg,wu [E,I,H] and wd [E,H,I]; the shared expert's are sg,su [I,H], sd [H,I] (NULL = none).
+ * When use_logits != 0, `logits` is taken as input and the router projection is skipped;
+ * otherwise it is written. All outputs are caller-owned host arrays:
+ * topk_idx/topk_w [T,K], counts [E], offsets [E+1], row_to_slot/slot_to_row [T*K],
+ * h_routed [T*K,I], y_routed [T*K,H] (rows >= offsets[E] untouched), h_shared [T,I],
+ * y_shared [T,H], out [T,H]. h_* and y_shared may be NULL when not wanted. */
+void oracle_layer_forward(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                          double limit, int capacity, const uint16_t* x, const uint16_t* wr,
+                          const float* bias, const uint16_t* wg, const uint16_t* wu,
+                          const uint16_t* wd, const uint16_t* sg, const uint16_t* su,
+                          const uint16_t* sd, int use_logits, float* logits, int32_t* topk_idx,
+                          float* topk_w, int32_t* counts, int32_t* offsets,
+                          int32_t* row_to_slot, int32_t* slot_to_row, uint16_t* h_routed,
+                          uint16_t* y_routed, uint16_t* h_shared, uint16_t* y_shared,
+                          uint16_t* out);
+
+/* Dense brute force (small inputs only): every expert evaluated on every token, then masked
+ * by the kept top-k assignment, [Hy4-deep-dive] token loop `routed[b,s] += w * expert(x)`.
+ * Takes the routing (topk_idx, topk_w, slot_to_row kept mask) as input, no permutation. */
+void oracle_layer_dense(int T, int H, int E, int K, int I, double limit, const uint16_t* x,
+                        const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                        const uint16_t* sg, const uint16_t* su, const uint16_t* sd,
+                        const int32_t* topk_idx, const float* topk_w,
+                        const int32_t* slot_to_row, uint16_t* out);
+
+/* Number of OpenMP threads the oracle's parallel loops use. */
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
