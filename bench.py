@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MoE FFN layer forward on one MI355X.
+
+One step = one moe_layer_forward (router GEMM + softmax/top-k/renorm/scale, dispatch, routed and
+shared SwiGLU expert FFNs, combine) over one batch of synthetic, seeded inputs already resident
+in HBM. Default workload: the Hy4-shape decode batch (T=64, H=6144, 256 experts, top-8, one
+shared expert, intermediate 2048, bf16). Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calibration     # plain device copy, for scaling HBM counters
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer tokens/s at Hy4 shape; % of bf16 MFMA or HBM roofline"
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="hy4_decode_t64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true")
+    return ap.parse_args()
+
+
+def algorithmic(wl, counts):
+    """Per-call algorithmic work from the run's actual routing (implementation buffers such as
+    the permuted h and y rows are not counted for the layer)."""
+    T, H, E, K, I, S = wl.T, wl.H, wl.E, wl.K, wl.I, wl.n_shared
+    R = int(counts.sum())
+    touched = int((counts > 0).sum())
+    layer_flops = 2 * T * H * E + 6 * H * I * (R + S * T)
+    layer_bytes = (touched + S) * 6 * H * I + 2 * E * H + 2 * 2 * T * H + 4 * T * E + 8 * T * K
+    # gate/up grouped GEMM launch: its weights, x in, h out
+    gu_flops = 4 * H * I * (R + S * T)
+    gu_bytes = (touched + S) * 4 * H * I + 2 * T * H + 2 * (R + S * T) * I
+    # down grouped GEMM launch: its weights, h in, y out
+    dn_flops = 2 * H * I * (R + S * T)
+    dn_bytes = (touched + S) * 2 * H * I + 2 * (R + S * T) * I + 2 * (R + S * T) * H
+    return dict(R=R, touched=touched, layer_flops=layer_flops, layer_bytes=layer_bytes,
+                gu_flops=gu_flops, gu_bytes=gu_bytes, dn_flops=dn_flops, dn_bytes=dn_bytes)
+
+
+def roofline(flops, nbytes, seconds):
+    ai = flops / nbytes
+    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        a = flops / seconds / 1e12
+        return dict(bound="mfma", achieved=round(a, 2), peak=PEAK_MFMA_TFLOPS, unit="TFLOP/s",
+                    frac=round(a / PEAK_MFMA_TFLOPS, 4))
+    a = nbytes / seconds / 1e9
+    return dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(a / PEAK_HBM_GBS, 4))
+
+
+def cpu_baseline(wl, dev, n_tok):
+    """The CPU oracle, timed on a bounded sample of the workload's tokens (every step of the
+    layer for those tokens: router logits, routing, their routed and shared expert FFNs, combine).
+    Weights are copied to host memory before the clock starts."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_moe_layer_softmax_amd.workloads import as_u16
+
+    rng = np.random.default_rng(99)
+    toks = np.sort(rng.choice(wl.T, min(n_tok, wl.T), replace=False))
+    x = as_u16(dev["x"][torch.from_numpy(toks).to(dev["x"].device)])
+    wr = as_u16(dev["w_router"])
+    bias = None if dev["router_bias"] is None else dev["router_bias"].cpu().numpy()
+    # routing of the sample decides which expert weights the timed region needs
+    lg = oracle.router_logits(x, wr, bias)
+    idx, _ = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
+    experts = sorted(set(int(e) for e in idx.ravel()))
+    W = {e: (as_u16(dev["w_gate"][e]), as_u16(dev["w_up"][e]), as_u16(dev["w_down"][e])) for e in experts}
+    SW = (as_u16(dev["s_gate"]), as_u16(dev["s_up"]), as_u16(dev["s_down"])) if wl.n_shared else None
+    t0 = time.perf_counter()
+    lg = oracle.router_logits(x, wr, bias)
+    idx, w = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
+    counts, offsets, r2s, s2r = oracle.dispatch(idx, wl.E, 0)
+    y = np.zeros((len(toks) * wl.K, wl.H), np.uint16)
+    for e in experts:  # expert-major, as the oracle's layer does
+        a, b = offsets[e], offsets[e + 1]
+        _, y[a:b] = oracle.expert_ffn_rows(x[r2s[a:b] // wl.K], *W[e], wl.limit)
+    ys = oracle.expert_ffn_rows(x, *SW, wl.limit)[1] if SW else None
+    oracle.combine(w, s2r, y, ys)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d of the workload's %d tokens (all steps of the layer for them; %d distinct "
+                      "routed experts + shared), fp64 C++ oracle" % (len(toks), wl.T, len(experts))}
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30  # 1 GiB
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "reads_bytes": n, "writes_bytes": n}))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X, so "
+              "--gpus %d (WORLD_SIZE=%d) is not supported" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import numpy as np
+    import torch
+
+    import sparse_moe_layer_softmax_amd as moe
+    from sparse_moe_layer_softmax_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    dev = generate_inputs(wl)
+    shape = moe.Shape.of(wl)
+    layer = moe.MoELayer(shape, dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                         dev["s_gate"], dev["s_up"], dev["s_down"], dev["router_bias"])
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        layer.forward(dev["x"], out)
+    torch.cuda.synchronize()
+
+    # phase events: one set per step, created once (a first record makes the HIP event)
+    nph = moe.MOE_LAYER_PHASE_EVENTS
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)
+    import ctypes
+    handles = [(ctypes.c_void_p * nph)(*[e.cuda_event for e in row]) for row in evs]
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    wr, b, wg, wu, wd, sg, su, sd = layer.w
+    for i in range(args.steps):
+        moe.moe_layer_forward_profiled(shape, dev["x"], wr, b, wg, wu, wd, sg, su, sd, out,
+                                       layer.ws, handles[i], stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    names = ["route", "permute", "tile_table", "gate_up_gemm", "down_gemm", "combine"]
+    phase_ms = {n: float(np.mean([row[j].elapsed_time(row[j + 1]) for row in evs]))
+                for j, n in enumerate(names)}
+    counts = layer.intermediate("counts", torch.int32, (wl.E,)).cpu().numpy()
+    alg = algorithmic(wl, counts)
+    gu_s = phase_ms["gate_up_gemm"] / 1e3
+    dn_s = phase_ms["down_gemm"] / 1e3
+    rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s)
+    rf["traffic"] = None
+    rf["kernel"] = "ffn_skinny_kernel<true> (routed+shared gate/up grouped GEMM, clamped SwiGLU)"
+    rf["algorithmic_bytes"] = alg["gu_bytes"]
+    rf["algorithmic_flops"] = alg["gu_flops"]
+    rf["avg_launch_ms"] = round(phase_ms["gate_up_gemm"], 4)
+    layer_s = ms / 1e3
+    res = {
+        "metric": METRIC,
+        "value": round(wl.T / layer_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I,
+                   "n_shared": wl.n_shared, "routed_scaling": wl.scale, "swiglu_limit": wl.limit,
+                   "capacity": wl.capacity, "parallelism": "none (1 GPU)"},
+        "roofline": rf,
+        "layer": {"algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"],
+                  "hbm_GBs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
+                  "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                  "mfma_TFLOPs": round(alg["layer_flops"] / layer_s / 1e12, 2),
+                  "mfma_frac": round(alg["layer_flops"] / layer_s / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                  "routed_rows": alg["R"], "touched_experts": alg["touched"],
+                  "max_rows_per_expert": int(counts.max())},
+        "down_gemm": roofline(alg["dn_flops"], alg["dn_bytes"], dn_s),
+        "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+    }
+    if not args.no_cpu_baseline:
+        n_tok = args.cpu_tokens or (16 if wl.T <= 64 else 8)
+        res["cpu_baseline"] = cpu_baseline(wl, dev, n_tok)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def generate_inputs(wl):
+    from sparse_moe_layer_softmax_amd.workloads import generate
+    return generate(wl, "cuda")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,193 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer forward.
+ *
+ * The layer (Hy4 preview shape: hidden 6144, 256 routed experts, top-8, one always-on shared
+ * expert, expert intermediate 2048, routed_scaling_factor 2.827, swiglu_limit 10, silu, bf16):
+ *
+ *   logits = x Wr^T (+ b)                        router projection
+ *   p = softmax(logits); top-k; w = s * p_top / sum(p_top)     routing weights
+ *   dispatch (t, j) slots to their experts (stable, optional per-expert capacity)
+ *   y_e = Wd_e ( silu(clamp(Wg_e x)) * clamp(Wu_e x) )        SwiGLU expert FFN
+ *   out = sum_j w_j y_{e_j} + y_shared                         combine
+ *
+ * Sources, cited by page title and section:
+ *  - "Tencent Hunyuan Hy4 Preview deep technical analysis" (happyrock.cloud): the `MoERouter`
+ *    sketch (bias-free linear gate, softmax, top-k) and `MoELayer` (256 routed experts, one
+ *    shared expert always run, routed output plus shared output).
+ *  - "Tencent Hunyuan Hy3 official release deep analysis" (happyrock.cloud): `SparseMoERouter`
+ *    (token flattening, softmax, top-k, renormalisation of the selected probabilities,
+ *    capacity_factor) and `MoEFeedForward` (SwiGLU: down(silu(gate x) * up x), no biases).
+ *  - "Hy4 preview config.json deep interpretation" (lshu.cn), section "MoE routed experts":
+ *    n_routed_experts 256, num_experts_per_tok 8, n_shared_experts 1, moe_intermediate_size
+ *    2048, norm_topk_prob true, routed_scaling_factor 2.827, swiglu_limit 10; section
+ *    "length, vocabulary and training details": hidden_act silu, dtype bfloat16.
+ *  - Hy3 sparse-MoE explainer (tqpw.cn), section 2.1: expert-major dispatch, each expert run on
+ *    the rows routed to it, then aggregation.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers (HBM), row-major, densely packed. bf16 tensors are
+ *    passed as their 16-bit patterns (uint16_t). The `moe_shape` is a HOST pointer.
+ *  - The caller owns every buffer, including the workspace. The library never allocates,
+ *    frees, synchronises, or reads device memory from the host.
+ *  - Each call only enqueues kernels on `stream` (0 = the null stream) and returns; results are
+ *    visible after the caller synchronises that stream. Calls are stateless; concurrent calls
+ *    on different streams need separate workspaces.
+ *  - Every argument check runs on the host before any launch; on error nothing is enqueued.
+ *    Faults inside kernels surface at the caller's next synchronisation (HIP convention).
+ *  - Inputs must be finite. Results are deterministic: the same inputs give the same bits.
+ *  - Supported shapes: 1 <= K <= 16, K <= E <= 256, H and I multiples of 256, T >= 1 with
+ *    T*K < 2^31. Others return MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* NULL required pointer, non-positive size, K > E, ... */
+#define MOE_ERR_UNSUPPORTED (-2) /* shape outside the supported set listed above          */
+#define MOE_ERR_WORKSPACE (-3)   /* ws_bytes smaller than the matching *_workspace_size     */
+#define MOE_ERR_HIP (-4)         /* a kernel launch failed (hipGetLastError)                */
+
+/* Layer shape and constants (Hy4 config walkthrough, section "MoE routed experts"). */
+typedef struct moe_shape {
+  int32_t T;              /* tokens = batch * sequence (the Hy3 router flattens them)       */
+  int32_t H;              /* hidden size (6144)                                              */
+  int32_t E;              /* routed experts (256)                                            */
+  int32_t K;              /* experts per token, top-k (8)                                    */
+  int32_t I;              /* expert intermediate size (2048); the shared expert's too        */
+  int32_t n_shared;       /* shared experts: 0 or 1                                          */
+  int32_t norm_topk_prob; /* 1: renormalise the k selected probabilities to sum 1            */
+  float routed_scaling;   /* s, multiplies every routed weight (2.827); never the shared one */
+  float swiglu_limit;     /* L: gate and up pre-activations clamped to [-L, L]; <= 0 = off   */
+  int32_t capacity;       /* per-expert capacity C (slots beyond it are dropped); <= 0 = off */
+} moe_shape;
+
+/* Human-readable text for a return code (static storage). */
+const char* moe_strerror(int code);
+
+/* ---------------------------------------------------------------- router: moe_route
+ * Router projection, softmax over the E experts, top-k, renormalisation and routed scaling
+ * (Hy4 deep-dive `MoERouter.forward`; Hy3 deep-dive `SparseMoERouter.forward`; Hy4 config
+ * walkthrough `norm_topk_prob`, `routed_scaling_factor`).
+ *   x        [T,H] bf16           tokens
+ *   w_router [E,H] bf16           gate weight in nn.Linear (out, in) layout
+ *   bias     [E]   fp32 or NULL   optional additive logit bias (the pages' router has none)
+ *   logits   [T,E] fp32 or NULL   out: logits = x w_router^T + bias, fp32 accumulation
+ *   topk_w   [T,K] fp32           out: w_j = s * p_j / sum_{i<K} p_i   (s * p_j without renorm)
+ *   topk_idx [T,K] int32          out: expert ids by logit descending; equal logits -> lower id
+ * Selection compares the fp32 logits (-0.0 == +0.0), so it is exact given the logits.
+ * ws: moe_route_workspace_size(shape) bytes, 256-byte aligned.                              */
+size_t moe_route_workspace_size(const moe_shape* shape);
+int moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+              const float* bias, float* logits, float* topk_w, int32_t* topk_idx, void* ws,
+              size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- dispatch: moe_permute
+ * Token-to-expert dispatch (Hy3 explainer 2.1: the rows of each expert gathered together).
+ * A slot is (t, j), id s = t*K + j. Rows are grouped by expert, ascending expert id; inside an
+ * expert, ascending slot id (a stable counting sort). With capacity C > 0 only the first C
+ * slots of each expert (in slot order) are kept.
+ *   topk_idx    [T*K]  int32 in   expert of each slot (0 <= id < E)
+ *   counts      [E]    int32 out  kept rows per expert
+ *   offsets     [E+1]  int32 out  exclusive prefix sum of counts; offsets[E] = R kept rows
+ *   row_to_slot [T*K]  int32 out  slot id of row r for r < R; -1 for R <= r < T*K
+ *   slot_to_row [T*K]  int32 out  row of slot s, -1 if dropped
+ * ws: moe_permute_workspace_size(shape) bytes.                                              */
+size_t moe_permute_workspace_size(const moe_shape* shape);
+int moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row, void* ws,
+                size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- experts: moe_expert_ffn
+ * Grouped SwiGLU FFN over variable-length row groups (Hy3 deep-dive `MoEFeedForward`; clamp
+ * from the Hy4 config walkthrough's swiglu_limit; silu from hidden_act):
+ *   for group g and row r in [group_offsets[g], group_offsets[g+1]):
+ *     a = x[token(r)],  token(r) = row_to_slot[r] / K   (row_to_slot != NULL)
+ *                       token(r) = r                     (row_to_slot == NULL)
+ *     h[r] = bf16( silu(clamp(a Wg_g^T, L)) * clamp(a Wu_g^T, L) )     fp32 accumulate
+ *     y[r] = bf16( h[r] Wd_g^T )                                        fp32 accumulate
+ *   n_groups       G >= 1 (E for the routed experts, 1 for the shared expert)
+ *   rows_max       upper bound on group_offsets[G] (T*K routed, T shared); sizes the grid
+ *   x              [T,H] bf16
+ *   row_to_slot    [rows_max] int32 or NULL (identity: row r is token r, rows_max <= T)
+ *   group_offsets  [G+1] int32 on the device, non-decreasing, group_offsets[0] = 0, or NULL
+ *                  meaning one group of rows_max rows
+ *   w_gate, w_up   [G,I,H] bf16;  w_down [G,H,I] bf16
+ *   h              [rows_max,I] bf16 out, or NULL (then kept in the workspace)
+ *   y              [rows_max,H] bf16 out; rows >= group_offsets[G] are left untouched
+ * ws: moe_expert_ffn_workspace_size(shape, G, rows_max) bytes.                              */
+size_t moe_expert_ffn_workspace_size(const moe_shape* shape, int32_t n_groups, int32_t rows_max);
+int moe_expert_ffn(const moe_shape* shape, int32_t n_groups, int32_t rows_max,
+                   const uint16_t* x, const int32_t* row_to_slot, const int32_t* group_offsets,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   uint16_t* h, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- combine: moe_combine
+ * Weighted combine (Hy4 deep-dive `MoELayer.forward`: routed_output + shared_output):
+ *   out[t] = bf16( sum_{j<K, slot_to_row[t*K+j] >= 0} topk_w[t,j] * y_routed[slot_to_row[t*K+j]]
+ *                  + y_shared[t] )
+ * summed in fp32 in slot order j = 0..K-1, the shared row last; no atomics.
+ *   y_routed    [R,H] bf16,  topk_w [T,K] fp32,  slot_to_row [T*K] int32
+ *   y_shared    [T,H] bf16 or NULL,   out [T,H] bf16                                       */
+int moe_combine(const moe_shape* shape, const uint16_t* y_routed, const float* topk_w,
+                const int32_t* slot_to_row, const uint16_t* y_shared, uint16_t* out,
+                hipStream_t stream);
+
+/* ---------------------------------------------------------------- whole layer
+ * moe_route -> moe_permute -> routed + shared expert FFN (one grouped launch per projection,
+ * the shared expert is one more group) -> moe_combine, all on `stream`, no host sync.
+ *   x [T,H], w_router [E,H], bias [E] fp32 or NULL,
+ *   w_gate/w_up [E,I,H], w_down [E,H,I]           routed experts
+ *   s_gate/s_up [I,H], s_down [H,I]               shared expert (NULL iff n_shared == 0)
+ *   out [T,H] bf16
+ * The intermediates stay in the workspace; moe_layer_workspace_layout gives their byte
+ * offsets so a caller may read them after the stream completes.
+ * ws: moe_layer_workspace_size(shape) bytes, 256-byte aligned.                              */
+typedef struct moe_layer_ws_layout {
+  size_t logits;      /* [T,E] fp32                                      */
+  size_t topk_w;      /* [T,K] fp32                                      */
+  size_t topk_idx;    /* [T,K] int32                                     */
+  size_t counts;      /* [E] int32                                       */
+  size_t offsets;     /* [E+1] int32                                     */
+  size_t row_to_slot; /* [T*K] int32                                     */
+  size_t slot_to_row; /* [T*K] int32                                     */
+  size_t h;           /* [T + T*K, I] bf16: shared rows first, then routed rows */
+  size_t y;           /* [T + T*K, H] bf16: same row order as h          */
+  size_t total;       /* bytes                                           */
+} moe_layer_ws_layout;
+
+size_t moe_layer_workspace_size(const moe_shape* shape);
+int moe_layer_workspace_layout(const moe_shape* shape, moe_layer_ws_layout* layout);
+int moe_layer_forward(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                      const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
+                      const uint16_t* w_down, const uint16_t* s_gate, const uint16_t* s_up,
+                      const uint16_t* s_down, uint16_t* out, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Same as moe_layer_forward, and records caller-created HIP events on `stream` at the phase
+ * boundaries below (any entry may be NULL; `phase_events` itself may be NULL). For timing
+ * single kernels with hipEventElapsedTime; the computation is identical to moe_layer_forward.
+ *   [0] start  [1] after routing  [2] after dispatch  [3] after the tile table
+ *   [4] after the gate/up grouped GEMM  [5] after the down grouped GEMM  [6] after combine   */
+#define MOE_LAYER_PHASE_EVENTS 7
+int moe_layer_forward_profiled(const moe_shape* shape, const uint16_t* x,
+                               const uint16_t* w_router, const float* bias,
+                               const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, const uint16_t* s_gate,
+                               const uint16_t* s_up, const uint16_t* s_down, uint16_t* out,
+                               void* ws, size_t ws_bytes, hipStream_t stream,
+                               hipEvent_t const* phase_events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -1,0 +1,239 @@
+"""MI355X (gfx950) sparse Mixture-of-Experts FFN layer forward.
+
+Thin ctypes binding of ``libmoe.so`` (C ABI in ``include/moe.h``). Functions carry the same
+names as the C entry points and only marshal arguments: torch tensors supply device memory and
+the current HIP stream; every step of the layer runs in the library's kernels. There is no
+fallback: if ``libmoe.so`` is missing or cannot be loaded, the first call raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+EXPORTED = (
+    "moe_strerror", "moe_route_workspace_size", "moe_route", "moe_permute_workspace_size",
+    "moe_permute", "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
+    "moe_layer_workspace_size", "moe_layer_workspace_layout", "moe_layer_forward",
+    "moe_layer_forward_profiled",
+)
+MOE_LAYER_PHASE_EVENTS = 7
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__("%s failed: %s (%d)" % (where, strerror(code), code))
+        self.code = code
+
+
+class moe_shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("I", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("norm_topk_prob", ctypes.c_int32), ("routed_scaling", ctypes.c_float),
+                ("swiglu_limit", ctypes.c_float), ("capacity", ctypes.c_int32)]
+
+
+class moe_layer_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("logits", "topk_w", "topk_idx", "counts", "offsets",
+                                               "row_to_slot", "slot_to_row", "h", "y", "total")]
+
+
+@dataclass(frozen=True)
+class Shape:
+    T: int
+    H: int
+    E: int
+    K: int
+    I: int
+    n_shared: int = 1
+    norm_topk_prob: bool = True
+    routed_scaling: float = 1.0
+    swiglu_limit: float = 10.0
+    capacity: int = 0
+
+    @staticmethod
+    def of(wl) -> "Shape":
+        """From a workloads.Workload."""
+        return Shape(wl.T, wl.H, wl.E, wl.K, wl.I, wl.n_shared, wl.norm_topk, wl.scale, wl.limit,
+                     wl.capacity)
+
+    def c(self) -> moe_shape:
+        return moe_shape(self.T, self.H, self.E, self.K, self.I, self.n_shared,
+                         int(bool(self.norm_topk_prob)), self.routed_scaling, self.swiglu_limit,
+                         self.capacity)
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libmoe.so is not built (run `python -m sparse_moe_layer_softmax_amd.build`)")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    sp = ctypes.POINTER(moe_shape)
+    sig = {
+        "moe_strerror": ([ctypes.c_int], ctypes.c_char_p),
+        "moe_route_workspace_size": ([sp], S),
+        "moe_route": ([sp, P, P, P, P, P, P, P, S, P], ctypes.c_int),
+        "moe_permute_workspace_size": ([sp], S),
+        "moe_permute": ([sp, P, P, P, P, P, P, S, P], ctypes.c_int),
+        "moe_expert_ffn_workspace_size": ([sp, I32, I32], S),
+        "moe_expert_ffn": ([sp, I32, I32, P, P, P, P, P, P, P, P, P, S, P], ctypes.c_int),
+        "moe_combine": ([sp, P, P, P, P, P, P], ctypes.c_int),
+        "moe_layer_workspace_size": ([sp], S),
+        "moe_layer_workspace_layout": ([sp, ctypes.POINTER(moe_layer_ws_layout)], ctypes.c_int),
+        "moe_layer_forward": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P], ctypes.c_int),
+        "moe_layer_forward_profiled": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P, P], ctypes.c_int),
+    }
+    for name, (argtypes, restype) in sig.items():
+        fn = getattr(L, name)
+        fn.argtypes = argtypes
+        fn.restype = restype
+    return L
+
+
+_lib = None
+
+
+def library():
+    """The loaded libmoe.so (loaded on first use; raises ImportError if it is not built)."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return library().moe_strerror(code).decode()
+
+
+def _p(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int, where: str):
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+def _ws(nbytes: int, device):
+    # 256-byte alignment: torch's caching allocator returns 512-byte aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------- workspace sizes
+def moe_route_workspace_size(shape: Shape) -> int:
+    return library().moe_route_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_permute_workspace_size(shape: Shape) -> int:
+    return library().moe_permute_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_expert_ffn_workspace_size(shape: Shape, n_groups: int, rows_max: int) -> int:
+    return library().moe_expert_ffn_workspace_size(ctypes.byref(shape.c()), n_groups, rows_max)
+
+
+def moe_layer_workspace_size(shape: Shape) -> int:
+    return library().moe_layer_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_layer_workspace_layout(shape: Shape) -> dict:
+    lay = moe_layer_ws_layout()
+    _check(library().moe_layer_workspace_layout(ctypes.byref(shape.c()), ctypes.byref(lay)),
+           "moe_layer_workspace_layout")
+    return {n: getattr(lay, n) for n, _ in moe_layer_ws_layout._fields_}
+
+
+# ----------------------------------------------------------------------------- entry points
+def moe_route(shape: Shape, x, w_router, bias, logits, topk_w, topk_idx, ws, stream=None):
+    _check(library().moe_route(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(logits),
+                         _p(topk_w), _p(topk_idx), _p(ws), ws.numel() if ws is not None else 0,
+                         _stream(stream)), "moe_route")
+
+
+def moe_permute(shape: Shape, topk_idx, counts, offsets, row_to_slot, slot_to_row, ws,
+                stream=None):
+    _check(library().moe_permute(ctypes.byref(shape.c()), _p(topk_idx), _p(counts), _p(offsets),
+                           _p(row_to_slot), _p(slot_to_row), _p(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
+
+
+def moe_expert_ffn(shape: Shape, n_groups: int, rows_max: int, x, row_to_slot, group_offsets,
+                   w_gate, w_up, w_down, h, y, ws, stream=None):
+    _check(library().moe_expert_ffn(ctypes.byref(shape.c()), n_groups, rows_max, _p(x), _p(row_to_slot),
+                              _p(group_offsets), _p(w_gate), _p(w_up), _p(w_down), _p(h), _p(y),
+                              _p(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_expert_ffn")
+
+
+def moe_combine(shape: Shape, y_routed, topk_w, slot_to_row, y_shared, out, stream=None):
+    _check(library().moe_combine(ctypes.byref(shape.c()), _p(y_routed), _p(topk_w), _p(slot_to_row),
+                           _p(y_shared), _p(out), _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,
+                      s_down, out, ws, stream=None):
+    _check(library().moe_layer_forward(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias),
+                                 _p(w_gate), _p(w_up), _p(w_down), _p(s_gate), _p(s_up),
+                                 _p(s_down), _p(out), _p(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)), "moe_layer_forward")
+
+
+def moe_layer_forward_profiled(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, s_gate,
+                               s_up, s_down, out, ws, phase_events, stream=None):
+    """phase_events: ctypes array of MOE_LAYER_PHASE_EVENTS hipEvent_t handles (entries may be 0)."""
+    _check(library().moe_layer_forward_profiled(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_up), _p(w_down),
+        _p(s_gate), _p(s_up), _p(s_down), _p(out), _p(ws), ws.numel() if ws is not None else 0,
+        _stream(stream), phase_events), "moe_layer_forward_profiled")
+
+
+# ----------------------------------------------------------------------------- conveniences
+class MoELayer:
+    """Holds device weights and a workspace; ``forward(x)`` runs moe_layer_forward."""
+
+    def __init__(self, shape: Shape, w_router, w_gate, w_up, w_down, s_gate=None, s_up=None,
+                 s_down=None, router_bias=None):
+        self.shape = shape
+        self.w = (w_router, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
+        self.device = w_router.device
+        self.ws = _ws(moe_layer_workspace_size(shape), self.device)
+        self.layout = moe_layer_workspace_layout(shape)
+
+    def forward(self, x, out=None, stream=None):
+        if out is None:
+            out = torch.empty((self.shape.T, self.shape.H), dtype=torch.bfloat16, device=self.device)
+        wr, b, wg, wu, wd, sg, su, sd = self.w
+        moe_layer_forward(self.shape, x, wr, b, wg, wu, wd, sg, su, sd, out, self.ws, stream)
+        return out
+
+    def intermediate(self, name: str, dtype, shape):
+        """A view of an intermediate inside the workspace (valid after the stream completes)."""
+        off = self.layout[name]
+        n = 1
+        for d in shape:
+            n *= d
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.ws[off:off + nbytes].view(dtype).view(*shape)

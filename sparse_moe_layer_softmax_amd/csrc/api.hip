@@ -1,0 +1,317 @@
+// api.hip -- the C ABI (include/moe.h): argument checks, workspace layout, launch order.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call leaves the
+// stream untouched. The library allocates nothing and never synchronises.
+#include <cmath>
+#include <climits>
+
+#include "moe.h"
+#include "moe_internal.h"
+
+using moe::align_up;
+
+namespace {
+
+int check_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->T < 1 || s->H < 1 || s->E < 1 || s->K < 1 || s->I < 1) return MOE_ERR_INVALID_ARG;
+  if (s->K > s->E) return MOE_ERR_INVALID_ARG;
+  if (s->n_shared != 0 && s->n_shared != 1) return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(s->routed_scaling) || std::isnan(s->swiglu_limit)) return MOE_ERR_INVALID_ARG;
+  if (s->K > 16 || s->E > 256) return MOE_ERR_UNSUPPORTED;
+  if (s->H % 256 != 0 || s->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  // row indices are int32 and rows_max = T + T*K must fit
+  if (static_cast<long long>(s->T) * (s->K + 1) >= INT_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// ----- workspace layouts (offsets in bytes, every buffer 256-byte aligned)
+struct RouteWs {
+  size_t partials, total;
+  int S;
+};
+RouteWs route_ws(const moe_shape& s) {
+  RouteWs w{};
+  w.S = moe::route_splits(s.T, s.H, s.E);
+  w.partials = 0;
+  w.total = align_up(sizeof(float) * static_cast<size_t>(w.S) * s.T * s.E);
+  return w;
+}
+
+struct PermuteWs {
+  size_t block_counts, block_base, total;
+};
+PermuteWs permute_ws(const moe_shape& s) {
+  PermuteWs w{};
+  const size_t nb = static_cast<size_t>(moe::permute_blocks(s.T * s.K)) * s.E * sizeof(int32_t);
+  w.block_counts = 0;
+  w.block_base = align_up(nb);
+  w.total = w.block_base + align_up(nb);
+  return w;
+}
+
+struct FfnWs {
+  size_t offsets, tiles, h, total;
+};
+FfnWs ffn_ws(const moe_shape& s, int n_groups, int rows_max, bool need_h) {
+  FfnWs w{};
+  w.offsets = 0;
+  w.tiles = align_up(2 * sizeof(int32_t));
+  // the tile table is sized for the smallest row tile any FFN kernel uses (16 rows)
+  w.h = w.tiles + align_up(moe::tile_table_bytes(moe::max_tiles_for(rows_max, n_groups, 16)));
+  w.total = w.h + (need_h ? align_up(sizeof(uint16_t) * static_cast<size_t>(rows_max) * s.I) : 0);
+  return w;
+}
+
+struct LayerWs {
+  moe_layer_ws_layout pub;
+  size_t route, permute, ext_offsets, tiles;
+};
+LayerWs layer_ws(const moe_shape& s) {
+  LayerWs w{};
+  const size_t TK = static_cast<size_t>(s.T) * s.K;
+  const size_t rows = TK + static_cast<size_t>(s.n_shared ? s.T : 0);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  w.pub.logits = take(sizeof(float) * s.T * s.E);
+  w.pub.topk_w = take(sizeof(float) * TK);
+  w.pub.topk_idx = take(sizeof(int32_t) * TK);
+  w.pub.counts = take(sizeof(int32_t) * s.E);
+  w.pub.offsets = take(sizeof(int32_t) * (s.E + 1));
+  w.pub.row_to_slot = take(sizeof(int32_t) * TK);
+  w.pub.slot_to_row = take(sizeof(int32_t) * TK);
+  w.pub.h = take(sizeof(uint16_t) * rows * s.I);
+  w.pub.y = take(sizeof(uint16_t) * rows * s.H);
+  w.route = take(route_ws(s).total);
+  w.permute = take(permute_ws(s).total);
+  w.ext_offsets = take(sizeof(int32_t) * (s.E + 2));
+  w.tiles = take(moe::tile_table_bytes(moe::max_tiles_for(static_cast<int>(rows), s.E + s.n_shared, 16)));
+  w.pub.total = o;
+  return w;
+}
+
+inline bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+size_t moe_route_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return route_ws(*s).total;
+}
+
+int moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, const float* bias,
+              float* logits, float* topk_w, int32_t* topk_idx, void* ws, size_t ws_bytes,
+              hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!x || !w_router || !topk_w || !topk_idx || !ws) return MOE_ERR_INVALID_ARG;
+  const RouteWs w = route_ws(*s);
+  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route(*s, x, w_router, bias, logits, topk_w, topk_idx,
+                                      reinterpret_cast<float*>(at(ws, w.partials)), w.S, stream));
+}
+
+size_t moe_permute_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return permute_ws(*s).total;
+}
+
+int moe_permute(const moe_shape* s, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                int32_t* row_to_slot, int32_t* slot_to_row, void* ws, size_t ws_bytes,
+                hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!topk_idx || !counts || !offsets || !row_to_slot || !slot_to_row || !ws)
+    return MOE_ERR_INVALID_ARG;
+  const PermuteWs w = permute_ws(*s);
+  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_permute(
+      *s, topk_idx, counts, offsets, row_to_slot, slot_to_row,
+      reinterpret_cast<int32_t*>(at(ws, w.block_counts)),
+      reinterpret_cast<int32_t*>(at(ws, w.block_base)), nullptr, 0, stream));
+}
+
+size_t moe_expert_ffn_workspace_size(const moe_shape* s, int32_t n_groups, int32_t rows_max) {
+  if (check_shape(s) != MOE_OK || n_groups < 1 || n_groups > 1024 || rows_max < 1) return 0;
+  return ffn_ws(*s, n_groups, rows_max, true).total;
+}
+
+int moe_expert_ffn(const moe_shape* s, int32_t n_groups, int32_t rows_max, const uint16_t* x,
+                   const int32_t* row_to_slot, const int32_t* group_offsets,
+                   const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                   uint16_t* h, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!x || !w_gate || !w_up || !w_down || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (n_groups < 1 || n_groups > 1024 || rows_max < 1) return MOE_ERR_INVALID_ARG;
+  if (!row_to_slot && rows_max > s->T) return MOE_ERR_INVALID_ARG;
+  if (!group_offsets && n_groups != 1) return MOE_ERR_INVALID_ARG;
+  const FfnWs w = ffn_ws(*s, n_groups, rows_max, h == nullptr);
+  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  const int32_t* offs = group_offsets;
+  if (!offs) {
+    int32_t* o = reinterpret_cast<int32_t*>(at(ws, w.offsets));
+    rc = hip_status(moe::launch_single_group_offsets(o, rows_max, stream));
+    if (rc != MOE_OK) return rc;
+    offs = o;
+  }
+  moe::FfnProblem p{};
+  p.x = x;
+  p.T = s->T;
+  p.gather = row_to_slot;
+  p.n_ident = row_to_slot ? 0 : INT_MAX;
+  p.topk = s->K;
+  p.offsets = offs;
+  p.n_groups = n_groups;
+  p.rows_max = rows_max;
+  p.g_split = 0;
+  p.gate_b = w_gate;
+  p.up_b = w_up;
+  p.down_b = w_down;
+  p.H = s->H;
+  p.I = s->I;
+  p.limit = s->swiglu_limit;
+  p.h = h ? h : reinterpret_cast<uint16_t*>(at(ws, w.h));
+  p.y = y;
+  p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  return hip_status(moe::launch_ffn(p, stream));
+}
+
+int moe_combine(const moe_shape* s, const uint16_t* y_routed, const float* topk_w,
+                const int32_t* slot_to_row, const uint16_t* y_shared, uint16_t* out,
+                hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!y_routed || !topk_w || !slot_to_row || !out) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(y_routed) | reinterpret_cast<uintptr_t>(out) |
+       reinterpret_cast<uintptr_t>(y_shared)) & 15u)
+    return MOE_ERR_INVALID_ARG;  // 16-byte vector accesses
+  return hip_status(moe::launch_combine(*s, y_routed, topk_w, slot_to_row, y_shared, out, stream));
+}
+
+size_t moe_layer_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return layer_ws(*s).pub.total;
+}
+
+int moe_layer_workspace_layout(const moe_shape* s, moe_layer_ws_layout* layout) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  *layout = layer_ws(*s).pub;
+  return MOE_OK;
+}
+
+int moe_layer_forward(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                      const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
+                      const uint16_t* w_down, const uint16_t* s_gate, const uint16_t* s_up,
+                      const uint16_t* s_down, uint16_t* out, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  return moe_layer_forward_profiled(s, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,
+                                    s_down, out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_layer_forward_profiled(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                               const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
+                               const uint16_t* w_down, const uint16_t* s_gate,
+                               const uint16_t* s_up, const uint16_t* s_down, uint16_t* out,
+                               void* ws, size_t ws_bytes, hipStream_t stream,
+                               hipEvent_t const* ev) {
+  auto mark = [&](int i) {
+    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+  };
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !out || !ws) return MOE_ERR_INVALID_ARG;
+  const bool shared = s->n_shared == 1;
+  if (shared != (s_gate && s_up && s_down)) return MOE_ERR_INVALID_ARG;
+  if (!shared && (s_gate || s_up || s_down)) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(out) & 15u) return MOE_ERR_INVALID_ARG;
+  const LayerWs w = layer_ws(*s);
+  if (ws_bytes < w.pub.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+
+  float* logits = reinterpret_cast<float*>(at(ws, w.pub.logits));
+  float* topk_w = reinterpret_cast<float*>(at(ws, w.pub.topk_w));
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(at(ws, w.pub.topk_idx));
+  int32_t* counts = reinterpret_cast<int32_t*>(at(ws, w.pub.counts));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, w.pub.offsets));
+  int32_t* r2s = reinterpret_cast<int32_t*>(at(ws, w.pub.row_to_slot));
+  int32_t* s2r = reinterpret_cast<int32_t*>(at(ws, w.pub.slot_to_row));
+  uint16_t* h = reinterpret_cast<uint16_t*>(at(ws, w.pub.h));
+  uint16_t* y = reinterpret_cast<uint16_t*>(at(ws, w.pub.y));
+  int32_t* ext = reinterpret_cast<int32_t*>(at(ws, w.ext_offsets));
+
+  mark(0);
+  const RouteWs rw = route_ws(*s);
+  rc = hip_status(moe::launch_route(*s, x, w_router, bias, logits, topk_w, topk_idx,
+                                    reinterpret_cast<float*>(at(ws, w.route + rw.partials)), rw.S,
+                                    stream));
+  if (rc != MOE_OK) return rc;
+  mark(1);
+
+  const PermuteWs pw = permute_ws(*s);
+  const int n_ident = shared ? s->T : 0;
+  rc = hip_status(moe::launch_permute(
+      *s, topk_idx, counts, offsets, r2s, s2r,
+      reinterpret_cast<int32_t*>(at(ws, w.permute + pw.block_counts)),
+      reinterpret_cast<int32_t*>(at(ws, w.permute + pw.block_base)), shared ? ext : nullptr,
+      n_ident, stream));
+  if (rc != MOE_OK) return rc;
+  mark(2);
+
+  // routed experts and the shared expert in one grouped launch per projection:
+  // group 0 = shared expert over rows [0, T) (identity), groups 1..E = routed experts
+  moe::FfnProblem p{};
+  p.x = x;
+  p.T = s->T;
+  p.gather = r2s;
+  p.n_ident = n_ident;
+  p.topk = s->K;
+  p.offsets = shared ? ext : offsets;
+  p.n_groups = s->E + (shared ? 1 : 0);
+  p.rows_max = n_ident + s->T * s->K;
+  p.g_split = shared ? 1 : 0;
+  p.gate_a = s_gate;
+  p.up_a = s_up;
+  p.down_a = s_down;
+  p.gate_b = w_gate;
+  p.up_b = w_up;
+  p.down_b = w_down;
+  p.H = s->H;
+  p.I = s->I;
+  p.limit = s->swiglu_limit;
+  p.h = h;
+  p.y = y;
+  p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  rc = hip_status(moe::launch_ffn(p, stream, ev ? ev + 3 : nullptr));
+  if (rc != MOE_OK) return rc;
+
+  const uint16_t* y_routed = y + static_cast<size_t>(n_ident) * s->H;
+  rc = hip_status(moe::launch_combine(*s, y_routed, topk_w, s2r, shared ? y : nullptr, out,
+                                      stream));
+  mark(6);
+  return rc;
+}
+
+}  // extern "C"

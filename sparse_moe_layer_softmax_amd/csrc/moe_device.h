@@ -1,0 +1,57 @@
+// moe_device.h -- gfx950 device helpers shared by the MoE kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// 16-byte global load (8 bf16).
+__device__ __forceinline__ u32x4_t ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
+// Lane l supplies A[l%16][8*(l/16) + 0..7] and B[8*(l/16) + 0..7][l%16] and holds
+// D[4*(l/16) + v][l%16] for v = 0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// D(32x32) += A(32x16) * B(16x32). Lane l supplies A[l%32][8*(l/32) + 0..7] and
+// B[8*(l/32) + 0..7][l%32]; holds D[8*(v/4) + 4*(l/32) + v%4][l%32] for v = 0..15.
+__device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// silu(clamp(g)) * clamp(u): the SwiGLU activation with swiglu_limit applied to both
+// pre-activations (limit <= 0 disables the clamp).
+__device__ __forceinline__ float clamped_swiglu(float g, float u, float limit) {
+  if (limit > 0.f) {
+    g = fminf(fmaxf(g, -limit), limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return g / (1.f + __expf(-g)) * u;
+}
+
+}  // namespace moe

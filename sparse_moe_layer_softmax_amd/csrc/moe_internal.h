@@ -1,0 +1,68 @@
+// moe_internal.h -- host-side launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+// ---- router (route.hip)
+// Split of the hidden dimension used by the router GEMM (a divisor of H/128).
+int route_splits(int T, int H, int E);
+// partials: [S, T, E] fp32 scratch. logits may be NULL.
+hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w_router,
+                        const float* bias, float* logits, float* topk_w, int32_t* topk_idx,
+                        float* partials, int S, hipStream_t stream);
+
+// ---- dispatch (permute.hip)
+// Slots handled by one dispatch block, and the number of blocks.
+int permute_chunk(int TK);
+int permute_blocks(int TK);
+// block_counts/block_base: [nblk, E] int32 scratch each.
+// ext_offsets (may be NULL): [E+2] = {0, n_ident, n_ident + offsets[0..E]} where n_ident
+// rows of identity (shared expert) precede the routed rows; written when n_ident > 0.
+hipError_t launch_permute(const moe_shape& s, const int32_t* topk_idx, int32_t* counts,
+                          int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                          int32_t* block_counts, int32_t* block_base, int32_t* ext_offsets,
+                          int n_ident, hipStream_t stream);
+
+// ---- grouped FFN (ffn.hip)
+// Tile table: tiles[0] = number of tiles, tiles[1 + i] = group, tiles[1 + max + i] = first row.
+size_t tile_table_bytes(int max_tiles);
+int max_tiles_for(int rows_max, int n_groups, int bm);
+// Writes {0, rows} into offsets[0..1] (a one-group offsets array on the device).
+hipError_t launch_single_group_offsets(int32_t* offsets, int rows, hipStream_t stream);
+
+struct FfnProblem {
+  const uint16_t* x;          // [T, H] activations
+  int32_t T;
+  const int32_t* gather;      // row_to_slot (NULL: no gathered rows)
+  int32_t n_ident;            // rows r < n_ident read x row r; others x row gather[r-n_ident]/K
+  int32_t topk;               // K
+  const int32_t* offsets;     // [G+1] group row offsets on the device
+  int32_t n_groups;           // G
+  int32_t rows_max;           // bound on offsets[G]
+  int32_t g_split;            // groups < g_split take the *_a weights, others *_b
+  const uint16_t *gate_a, *gate_b, *up_a, *up_b, *down_a, *down_b;
+  int32_t H, I;
+  float limit;
+  uint16_t* h;                // [rows_max, I]
+  uint16_t* y;                // [rows_max, H]
+  int32_t* tiles;             // tile table scratch (tile_table_bytes(max_tiles_for(...)))
+};
+// ev (may be NULL): three events recorded after the tile table, the gate/up GEMM and the
+// down GEMM (each entry may be NULL).
+hipError_t launch_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t const* ev = nullptr);
+
+// ---- combine (combine.hip)
+hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,
+                          const int32_t* slot_to_row, const uint16_t* y_shared, uint16_t* out,
+                          hipStream_t stream);
+
+}  // namespace moe

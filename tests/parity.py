@@ -1,0 +1,156 @@
+"""Helpers shared by the GPU parity tests: tolerance checks and GPU/oracle runners.
+
+Tolerances (stated where the pages and the layer's definition leave them open):
+  * bf16 tensors h, y, y_shared, out: |gpu - oracle| <= 1e-2*|oracle| + 1e-3*rms(oracle),
+    element-wise, rms over the whole compared tensor.
+  * When the oracle computes `out` from its OWN y (not the GPU's), a y element that sits on a
+    bf16 rounding boundary can round one ulp apart on the two sides (fp32 vs fp64 accumulation);
+    such a flip moves out by |w_j| * ulp(y_j). That propagated term is added to the bound for
+    this independent comparison only; the chained comparison (oracle combine of the GPU's y)
+    uses the bare tolerance.
+  * fp32 router logits: |gpu - oracle| <= 1e-4 * rms(oracle) + 1e-5 * |oracle| (fp32
+    accumulation over H terms against a double sum).
+  * fp32 routing weights: |gpu - oracle| <= 1e-5 * routed_scaling.
+  * Integers (indices, counts, offsets, permutation): bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sparse_moe_layer_softmax_amd as moe
+from sparse_moe_layer_softmax_amd.workloads import as_u16
+
+f64 = oracle.bf16_to_f64
+
+
+def ulp_bf16(u16: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at each element (2^(e-7), fixed below the smallest normal)."""
+    e = (np.asarray(u16, np.uint16).astype(np.int64) >> 7) & 0xFF
+    return np.ldexp(1.0, np.maximum(e, 1) - 127 - 7)
+
+
+def bf16_close(got_u16, ref_u16, extra=None):
+    g, r = f64(got_u16), f64(ref_u16)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    tol = 1e-2 * np.abs(r) + 1e-3 * rms
+    if extra is not None:
+        tol = tol + extra
+    ok = np.abs(g - r) <= tol
+    return ok, g, r, tol
+
+
+def assert_bf16_close(got_u16, ref_u16, what, extra=None):
+    got_u16 = np.asarray(got_u16)
+    ref_u16 = np.asarray(ref_u16)
+    assert got_u16.shape == ref_u16.shape, (what, got_u16.shape, ref_u16.shape)
+    ok, g, r, tol = bf16_close(got_u16, ref_u16, extra)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError("%s: %d/%d elements out of tolerance; first at %s: gpu=%r oracle=%r tol=%r"
+                             % (what, len(bad), ok.size, i, g[i], r[i], tol[i]))
+
+
+def assert_logits_close(got, ref, what="logits"):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    tol = 1e-4 * rms + 1e-5 * np.abs(ref)
+    err = np.abs(got - ref)
+    assert np.all(err <= tol), "%s: max err %g (tol at worst %g)" % (what, err.max(), tol.flat[err.argmax()])
+
+
+def margin_ok(probs: np.ndarray, K: int, thresh: float = 1e-4) -> np.ndarray:
+    """Tokens whose k-th / (k+1)-th largest probabilities differ by at least `thresh`."""
+    E = probs.shape[1]
+    if K >= E:
+        return np.ones(probs.shape[0], bool)
+    srt = -np.sort(-probs, axis=1)
+    return (srt[:, K - 1] - srt[:, K]) >= thresh
+
+
+def propagated_y_flip(topk_w, slot_to_row, y_routed_u16, y_shared_u16):
+    """Per-element bound of |w_j| * ulp(y_j) summed over the kept slots, plus ulp(y_shared)."""
+    T, K = topk_w.shape
+    H = y_routed_u16.shape[1]
+    acc = np.zeros((T, H))
+    for j in range(K):
+        rows = slot_to_row.reshape(T, K)[:, j]
+        kept = rows >= 0
+        acc[kept] += np.abs(topk_w[kept, j:j + 1].astype(np.float64)) * ulp_bf16(y_routed_u16[rows[kept]])
+    if y_shared_u16 is not None:
+        acc += ulp_bf16(y_shared_u16)
+    return acc
+
+
+def host(wts: dict) -> dict:
+    """Host copies (uint16 / float32 numpy) of a generated input dict."""
+    out = {}
+    for k, v in wts.items():
+        if v is None:
+            out[k] = None
+        elif v.dtype == torch.bfloat16:
+            out[k] = as_u16(v)
+        else:
+            out[k] = v.detach().cpu().numpy()
+    return out
+
+
+def run_layer_gpu(wl, dev: dict):
+    """moe_layer_forward on the GPU; returns host copies of out and every intermediate."""
+    shape = moe.Shape.of(wl)
+    layer = moe.MoELayer(shape, dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                         dev["s_gate"], dev["s_up"], dev["s_down"], dev["router_bias"])
+    out = layer.forward(dev["x"])
+    torch.cuda.synchronize()
+    T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
+    n_id = T if wl.n_shared else 0
+    rows = n_id + T * K
+    g = dict(
+        out=as_u16(out),
+        logits=layer.intermediate("logits", torch.float32, (T, E)).cpu().numpy(),
+        topk_w=layer.intermediate("topk_w", torch.float32, (T, K)).cpu().numpy(),
+        topk_idx=layer.intermediate("topk_idx", torch.int32, (T, K)).cpu().numpy(),
+        counts=layer.intermediate("counts", torch.int32, (E,)).cpu().numpy(),
+        offsets=layer.intermediate("offsets", torch.int32, (E + 1,)).cpu().numpy(),
+        row_to_slot=layer.intermediate("row_to_slot", torch.int32, (T * K,)).cpu().numpy(),
+        slot_to_row=layer.intermediate("slot_to_row", torch.int32, (T * K,)).cpu().numpy(),
+    )
+    h = layer.intermediate("h", torch.int16, (rows, I)).cpu().numpy().view(np.uint16)
+    y = layer.intermediate("y", torch.int16, (rows, H)).cpu().numpy().view(np.uint16)
+    g["h_shared"], g["h_routed"] = (h[:n_id], h[n_id:]) if n_id else (None, h)
+    g["y_shared"], g["y_routed"] = (y[:n_id], y[n_id:]) if n_id else (None, y)
+    return g, layer, out
+
+
+def oracle_same_logits(wl, hw: dict, logits: np.ndarray) -> dict:
+    """Oracle steps 2-9 from the given fp32 logits (router projection skipped)."""
+    return oracle.layer_forward(
+        hw["x"], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], wl.K,
+        bias=hw["router_bias"], sg=hw["s_gate"], su=hw["s_up"], sd=hw["s_down"], scale=wl.scale,
+        limit=wl.limit, capacity=wl.capacity, norm_topk=wl.norm_topk, logits=logits)
+
+
+def compare_layer(wl, g: dict, r: dict, check_routing_bits: bool = True):
+    """Element-wise comparison of a GPU layer run with the oracle run from the same logits."""
+    if check_routing_bits:
+        np.testing.assert_array_equal(g["topk_idx"], r["topk_idx"], err_msg="topk_idx")
+        np.testing.assert_array_equal(g["counts"], r["counts"], err_msg="counts")
+        np.testing.assert_array_equal(g["offsets"], r["offsets"], err_msg="offsets")
+        np.testing.assert_array_equal(g["row_to_slot"], r["row_to_slot"], err_msg="row_to_slot")
+        np.testing.assert_array_equal(g["slot_to_row"], r["slot_to_row"], err_msg="slot_to_row")
+    np.testing.assert_allclose(g["topk_w"], r["topk_w"], rtol=0, atol=1e-5 * max(wl.scale, 1e-30))
+    R = int(r["offsets"][-1])
+    assert_bf16_close(g["h_routed"][:R], r["h_routed"][:R], "h_routed")
+    assert_bf16_close(g["y_routed"][:R], r["y_routed"][:R], "y_routed")
+    if wl.n_shared:
+        assert_bf16_close(g["h_shared"], r["h_shared"], "h_shared")
+        assert_bf16_close(g["y_shared"], r["y_shared"], "y_shared")
+    # chained: the oracle's combine of the GPU's own rows must match with the bare tolerance
+    chained = oracle.combine(g["topk_w"], g["slot_to_row"], g["y_routed"], g["y_shared"])
+    assert_bf16_close(g["out"], chained, "out (oracle combine of the GPU rows)")
+    # independent: the oracle's own rows, plus the propagated one-ulp y flips
+    extra = propagated_y_flip(r["topk_w"], r["slot_to_row"], r["y_routed"], r.get("y_shared"))
+    assert_bf16_close(g["out"], r["out"], "out (oracle end to end)", extra=extra)

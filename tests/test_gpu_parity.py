@@ -1,0 +1,334 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Small shapes are compared element by element (all tokens, all rows); they span several tiles
+of every kernel and end on ragged tails. Full workload sizes are checked on sampled tokens
+(every routed row of each sampled token, the shared row, the combined output) plus properties
+that hold at any size. Routing integers are compared bit-exactly from the same fp32 logits.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_softmax_amd as moe
+from sparse_moe_layer_softmax_amd.workloads import WORKLOADS, Workload, as_u16, capacity_for, from_u16, generate
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+
+
+BASE = WORKLOADS["tiny_t128_h512_e32_k2"]
+SMALL = {
+    "tiny_t128_h512_e32_k2": BASE,
+    "ragged_t130_h256_e256_k8": Workload("ragged_t130_h256_e256_k8", T=130, H=256, E=256, K=8, I=256,
+                                         scale=2.827, w_std=0.02, router_std=0.02, seed=11),
+    "single_token_t1_e256_k8": Workload("single_token_t1_e256_k8", T=1, H=256, E=256, K=8, I=512,
+                                        scale=2.827, w_std=0.02, router_std=0.02, seed=12),
+    "t3_e64_k6": Workload("t3_e64_k6", T=3, H=512, E=64, K=6, I=256, scale=2.827, seed=13),
+    "dense_e1_k1_t100": Workload("dense_e1_k1_t100", T=100, H=512, E=1, K=1, I=256, n_shared=0,
+                                 seed=14),
+    "no_shared_t128": BASE.with_(name="no_shared_t128", n_shared=0, seed=15),
+    "no_renorm_t128": BASE.with_(name="no_renorm_t128", norm_topk=False, scale=2.827, seed=16),
+    "capacity_drops_t200_e8_k2": Workload("capacity_drops_t200_e8_k2", T=200, H=256, E=8, K=2, I=256,
+                                          capacity=30, zipf=0.3, seed=17),
+    "capacity_t256_h512_e32_k2": Workload("capacity_t256_h512_e32_k2", T=256, H=512, E=32, K=2, I=512,
+                                          limit=0.0, capacity=capacity_for(256, 2, 32),
+                                          w_std=0.006, router_std=0.006, seed=18),
+    "clamp_forced_t128": BASE.with_(name="clamp_forced_t128", x_std=30.0, seed=19),
+    "multi_tile_t300_e16_k4": Workload("multi_tile_t300_e16_k4", T=300, H=512, E=16, K=4, I=256,
+                                       scale=2.827, seed=20),
+}
+
+
+# ----------------------------------------------------------------------------- end to end, small
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_forward_small(name):
+    _require_gpu()
+    wl = SMALL[name]
+    dev = generate(wl, DEV)
+    hw = P.host(dev)
+    g, _, _ = P.run_layer_gpu(wl, dev)
+    # logits against the oracle's own projection
+    lo = oracle.router_logits(hw["x"], hw["w_router"], hw["router_bias"])
+    P.assert_logits_close(g["logits"], lo)
+    # same-logits mode: every routing integer bit-exact, every tensor in tolerance
+    r = P.oracle_same_logits(wl, hw, g["logits"])
+    P.compare_layer(wl, g, r)
+    # independent logits: indices agree on every token with a clear k-th / (k+1)-th margin
+    idx_i, _, probs = oracle.route_from_logits(lo, wl.K, wl.scale, wl.norm_topk, want_probs=True)
+    ok = P.margin_ok(probs, wl.K)
+    np.testing.assert_array_equal(g["topk_idx"][ok], idx_i[ok])
+    if name == "capacity_drops_t200_e8_k2":
+        assert (g["slot_to_row"] < 0).sum() > 0, "this case must drop slots"
+    if name == "clamp_forced_t128":
+        hv = P.f64(g["h_routed"][: int(g["offsets"][-1])])
+        assert np.abs(hv).max() > 50, "this case must reach the clamp"
+
+
+def test_layer_is_deterministic():
+    _require_gpu()
+    wl = SMALL["ragged_t130_h256_e256_k8"]
+    dev = generate(wl, DEV)
+    g1, layer, _ = P.run_layer_gpu(wl, dev)
+    outs = []
+    for _ in range(3):
+        outs.append(as_u16(layer.forward(dev["x"])))
+    torch.cuda.synchronize()
+    for o in outs:
+        np.testing.assert_array_equal(o, g1["out"])
+
+
+def test_exact_logit_ties_go_to_lower_expert():
+    _require_gpu()
+    wl = SMALL["ragged_t130_h256_e256_k8"].with_(name="ties", seed=21)
+    dev = generate(wl, DEV)
+    # duplicate router rows: expert 2e+1 gets expert 2e's row, so their logits are bit-equal
+    wr = dev["w_router"].clone()
+    wr[1::2] = wr[0::2]
+    dev["w_router"] = wr
+    hw = P.host(dev)
+    g, _, _ = P.run_layer_gpu(wl, dev)
+    np.testing.assert_array_equal(g["logits"][:, 0::2], g["logits"][:, 1::2])
+    r = P.oracle_same_logits(wl, hw, g["logits"])
+    P.compare_layer(wl, g, r)
+    # each selected odd expert is preceded by its even twin
+    for t in range(wl.T):
+        sel = list(g["topk_idx"][t])
+        for e in sel:
+            if e % 2 == 1:
+                assert e - 1 in sel and sel.index(e - 1) < sel.index(e)
+
+
+def test_zero_input():
+    _require_gpu()
+    wl = SMALL["t3_e64_k6"].with_(name="zero", T=5)
+    dev = generate(wl, DEV)
+    dev["x"] = torch.zeros_like(dev["x"])
+    g, _, _ = P.run_layer_gpu(wl, dev)
+    assert np.all(g["topk_idx"] == np.arange(wl.K))
+    np.testing.assert_allclose(g["topk_w"], wl.scale / wl.K, rtol=1e-6)
+    assert np.all((g["out"] & 0x7FFF) == 0)
+
+
+# ----------------------------------------------------------------------------- per entry point
+def _ws(n):
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8", "no_renorm_t128"])
+def test_moe_route(name):
+    _require_gpu()
+    wl = SMALL[name]
+    dev = generate(wl, DEV)
+    hw = P.host(dev)
+    s = moe.Shape.of(wl)
+    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=DEV)
+    w = torch.empty((wl.T, wl.K), dtype=torch.float32, device=DEV)
+    idx = torch.empty((wl.T, wl.K), dtype=torch.int32, device=DEV)
+    moe.moe_route(s, dev["x"], dev["w_router"], dev["router_bias"], logits, w, idx,
+                  _ws(moe.moe_route_workspace_size(s)))
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    P.assert_logits_close(lg, oracle.router_logits(hw["x"], hw["w_router"], hw["router_bias"]))
+    ri, rw = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ri)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=0, atol=1e-5 * wl.scale)
+    # logits pointer is optional
+    w2 = torch.empty_like(w)
+    idx2 = torch.empty_like(idx)
+    moe.moe_route(s, dev["x"], dev["w_router"], dev["router_bias"], None, w2, idx2,
+                  _ws(moe.moe_route_workspace_size(s)))
+    torch.cuda.synchronize()
+    assert torch.equal(idx2, idx) and torch.equal(w2, w)
+
+
+@pytest.mark.parametrize("T,K,E,C", [(128, 2, 32, 0), (130, 8, 256, 0), (1, 8, 256, 0),
+                                     (200, 2, 8, 30), (4096, 2, 32, 320), (65536, 8, 256, 0),
+                                     (40000, 8, 256, 1200)])
+def test_moe_permute(T, K, E, C):
+    _require_gpu()
+    rng = np.random.default_rng(T + K + E + C)
+    pop = np.exp(-0.08 * np.arange(E))  # skewed popularity, empty experts likely when E is large
+    pop /= pop.sum()
+    # k distinct experts per token, drawn without replacement by Gumbel-top-k on log popularity
+    keys = np.log(pop)[None, :] + rng.gumbel(size=(T, E))
+    idx = np.argsort(-keys, axis=1)[:, :K].astype(np.int32)
+    s = moe.Shape(T=T, H=256, E=E, K=K, I=256, capacity=C)
+    d_idx = torch.from_numpy(idx).to(DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    r2s = torch.full((T * K,), 7, dtype=torch.int32, device=DEV)
+    s2r = torch.full((T * K,), 7, dtype=torch.int32, device=DEV)
+    moe.moe_permute(s, d_idx, counts, offsets, r2s, s2r, _ws(moe.moe_permute_workspace_size(s)))
+    torch.cuda.synchronize()
+    rc, ro, rr, rs = oracle.dispatch(idx, E, C)
+    np.testing.assert_array_equal(counts.cpu().numpy(), rc)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ro)
+    np.testing.assert_array_equal(r2s.cpu().numpy(), rr)
+    np.testing.assert_array_equal(s2r.cpu().numpy(), rs)
+    if C:
+        assert rc.max() <= C
+
+
+@pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8",
+                                  "clamp_forced_t128", "multi_tile_t300_e16_k4"])
+def test_moe_expert_ffn_routed_and_identity(name):
+    _require_gpu()
+    wl = SMALL[name]
+    dev = generate(wl, DEV)
+    hw = P.host(dev)
+    s = moe.Shape.of(wl)
+    lo = oracle.router_logits(hw["x"], hw["w_router"], hw["router_bias"])
+    idx, w = oracle.route_from_logits(lo, wl.K, wl.scale, wl.norm_topk)
+    counts, offsets, r2s, s2r = oracle.dispatch(idx, wl.E, wl.capacity)
+    TK = wl.T * wl.K
+    h = torch.empty((TK, wl.I), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((TK, wl.H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_ffn(s, wl.E, TK, dev["x"], torch.from_numpy(r2s).to(DEV),
+                       torch.from_numpy(offsets).to(DEV), dev["w_gate"], dev["w_up"], dev["w_down"],
+                       h, y, _ws(moe.moe_expert_ffn_workspace_size(s, wl.E, TK)))
+    torch.cuda.synchronize()
+    R = int(offsets[-1])
+    hg, yg = as_u16(h)[:R], as_u16(y)[:R]
+    for e in range(wl.E):
+        a, b = offsets[e], offsets[e + 1]
+        if a == b:
+            continue
+        xr = hw["x"][r2s[a:b] // wl.K]
+        rh, ry = oracle.expert_ffn_rows(xr, hw["w_gate"][e], hw["w_up"][e], hw["w_down"][e], wl.limit)
+        P.assert_bf16_close(hg[a:b], rh, "h expert %d" % e)
+        P.assert_bf16_close(yg[a:b], ry, "y expert %d" % e)
+    # identity rows, one group, no offsets: the shared-expert form; h kept in the workspace
+    ys = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_expert_ffn(s, 1, wl.T, dev["x"], None, None, dev["s_gate"][None], dev["s_up"][None],
+                       dev["s_down"][None], None, ys, _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
+    torch.cuda.synchronize()
+    _, rys = oracle.expert_ffn_rows(hw["x"], hw["s_gate"], hw["s_up"], hw["s_down"], wl.limit)
+    P.assert_bf16_close(as_u16(ys), rys, "identity-row FFN")
+
+
+@pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "capacity_drops_t200_e8_k2", "no_shared_t128"])
+def test_moe_combine(name):
+    _require_gpu()
+    wl = SMALL[name]
+    rng = np.random.default_rng(31)
+    lo = (rng.standard_normal((wl.T, wl.E)) * 0.5).astype(np.float32)
+    idx, w = oracle.route_from_logits(lo, wl.K, 2.827)
+    counts, offsets, r2s, s2r = oracle.dispatch(idx, wl.E, wl.capacity)
+    R = int(offsets[-1])
+    yr = as_u16((torch.randn(max(R, 1), wl.H) * 0.3).to(torch.bfloat16))
+    ysh = as_u16((torch.randn(wl.T, wl.H) * 0.3).to(torch.bfloat16)) if wl.n_shared else None
+    s = moe.Shape.of(wl)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    moe.moe_combine(s, from_u16(yr, DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s2r).to(DEV),
+                    None if ysh is None else from_u16(ysh, DEV), out)
+    torch.cuda.synchronize()
+    P.assert_bf16_close(as_u16(out), oracle.combine(w, s2r, yr, ysh), "combine")
+
+
+# ----------------------------------------------------------------------------- full sizes, sampled
+FULL = ["hy4_decode_t64", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2", "hy4_skew_t65536"]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    _require_gpu()
+    wl = WORKLOADS[name]
+    print("\n[full-size] %s T=%d H=%d E=%d K=%d I=%d" % (name, wl.T, wl.H, wl.E, wl.K, wl.I), flush=True)
+    dev = generate(wl, DEV)
+    shape = moe.Shape.of(wl)
+    layer = moe.MoELayer(shape, dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
+                         dev["s_gate"], dev["s_up"], dev["s_down"], dev["router_bias"])
+    out = layer.forward(dev["x"])
+    torch.cuda.synchronize()
+    T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
+    n_id = T if wl.n_shared else 0
+    logits = layer.intermediate("logits", torch.float32, (T, E)).cpu().numpy()
+    g_idx = layer.intermediate("topk_idx", torch.int32, (T, K)).cpu().numpy()
+    g_w = layer.intermediate("topk_w", torch.float32, (T, K)).cpu().numpy()
+    g_counts = layer.intermediate("counts", torch.int32, (E,)).cpu().numpy()
+    g_off = layer.intermediate("offsets", torch.int32, (E + 1,)).cpu().numpy()
+    g_r2s = layer.intermediate("row_to_slot", torch.int32, (T * K,)).cpu().numpy()
+    g_s2r = layer.intermediate("slot_to_row", torch.int32, (T * K,)).cpu().numpy()
+    h_all = layer.intermediate("h", torch.bfloat16, (n_id + T * K, I))
+    y_all = layer.intermediate("y", torch.bfloat16, (n_id + T * K, H))
+
+    # routing from the same fp32 logits: bit-exact on every token
+    r_idx, r_w = oracle.route_from_logits(logits, K, wl.scale, wl.norm_topk)
+    np.testing.assert_array_equal(g_idx, r_idx)
+    np.testing.assert_allclose(g_w, r_w, rtol=0, atol=1e-5 * wl.scale)
+    rc, ro, rr, rs = oracle.dispatch(r_idx, E, wl.capacity)
+    np.testing.assert_array_equal(g_counts, rc)
+    np.testing.assert_array_equal(g_off, ro)
+    np.testing.assert_array_equal(g_r2s, rr)
+    np.testing.assert_array_equal(g_s2r, rs)
+    # properties at any size
+    np.testing.assert_allclose(g_w.astype(np.float64).sum(1), wl.scale, rtol=1e-5)
+    R = int(g_off[-1])
+    assert R == T * K - int((g_s2r < 0).sum())
+    np.testing.assert_array_equal(np.sort(g_r2s[:R]), np.sort(np.nonzero(g_s2r >= 0)[0]))
+
+    # sampled tokens: logits, every routed row, the shared row and the output
+    rng = np.random.default_rng(1234)
+    n_s = 8 if T <= 64 else 5
+    toks = np.sort(rng.choice(T, n_s, replace=False))
+    if wl.capacity:
+        dropped_tok = np.nonzero((g_s2r < 0).reshape(T, K).any(1))[0]
+        if len(dropped_tok):
+            toks = np.unique(np.concatenate([toks, dropped_tok[:1]]))
+    x_s = as_u16(dev["x"][torch.from_numpy(toks).to(DEV)])
+    bias = None if dev["router_bias"] is None else dev["router_bias"].cpu().numpy()
+    lo_s = oracle.router_logits(x_s, as_u16(dev["w_router"]), bias)
+    P.assert_logits_close(logits[toks], lo_s, "sampled logits")
+    _, _, probs = oracle.route_from_logits(lo_s, K, wl.scale, wl.norm_topk, want_probs=True)
+    ok = P.margin_ok(probs, K)
+    idx_i, _ = oracle.route_from_logits(lo_s, K, wl.scale, wl.norm_topk)
+    np.testing.assert_array_equal(g_idx[toks][ok], idx_i[ok])
+
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = (as_u16(dev["w_gate"][e]), as_u16(dev["w_up"][e]), as_u16(dev["w_down"][e]))
+        return cache[e]
+
+    for i, t in enumerate(toks):
+        rows = g_s2r[t * K:(t + 1) * K]
+        kept = [j for j in range(K) if rows[j] >= 0]
+        sel = torch.from_numpy((n_id + rows[kept]).astype(np.int64)).to(DEV)
+        gh = as_u16(h_all[sel])
+        gy = as_u16(y_all[sel])
+        ry = np.zeros((max(R, 1), H), np.uint16)
+        for n, j in enumerate(kept):
+            wg_, wu_, wd_ = expert(int(g_idx[t, j]))
+            rh1, ry1 = oracle.expert_ffn_rows(x_s[i:i + 1], wg_, wu_, wd_, wl.limit)
+            P.assert_bf16_close(gh[n:n + 1], rh1, "h token %d slot %d" % (t, j))
+            P.assert_bf16_close(gy[n:n + 1], ry1, "y token %d slot %d" % (t, j))
+            ry[rows[j]] = ry1[0]
+        ys_r = None
+        if wl.n_shared:
+            rhs, ys_r = oracle.expert_ffn_rows(x_s[i:i + 1], as_u16(dev["s_gate"]), as_u16(dev["s_up"]),
+                                               as_u16(dev["s_down"]), wl.limit)
+            P.assert_bf16_close(as_u16(h_all[int(t):int(t) + 1]), rhs, "h_shared token %d" % t)
+            P.assert_bf16_close(as_u16(y_all[int(t):int(t) + 1]), ys_r, "y_shared token %d" % t)
+        g_out = as_u16(out[int(t):int(t) + 1])
+        w1 = g_w[t:t + 1]
+        s2r1 = g_s2r[t * K:(t + 1) * K]
+        # chained: oracle combine of the GPU rows
+        gy_full = np.zeros((max(R, 1), H), np.uint16)
+        gy_full[rows[kept]] = gy
+        gys = as_u16(y_all[int(t):int(t) + 1]) if wl.n_shared else None
+        P.assert_bf16_close(g_out, oracle.combine(w1, s2r1, gy_full, gys), "out (chained) token %d" % t)
+        # independent: oracle rows, with the one-ulp y-flip propagation term
+        r_out = oracle.combine(w1, s2r1, ry, ys_r)
+        extra = P.propagated_y_flip(w1, s2r1, ry, ys_r)
+        P.assert_bf16_close(g_out, r_out, "out (end to end) token %d" % t, extra=extra)
