@@ -15,6 +15,13 @@
 // projection (so the SwiGLU epilogue pairs them in registers), or 32 columns of the down
 // projection. Weight fragments are loaded straight from HBM with 16-byte loads in MFMA operand
 // order: this is the weight-streaming path for small row counts per expert.
+//
+// Kernel "tiled": 128-row x 128-column tiles, K staged through LDS 64 at a time (double
+// buffered, one barrier per K step), four wavefronts of 64x64 on MFMA 32x32x16. The LDS rows
+// are XOR-swizzled by 16-byte chunk so the MFMA operand reads are bank-conflict free. For the
+// gate/up projection the 128 weight rows of a tile are 64 gate rows and the 64 matching up rows,
+// interleaved by 32 so that each wavefront's accumulators hold matching gate and up columns and
+// the SwiGLU epilogue stays in registers. This is the MFMA-bound path for large row counts.
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -23,7 +30,7 @@ namespace {
 
 constexpr int kSkinnyRows = 64;
 
-struct SkinnyParams {
+struct GroupedParams {
   const uint16_t* A;        // activation rows: x [T, Kd] (gate/up) or h [rows, Kd] (down)
   int32_t a_rows;           // rows of A (bounds the gathered row index)
   const int32_t* gather;    // row_to_slot
@@ -84,7 +91,7 @@ __global__ void single_group_offsets_kernel(int32_t* offsets, int rows) {
 }
 
 template <bool GATED, int NS>
-__device__ __forceinline__ void skinny_tile(const SkinnyParams& p, int g, int r0, int r1,
+__device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r0, int r1,
                                             int col0) {
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15, lk = (lane >> 4) * 8;
@@ -164,7 +171,7 @@ __device__ __forceinline__ void skinny_tile(const SkinnyParams& p, int g, int r0
 }
 
 template <bool GATED>
-__global__ __launch_bounds__(256) void ffn_skinny_kernel(SkinnyParams p) {
+__global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
   const int tile = blockIdx.x;
   if (tile >= p.tiles[0]) return;
   const int g = p.tiles[1 + tile];
@@ -182,6 +189,136 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(SkinnyParams p) {
   }
 }
 
+
+constexpr int kTileM = 128;  // rows per tile
+constexpr int kTileN = 128;  // weight rows per tile (gate/up: 64 gate + 64 up)
+constexpr int kTileK = 64;   // reduction elements per LDS stage
+
+// LDS element offset of (row, k) inside a [rows][64] bf16 stage, 16-byte chunks XOR-swizzled.
+__device__ __forceinline__ int swz(int row, int k) {
+  return row * kTileK + ((((k >> 3) ^ (row & 7))) << 3) + (k & 7);
+}
+
+template <bool GATED>
+__global__ __launch_bounds__(256, 2) void ffn_tiled_kernel(GroupedParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kTileM * kTileK];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kTileN * kTileK];
+
+  const int tile = blockIdx.x;
+  if (tile >= p.tiles[0]) return;
+  const int g = p.tiles[1 + tile];
+  const int r0 = p.tiles[1 + p.max_tiles + tile];
+  const int r1 = min(min(r0 + kTileM, p.offsets[g + 1]), p.rows_max);
+  if (r0 < 0 || r1 <= r0) return;
+  const int Kd = p.Kd;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---- global -> LDS assignment: thread loads 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 i
+  const int lch = tid & 7;
+  const uint16_t* ga[4];
+  bool gav[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + (tid >> 3) + 32 * i;
+    gav[i] = r < r1;
+    int src = 0;
+    if (gav[i]) src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
+    if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) {
+      gav[i] = false;
+      src = 0;
+    }
+    ga[i] = p.A + static_cast<size_t>(src) * Kd + lch * 8;
+  }
+  const size_t wst = static_cast<size_t>(p.N) * Kd;
+  const uint16_t* W0 = g < p.g_split ? p.W0a + g * wst : p.W0b + (g - p.g_split) * wst;
+  const uint16_t* W1 = nullptr;
+  if (GATED) W1 = g < p.g_split ? p.W1a + g * wst : p.W1b + (g - p.g_split) * wst;
+  const uint16_t* gb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = (tid >> 3) + 32 * i;  // B tile row
+    if (GATED) {
+      const int w = b & 63;
+      const int col = blockIdx.y * 64 + (b >> 6) * 32 + (w & 31);
+      gb[i] = (w < 32 ? W0 : W1) + static_cast<size_t>(col) * Kd + lch * 8;
+    } else {
+      gb[i] = W0 + static_cast<size_t>(blockIdx.y * kTileN + b) * Kd + lch * 8;
+    }
+  }
+  int soff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) soff[i] = swz((tid >> 3) + 32 * i, lch * 8);
+
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  u32x4_t ra[4], rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ra[i] = gav[i] ? ld16(ga[i] + k0) : zero;
+      rb[i] = ld16(gb[i] + k0);
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4_t*>(&sA[buf][soff[i]]) = ra[i];
+      *reinterpret_cast<u32x4_t*>(&sB[buf][soff[i]]) = rb[i];
+    }
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int nk = Kd / kTileK;
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * kTileK);
+#pragma unroll
+    for (int ks = 0; ks < kTileK / 16; ++ks) {
+      u32x4_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const u32x4_t*>(&sA[buf][swz(wm * 64 + i * 32 + fr, ks * 16 + fk)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const u32x4_t*>(&sB[buf][swz(wn * 64 + j * 32 + fr, ks * 16 + fk)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+    }
+    if (kt + 1 < nk) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = r0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      if (r >= r1) continue;
+      uint16_t* o = p.out + static_cast<size_t>(r) * p.N;
+      if (GATED) {
+        o[blockIdx.y * 64 + wn * 32 + fr] = f32_to_bf16(clamped_swiglu(acc[i][0][v], acc[i][1][v], p.limit));
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) o[blockIdx.y * kTileN + wn * 64 + j * 32 + fr] = f32_to_bf16(acc[i][j][v]);
+      }
+    }
+}
+
 }  // namespace
 
 size_t tile_table_bytes(int max_tiles) { return sizeof(int32_t) * (1 + 2 * static_cast<size_t>(max_tiles)); }
@@ -197,13 +334,15 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   auto mark = [&](int i) {
     if (ev && ev[i]) hipEventRecord(ev[i], stream);
   };
-  const int bm = kSkinnyRows;
+  // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA.
+  const bool tiled = q.rows_max >= 64 * q.n_groups;
+  const int bm = tiled ? kTileM : kSkinnyRows;
   const int max_tiles = max_tiles_for(q.rows_max, q.n_groups, bm);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, q.offsets, q.n_groups, bm,
                      max_tiles, q.tiles);
   mark(0);
 
-  SkinnyParams p{};
+  GroupedParams p{};
   p.gather = q.gather;
   p.rows_max = q.rows_max;
   p.n_ident = q.n_ident;
@@ -224,7 +363,10 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.out = q.h;
   p.N = q.I;
   p.Kd = q.H;
-  hipLaunchKernelGGL(ffn_skinny_kernel<true>, dim3(max_tiles, q.I / 64), dim3(256), 0, stream, p);
+  if (tiled)
+    hipLaunchKernelGGL(ffn_tiled_kernel<true>, dim3(max_tiles, q.I / 64), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(ffn_skinny_kernel<true>, dim3(max_tiles, q.I / 64), dim3(256), 0, stream, p);
   mark(1);
 
   // down -> y (h rows are already in row order: identity gather)
@@ -238,7 +380,10 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.out = q.y;
   p.N = q.H;
   p.Kd = q.I;
-  hipLaunchKernelGGL(ffn_skinny_kernel<false>, dim3(max_tiles, q.H / 128), dim3(256), 0, stream, p);
+  if (tiled)
+    hipLaunchKernelGGL(ffn_tiled_kernel<false>, dim3(max_tiles, q.H / kTileN), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(ffn_skinny_kernel<false>, dim3(max_tiles, q.H / 128), dim3(256), 0, stream, p);
   mark(2);
   return hipGetLastError();
 }

@@ -3,11 +3,15 @@
 Tolerances (stated where the pages and the layer's definition leave them open):
   * bf16 tensors h, y, y_shared, out: |gpu - oracle| <= 1e-2*|oracle| + 1e-3*rms(oracle),
     element-wise, rms over the whole compared tensor.
-  * When the oracle computes `out` from its OWN y (not the GPU's), a y element that sits on a
-    bf16 rounding boundary can round one ulp apart on the two sides (fp32 vs fp64 accumulation);
-    such a flip moves out by |w_j| * ulp(y_j). That propagated term is added to the bound for
-    this independent comparison only; the chained comparison (oracle combine of the GPU's y)
-    uses the bare tolerance.
+  * Chained checks (the bar): every bf16 tensor is compared with the oracle applied to the SAME
+    bf16 inputs the GPU stage consumed (h from x; y from the GPU's h; out from the GPU's y and
+    y_shared), with the bare tolerance above.
+  * Independent checks (consistency): the oracle's own chain from x. An element that lies on a
+    bf16 rounding boundary can round one ulp apart on the two sides (fp32 vs fp64 accumulation),
+    and the next linear map carries that difference on. So the bound for y adds
+    sum_i |h_gpu - h_oracle|_i * |Wd[c,i]|, and the bound for out adds
+    sum_j |w_j| * |y_gpu - y_oracle|_j + |y_shared_gpu - y_shared_oracle|: the measured upstream
+    differences propagated through the layer's own maps.
   * fp32 router logits: |gpu - oracle| <= 1e-4 * rms(oracle) + 1e-5 * |oracle| (fp32
     accumulation over H terms against a double sum).
   * fp32 routing weights: |gpu - oracle| <= 1e-5 * routed_scaling.
@@ -71,17 +75,24 @@ def margin_ok(probs: np.ndarray, K: int, thresh: float = 1e-4) -> np.ndarray:
     return (srt[:, K - 1] - srt[:, K]) >= thresh
 
 
-def propagated_y_flip(topk_w, slot_to_row, y_routed_u16, y_shared_u16):
-    """Per-element bound of |w_j| * ulp(y_j) summed over the kept slots, plus ulp(y_shared)."""
+def propagated_h_diff(h_gpu_u16, h_orc_u16, wd_u16):
+    """sum_i |h_gpu - h_oracle|_i * |Wd[c, i]| for each row and output column c."""
+    dh = np.abs(f64(h_gpu_u16) - f64(h_orc_u16))
+    return dh @ np.abs(f64(wd_u16)).T
+
+
+def propagated_y_diff(topk_w, slot_to_row, y_gpu_u16, y_orc_u16, ys_gpu_u16=None, ys_orc_u16=None):
+    """sum over kept slots of |w_j| * |y_gpu - y_oracle| (row of slot j), plus the shared row's."""
     T, K = topk_w.shape
-    H = y_routed_u16.shape[1]
+    H = y_gpu_u16.shape[1]
     acc = np.zeros((T, H))
+    dy = np.abs(f64(y_gpu_u16) - f64(y_orc_u16))
     for j in range(K):
         rows = slot_to_row.reshape(T, K)[:, j]
         kept = rows >= 0
-        acc[kept] += np.abs(topk_w[kept, j:j + 1].astype(np.float64)) * ulp_bf16(y_routed_u16[rows[kept]])
-    if y_shared_u16 is not None:
-        acc += ulp_bf16(y_shared_u16)
+        acc[kept] += np.abs(topk_w[kept, j:j + 1].astype(np.float64)) * dy[rows[kept]]
+    if ys_gpu_u16 is not None:
+        acc += np.abs(f64(ys_gpu_u16) - f64(ys_orc_u16))
     return acc
 
 
@@ -133,7 +144,7 @@ def oracle_same_logits(wl, hw: dict, logits: np.ndarray) -> dict:
         limit=wl.limit, capacity=wl.capacity, norm_topk=wl.norm_topk, logits=logits)
 
 
-def compare_layer(wl, g: dict, r: dict, check_routing_bits: bool = True):
+def compare_layer(wl, hw: dict, g: dict, r: dict, check_routing_bits: bool = True):
     """Element-wise comparison of a GPU layer run with the oracle run from the same logits."""
     if check_routing_bits:
         np.testing.assert_array_equal(g["topk_idx"], r["topk_idx"], err_msg="topk_idx")
@@ -143,14 +154,28 @@ def compare_layer(wl, g: dict, r: dict, check_routing_bits: bool = True):
         np.testing.assert_array_equal(g["slot_to_row"], r["slot_to_row"], err_msg="slot_to_row")
     np.testing.assert_allclose(g["topk_w"], r["topk_w"], rtol=0, atol=1e-5 * max(wl.scale, 1e-30))
     R = int(r["offsets"][-1])
+    off = r["offsets"]
+    # h from x: both sides start from the same bf16 x
     assert_bf16_close(g["h_routed"][:R], r["h_routed"][:R], "h_routed")
-    assert_bf16_close(g["y_routed"][:R], r["y_routed"][:R], "y_routed")
+    # y, chained (oracle down projection of the GPU's h) and independent (oracle's own h)
+    for e in range(wl.E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a == b:
+            continue
+        wd = hw["w_down"][e]
+        assert_bf16_close(g["y_routed"][a:b], oracle.down_rows(g["h_routed"][a:b], wd),
+                          "y_routed expert %d (chained)" % e)
+        assert_bf16_close(g["y_routed"][a:b], r["y_routed"][a:b], "y_routed expert %d (end to end)" % e,
+                          extra=propagated_h_diff(g["h_routed"][a:b], r["h_routed"][a:b], wd))
     if wl.n_shared:
         assert_bf16_close(g["h_shared"], r["h_shared"], "h_shared")
-        assert_bf16_close(g["y_shared"], r["y_shared"], "y_shared")
-    # chained: the oracle's combine of the GPU's own rows must match with the bare tolerance
+        assert_bf16_close(g["y_shared"], oracle.down_rows(g["h_shared"], hw["s_down"]), "y_shared (chained)")
+        assert_bf16_close(g["y_shared"], r["y_shared"], "y_shared (end to end)",
+                          extra=propagated_h_diff(g["h_shared"], r["h_shared"], hw["s_down"]))
+    # out, chained: the oracle's combine of the GPU's own rows, bare tolerance
     chained = oracle.combine(g["topk_w"], g["slot_to_row"], g["y_routed"], g["y_shared"])
-    assert_bf16_close(g["out"], chained, "out (oracle combine of the GPU rows)")
-    # independent: the oracle's own rows, plus the propagated one-ulp y flips
-    extra = propagated_y_flip(r["topk_w"], r["slot_to_row"], r["y_routed"], r.get("y_shared"))
-    assert_bf16_close(g["out"], r["out"], "out (oracle end to end)", extra=extra)
+    assert_bf16_close(g["out"], chained, "out (chained)")
+    # out, independent: the oracle's own rows plus the propagated y differences
+    extra = propagated_y_diff(r["topk_w"], r["slot_to_row"], g["y_routed"], r["y_routed"],
+                              g.get("y_shared"), r.get("y_shared"))
+    assert_bf16_close(g["out"], r["out"], "out (end to end)", extra=extra)

@@ -61,7 +61,7 @@ def test_layer_forward_small(name):
     P.assert_logits_close(g["logits"], lo)
     # same-logits mode: every routing integer bit-exact, every tensor in tolerance
     r = P.oracle_same_logits(wl, hw, g["logits"])
-    P.compare_layer(wl, g, r)
+    P.compare_layer(wl, hw, g, r)
     # independent logits: indices agree on every token with a clear k-th / (k+1)-th margin
     idx_i, _, probs = oracle.route_from_logits(lo, wl.K, wl.scale, wl.norm_topk, want_probs=True)
     ok = P.margin_ok(probs, wl.K)
@@ -98,7 +98,7 @@ def test_exact_logit_ties_go_to_lower_expert():
     g, _, _ = P.run_layer_gpu(wl, dev)
     np.testing.assert_array_equal(g["logits"][:, 0::2], g["logits"][:, 1::2])
     r = P.oracle_same_logits(wl, hw, g["logits"])
-    P.compare_layer(wl, g, r)
+    P.compare_layer(wl, hw, g, r)
     # each selected odd expert is preceded by its even twin
     for t in range(wl.T):
         sel = list(g["topk_idx"][t])
@@ -312,23 +312,32 @@ def test_full_size_sampled(name):
             wg_, wu_, wd_ = expert(int(g_idx[t, j]))
             rh1, ry1 = oracle.expert_ffn_rows(x_s[i:i + 1], wg_, wu_, wd_, wl.limit)
             P.assert_bf16_close(gh[n:n + 1], rh1, "h token %d slot %d" % (t, j))
-            P.assert_bf16_close(gy[n:n + 1], ry1, "y token %d slot %d" % (t, j))
+            P.assert_bf16_close(gy[n:n + 1], oracle.down_rows(gh[n:n + 1], wd_),
+                                "y token %d slot %d (chained)" % (t, j))
+            P.assert_bf16_close(gy[n:n + 1], ry1, "y token %d slot %d (end to end)" % (t, j),
+                                extra=P.propagated_h_diff(gh[n:n + 1], rh1, wd_))
             ry[rows[j]] = ry1[0]
         ys_r = None
         if wl.n_shared:
+            sd_ = as_u16(dev["s_down"])
             rhs, ys_r = oracle.expert_ffn_rows(x_s[i:i + 1], as_u16(dev["s_gate"]), as_u16(dev["s_up"]),
-                                               as_u16(dev["s_down"]), wl.limit)
-            P.assert_bf16_close(as_u16(h_all[int(t):int(t) + 1]), rhs, "h_shared token %d" % t)
-            P.assert_bf16_close(as_u16(y_all[int(t):int(t) + 1]), ys_r, "y_shared token %d" % t)
+                                               sd_, wl.limit)
+            ghs = as_u16(h_all[int(t):int(t) + 1])
+            gys = as_u16(y_all[int(t):int(t) + 1])
+            P.assert_bf16_close(ghs, rhs, "h_shared token %d" % t)
+            P.assert_bf16_close(gys, oracle.down_rows(ghs, sd_), "y_shared token %d (chained)" % t)
+            P.assert_bf16_close(gys, ys_r, "y_shared token %d (end to end)" % t,
+                                extra=P.propagated_h_diff(ghs, rhs, sd_))
         g_out = as_u16(out[int(t):int(t) + 1])
         w1 = g_w[t:t + 1]
         s2r1 = g_s2r[t * K:(t + 1) * K]
         # chained: oracle combine of the GPU rows
         gy_full = np.zeros((max(R, 1), H), np.uint16)
         gy_full[rows[kept]] = gy
-        gys = as_u16(y_all[int(t):int(t) + 1]) if wl.n_shared else None
+        if not wl.n_shared:
+            gys = None
         P.assert_bf16_close(g_out, oracle.combine(w1, s2r1, gy_full, gys), "out (chained) token %d" % t)
-        # independent: oracle rows, with the one-ulp y-flip propagation term
+        # independent: oracle rows, with the measured y differences propagated
         r_out = oracle.combine(w1, s2r1, ry, ys_r)
-        extra = P.propagated_y_flip(w1, s2r1, ry, ys_r)
+        extra = P.propagated_y_diff(w1, s2r1, gy_full, ry, gys, ys_r)
         P.assert_bf16_close(g_out, r_out, "out (end to end) token %d" % t, extra=extra)
