@@ -64,6 +64,25 @@ def roofline(flops, nbytes, seconds):
                 frac=round(a / PEAK_HBM_GBS, 4))
 
 
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch from profiles/traffic.txt (rocprofv3 PMC, copy-calibrated), or None
+    when there is no record or the kernel source changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        f = line.split()
+        if len(f) != 6 or line.startswith("#") or f[0] != workload or f[1] != kernel:
+            continue
+        src = os.path.join(root, f[2])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != f[3]:
+            return None
+        return int(f[4]) + int(f[5])
+    return None
+
+
 def cpu_baseline(wl, dev, n_tok):
     """The CPU oracle, timed on a bounded sample of the workload's tokens (every step of the
     layer for those tokens: router logits, routing, their routed and shared expert FFNs, combine).
@@ -171,8 +190,10 @@ def main():
     gu_s = phase_ms["gate_up_gemm"] / 1e3
     dn_s = phase_ms["down_gemm"] / 1e3
     rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s)
-    rf["traffic"] = None
-    rf["kernel"] = "ffn_skinny_kernel<true> (routed+shared gate/up grouped GEMM, clamped SwiGLU)"
+    tiled = wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
+    kname = "ffn_tiled_kernel<true>" if tiled else "ffn_skinny_kernel<true>"
+    rf["traffic"] = recorded_traffic(wl.name, kname)
+    rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
     rf["algorithmic_flops"] = alg["gu_flops"]
     rf["avg_launch_ms"] = round(phase_ms["gate_up_gemm"], 4)
