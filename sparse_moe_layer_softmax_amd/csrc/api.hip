@@ -239,7 +239,7 @@ int moe_layer_forward_profiled(const moe_shape* s, const uint16_t* x, const uint
                                void* ws, size_t ws_bytes, hipStream_t stream,
                                hipEvent_t const* ev) {
   auto mark = [&](int i) {
-    if (ev && ev[i]) hipEventRecord(ev[i], stream);
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;

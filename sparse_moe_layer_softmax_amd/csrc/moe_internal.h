@@ -60,6 +60,12 @@ struct FfnProblem {
 // down GEMM (each entry may be NULL).
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t const* ev = nullptr);
 
+// Dense C[rows, N] (fp32) = A[rows, Kd] . W[N, Kd]^T on the tiled MFMA kernel (router logits
+// at large T). Supported when N == 256 and Kd % 64 == 0.
+bool dense_gemm_f32_supported(int N, int Kd);
+hipError_t launch_dense_gemm_f32(const uint16_t* A, int rows, const uint16_t* W, int N, int Kd,
+                                 float* out, hipStream_t stream);
+
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,
                           const int32_t* slot_to_row, const uint16_t* y_shared, uint16_t* out,

@@ -8,7 +8,8 @@
 // Two kernels:
 //  1. route_gemm: x [T,H] . Wr[E,H]^T on MFMA 16x16x32 bf16 with fp32 accumulation. The hidden
 //     dimension is split S ways when T is small so that enough workgroups stream Wr; each
-//     split writes its own fp32 partial [S,T,E] (no atomics).
+//     split writes its own fp32 partial [S,T,E] (no atomics). For T >= 1024 and E = 256 the
+//     LDS-tiled MFMA kernel of the expert FFN computes the logits in one pass instead.
 //  2. route_topk: one wavefront per token. Sums the S partials in split order, adds the bias,
 //     stores the logits, then selects the top-k by (logit descending, expert ascending) with
 //     wavefront arg-max reductions. Because the renormalised weight p_j / sum_top p_i equals
@@ -88,8 +89,17 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     v[q] = -FLT_MAX;
     if (e < E) {
       const float* src = part + static_cast<size_t>(t) * E + e;
+      // partials in split order; loads batched 8 at a time so their latencies overlap
       float s = src[0];
-      for (int z = 1; z < S; ++z) s += src[z * plane];
+      int z = 1;
+      for (; z + 8 <= S; z += 8) {
+        float pz[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pz[u] = src[(z + u) * plane];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += pz[u];
+      }
+      for (; z < S; ++z) s += src[z * plane];
       if (bias) s += bias[e];
       v[q] = s;
       if (logits) logits[static_cast<size_t>(t) * E + e] = s;
@@ -148,7 +158,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 
 }  // namespace
 
+// Large T with a 256-wide expert dimension: the tiled MFMA kernel computes the logits in one
+// pass (no hidden split).
+static bool route_tiled(int T, int H, int E) { return T >= 1024 && dense_gemm_f32_supported(E, H); }
+
 int route_splits(int T, int H, int E) {
+  if (route_tiled(T, H, E)) return 1;
   const int tiles = ((T + kRouteTokTile - 1) / kRouteTokTile) * ((E + kRouteExpTile - 1) / kRouteExpTile);
   const int kmax = H / 128;  // each split covers a multiple of 128 hidden elements
   int best = 1;
@@ -163,9 +178,14 @@ int route_splits(int T, int H, int E) {
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w_router,
                         const float* bias, float* logits, float* topk_w, int32_t* topk_idx,
                         float* partials, int S, hipStream_t stream) {
-  dim3 g1((s.T + kRouteTokTile - 1) / kRouteTokTile, (s.E + kRouteExpTile - 1) / kRouteExpTile, S);
-  hipLaunchKernelGGL(route_gemm_kernel, g1, dim3(256), 0, stream, x, w_router, partials, s.T,
-                     s.H, s.E, s.H / S);
+  if (route_tiled(s.T, s.H, s.E)) {
+    const hipError_t e = launch_dense_gemm_f32(x, s.T, w_router, s.E, s.H, partials, stream);
+    if (e != hipSuccess) return e;
+  } else {
+    dim3 g1((s.T + kRouteTokTile - 1) / kRouteTokTile, (s.E + kRouteExpTile - 1) / kRouteExpTile, S);
+    hipLaunchKernelGGL(route_gemm_kernel, g1, dim3(256), 0, stream, x, w_router, partials, s.T,
+                       s.H, s.E, s.H / S);
+  }
   hipLaunchKernelGGL(route_topk_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream, partials, S,
                      bias, logits, topk_w, topk_idx, s.T, s.E, s.K, s.norm_topk_prob,
                      s.routed_scaling);

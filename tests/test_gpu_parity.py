@@ -45,6 +45,12 @@ SMALL = {
     "clamp_forced_t128": BASE.with_(name="clamp_forced_t128", x_std=30.0, seed=19),
     "multi_tile_t300_e16_k4": Workload("multi_tile_t300_e16_k4", T=300, H=512, E=16, K=4, I=256,
                                        scale=2.827, seed=20),
+    # several 8-tile bands in one group (about 1500 rows per expert), ragged last tiles
+    "bands_t3000_e4_k2": Workload("bands_t3000_e4_k2", T=3000, H=256, E=4, K=2, I=256, scale=2.827,
+                                  seed=22),
+    # router on the tiled MFMA path (T >= 1024, E = 256), ragged T
+    "tiled_router_t1030_e256_k8": Workload("tiled_router_t1030_e256_k8", T=1030, H=256, E=256, K=8,
+                                           I=256, scale=2.827, seed=23),
 }
 
 
@@ -123,7 +129,8 @@ def _ws(n):
     return torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
 
 
-@pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8", "no_renorm_t128"])
+@pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8", "no_renorm_t128",
+                                  "tiled_router_t1030_e256_k8"])
 def test_moe_route(name):
     _require_gpu()
     wl = SMALL[name]
@@ -179,7 +186,7 @@ def test_moe_permute(T, K, E, C):
 
 
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8",
-                                  "clamp_forced_t128", "multi_tile_t300_e16_k4"])
+                                  "clamp_forced_t128", "multi_tile_t300_e16_k4", "bands_t3000_e4_k2"])
 def test_moe_expert_ffn_routed_and_identity(name):
     _require_gpu()
     wl = SMALL[name]
@@ -205,14 +212,26 @@ def test_moe_expert_ffn_routed_and_identity(name):
         xr = hw["x"][r2s[a:b] // wl.K]
         rh, ry = oracle.expert_ffn_rows(xr, hw["w_gate"][e], hw["w_up"][e], hw["w_down"][e], wl.limit)
         P.assert_bf16_close(hg[a:b], rh, "h expert %d" % e)
-        P.assert_bf16_close(yg[a:b], ry, "y expert %d" % e)
-    # identity rows, one group, no offsets: the shared-expert form; h kept in the workspace
+        P.assert_bf16_close(yg[a:b], oracle.down_rows(hg[a:b], hw["w_down"][e]), "y expert %d (chained)" % e)
+        P.assert_bf16_close(yg[a:b], ry, "y expert %d (end to end)" % e,
+                            extra=P.propagated_h_diff(hg[a:b], rh, hw["w_down"][e]))
+    # identity rows, one group, no offsets: the shared-expert form, once with h kept in the
+    # workspace and once with h returned; both runs must agree bit for bit
+    sg, su, sd = dev["s_gate"][None], dev["s_up"][None], dev["s_down"][None]
     ys = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_ffn(s, 1, wl.T, dev["x"], None, None, dev["s_gate"][None], dev["s_up"][None],
-                       dev["s_down"][None], None, ys, _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
+    moe.moe_expert_ffn(s, 1, wl.T, dev["x"], None, None, sg, su, sd, None, ys,
+                       _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
+    hs = torch.empty((wl.T, wl.I), dtype=torch.bfloat16, device=DEV)
+    ys2 = torch.empty_like(ys)
+    moe.moe_expert_ffn(s, 1, wl.T, dev["x"], None, None, sg, su, sd, hs, ys2,
+                       _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
     torch.cuda.synchronize()
-    _, rys = oracle.expert_ffn_rows(hw["x"], hw["s_gate"], hw["s_up"], hw["s_down"], wl.limit)
-    P.assert_bf16_close(as_u16(ys), rys, "identity-row FFN")
+    assert torch.equal(ys, ys2)
+    rhs, rys = oracle.expert_ffn_rows(hw["x"], hw["s_gate"], hw["s_up"], hw["s_down"], wl.limit)
+    P.assert_bf16_close(as_u16(hs), rhs, "identity-row h")
+    P.assert_bf16_close(as_u16(ys), oracle.down_rows(as_u16(hs), hw["s_down"]), "identity-row y (chained)")
+    P.assert_bf16_close(as_u16(ys), rys, "identity-row y (end to end)",
+                        extra=P.propagated_h_diff(as_u16(hs), rhs, hw["s_down"]))
 
 
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "capacity_drops_t200_e8_k2", "no_shared_t128"])
