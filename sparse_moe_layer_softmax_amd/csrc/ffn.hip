@@ -355,13 +355,24 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   constexpr int kMfmaPerTile = (BK / 16) * MIV * 4;
   constexpr int kStep = kMfmaPerTile >= NA + NB ? kMfmaPerTile / (NA + NB) : 1;
   static_assert(MIV == 0 || kMfmaPerTile % (NA + NB) == 0, "DMA spread must divide the MFMAs");
+  // Every iteration issues exactly one K-tile of DMA: past the end it reloads the last tile into
+  // the free stage (never read), so exactly S-2 later tiles are in flight at each wait and the
+  // loop body has no branch (which lets the instruction order below be pinned).
+  for (int t = nk; t < S - 1; ++t) issue(nk - 1);  // K shorter than the ring
   for (int kt = 0; kt < nk; ++kt) {
-    // K-tile kt has landed once at most the later tiles already issued are in flight
-    wait_tiles<NA + NB>(min(S - 2, nk - 1 - kt));
+    wait_vmcnt<(S - 2) * (NA + NB)>();  // K-tile kt has landed
     barrier_no_fence();
-    const bool more = kt + S - 1 < nk;  // next tile goes into the stage consumed in kt-1
+    const int kn = min(kt + S - 1, nk - 1);  // tile loaded into the stage consumed in kt-1
+    const int sn = (kt + S - 1) % S;
+    auto issue_next = [&](int d) {
+      if (d < NA)
+        lds_dma16(p.A + aoff[d] + kn * BK, sA + sn * kStageA + (wave + 4 * d) * 512);
+      else
+        lds_dma16(bsrc[d - NA] + kn * BK, sB + sn * kStageB + (wave + 4 * (d - NA)) * 512);
+    };
     if (MIV == 0) {
-      if (more) issue(kt + S - 1);
+#pragma unroll
+      for (int d = 0; d < NA + NB; ++d) issue_next(d);
       continue;
     }
     const uint16_t* a = sA + (kt % S) * kStageA + wm * (BM / 2) * BK;
@@ -386,8 +397,20 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
         for (int j = 0; j < 4; ++j) {
           acc[i][j] = mfma32x32x16(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
           const int m = (ks * MIV + i) * 4 + j + 1;  // MFMAs issued so far in this K-tile
-          if (more && m % kStep == 0 && m / kStep <= NA + NB) issue_one(kt + S - 1, m / kStep - 1);
+          if (m % kStep == 0 && m / kStep <= NA + NB) issue_next(m / kStep - 1);
         }
+    }
+    // Pin the order: K-step 0's fragment reads; then each MFMA followed by one of the next
+    // K-step's fragment reads (while any remain) and, every kStep MFMAs, one DMA instruction.
+    constexpr int kFrag = MIV + 4;           // fragment reads per K-step
+    constexpr int kMfmaStep = MIV * 4;       // MFMAs per K-step
+    __builtin_amdgcn_sched_group_barrier(0x100, kFrag, 0);
+#pragma unroll
+    for (int m = 0; m < kMfmaPerTile; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int in_step = m % kMfmaStep;
+      if (m / kMfmaStep + 1 < BK / 16 && in_step < kFrag) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if ((m + 1) % kStep == 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
   }
 
