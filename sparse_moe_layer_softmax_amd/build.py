@@ -14,13 +14,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["route.hip", "permute.hip", "ffn.hip", "combine.hip", "api.hip"]
+SOURCES = ["route.hip", "permute.hip", "ffn.hip", "ffn_skinny.hip", "ffn_tiled.hip", "combine.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
-    # packed fp32 arithmetic stays off; hipcc's host pass warns it does not
-    # know the feature, which is harmless
+    # no packed-fp32 instructions (v_pk_*_f32) are generated; hipcc's host pass warns that it
+    # does not know the feature, which is harmless
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",

@@ -1,0 +1,43 @@
+// ffn_kernels.h -- grouped-GEMM kernels of the expert FFN (internal; shared by ffn*.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Operands of one grouped projection (gate/up with the SwiGLU epilogue, or down).
+struct GroupedParams {
+  const uint16_t* A;        // activation rows: x [T, Kd] (gate/up) or h [rows, Kd] (down)
+  int32_t a_rows;           // rows of A (bounds the gathered row index)
+  const int32_t* gather;    // row_to_slot
+  int32_t n_ident;          // rows below this read A row r itself
+  int32_t topk;
+  int32_t rows_max;         // output rows; no row at or beyond it is read or written
+  const int32_t* offsets;   // [G+1]
+  const int32_t* tiles;     // tile table
+  int32_t max_tiles;
+  const uint16_t* W0a;      // gate (gated) or down weights for groups < g_split
+  const uint16_t* W0b;      // ... for groups >= g_split
+  const uint16_t* W1a;      // up weights (gated only)
+  const uint16_t* W1b;
+  int32_t g_split;
+  uint16_t* out;            // [rows, N] bf16
+  float* out_f32;           // [rows, N] fp32 (router logits)
+  int32_t N;                // output columns (I for gate/up, H for down)
+  int32_t Kd;               // reduction length (H for gate/up, I for down)
+  float limit;
+};
+
+
+// Weight-streaming kernel for few rows per group (ffn_skinny.hip): row tiles of kSkinnyRows.
+constexpr int kSkinnyRows = 64;
+// gated: gate/up + SwiGLU over N = I columns (64 per workgroup); else down (128 per workgroup).
+hipError_t launch_skinny(bool gated, const GroupedParams& p, int max_tiles, hipStream_t stream);
+
+// LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
+constexpr int kTiledRows = 256;
+enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2 };
+hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
+
+}  // namespace moe
