@@ -191,7 +191,7 @@ def main():
     dn_s = phase_ms["down_gemm"] / 1e3
     rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s)
     tiled = wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
-    kname = "ffn_tiled_kernel<true>" if tiled else "ffn_skinny_kernel<true>"
+    kname = "ffn_tiled_kernel<kEpiSwiglu>" if tiled else "ffn_skinny_kernel<true>"
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
