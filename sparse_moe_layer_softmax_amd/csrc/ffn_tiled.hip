@@ -17,20 +17,25 @@ namespace {
 // Kernel "tiled": a workgroup computes a 256-row x 256-weight-row output tile (gate/up: 128 gate
 // rows and the 128 matching up rows) with eight wavefronts, two per SIMD. Wavefront w owns rows
 // 128*(w/4) .. +128 and weight rows 64*(w%4) .. +64 of the tile: 4 x 2 MFMA 32x32x16 fragments,
-// 128 fp32 accumulators per lane in AGPRs.
-//  - K is staged BK = 32 at a time through a 4-stage LDS ring (128 KB) filled by direct
-//    global->LDS loads (global_load_lds_dwordx4, no VGPR staging).
-//  - Ping-pong: the two wavefronts of a SIMD alternate between a memory phase (issue their
-//    share of the DMA of a later K-tile, read all fragments of the current K-tile from LDS into
-//    VGPRs) and a compute phase (16 MFMAs on fragments already in registers, nothing else).
-//    Workgroup barriers separate the phases; the second half of the wavefronts starts one phase
-//    late, so while one wavefront of a SIMD computes, the other one moves data, and a stall of
-//    the memory pipeline (DMA issue back-pressure, LDS latency) never holds up the MFMA issue of
-//    the computing wavefront.
+// 128 fp32 accumulators per lane.
+//  - K is staged 64 at a time through a two-stage LDS ring (2 x 64 KB) filled by direct
+//    global->LDS loads (global_load_lds_dwordx4, no VGPR staging). One such instruction moves
+//    1 KB: 8 rows of 128 bytes, whole L2 lines. The DMA of K-tile kt+1 is issued at the start of
+//    K-tile kt, so it has a whole K-tile of compute to land.
+//  - Each wavefront loads the activation rows of its own live 32-row fragments (one instruction
+//    per fragment) and an eighth of the weight tile, so rows past the end of a group cost neither
+//    DMA nor MFMA: ragged expert tails are cheap.
+//  - Ping-pong: the two wavefronts of a SIMD alternate between a memory phase (issue DMA, read the
+//    fragments of a 32-wide K slice from LDS into VGPRs) and a compute phase (16 MFMAs on
+//    fragments already in registers, nothing else). Workgroup barriers separate the phases; the
+//    second half of the wavefronts starts one phase late, so while one wavefront of a SIMD
+//    computes, the other one moves data, and a stall of the memory pipeline (DMA issue
+//    back-pressure, LDS latency) never holds up the MFMA issue of the computing wavefront.
 //  - LDS rows are XOR-swizzled by 16-byte chunk (swz) so MFMA operand reads are conflict free
 //    on the 64-bank LDS.
 //  - The main loop is specialised on the number of 32-row fragments of a wavefront that hold
-//    rows of the group (MIV), so partly filled tiles skip MFMAs without branching in the loop.
+//    rows of the group (MIV), so partly filled tiles skip MFMAs and DMA without branching in the
+//    loop.
 //  - Work items are ordered inside XCD-contiguous slices of the real work list (its size comes
 //    from the device-side tile count, so spare grid slots do not unbalance the XCDs); inside a
 //    group the work runs in bands of up to kBand row tiles, n-blocks outer and the band's row
@@ -39,24 +44,22 @@ namespace {
 //    tiles reads each of its weight tiles from HBM once.
 //  - bf16 results are staged through LDS and written as whole 16-byte row segments.
 constexpr int kThreads = 512;
-constexpr int kBM = 256;       // rows per tile
-constexpr int kTN = 256;       // weight rows per tile (gate/up: 128 gate + 128 up)
-constexpr int kBK = 32;        // K per stage
-constexpr int kStages = 4;
+constexpr int kBM = 256;  // rows per tile
+constexpr int kTN = 256;  // weight rows per tile (gate/up: 128 gate + 128 up)
+constexpr int kBK = 64;   // K per stage
+constexpr int kStages = 2;
 constexpr int kXcds = 8;
 constexpr int kBand = 8;
 constexpr int kStageA = kBM * kBK, kStageB = kTN * kBK;  // bf16 elements per stage
 constexpr size_t kSmem = sizeof(uint16_t) * kStages * (kStageA + kStageB);
-// One DMA instruction fills a 1 KB block: 16 rows of BK = 32 elements. Each wavefront issues
-// kDmaA blocks of the A stage and kDmaB of the B stage per K-tile.
-constexpr int kDmaA = kBM / 16 / 8, kDmaB = kTN / 16 / 8;
-constexpr int kDmaW = kDmaA + kDmaB;
+constexpr int kDmaB = kTN / 8 / 8;  // weight-tile DMA instructions per wavefront per K-tile
 
-// LDS element offset of (row, k) in a [rows][32] bf16 stage. The four 16-byte chunks of a row
-// are XOR-swizzled by (row / 4) % 4 so that an MFMA operand read (32 consecutive rows at one
-// logical chunk per 32-lane half) touches every bank of the 64-bank LDS the same number of times.
+// LDS element offset of (row, k) in a [rows][64] bf16 stage. The eight 16-byte chunks of a row
+// are XOR-swizzled (slot = chunk ^ (row % 8) ^ ((row / 8) % 2)) so that an MFMA operand read (32
+// consecutive rows at one logical chunk per 32-lane half) puts the 16 lanes of each pass on 16
+// distinct 16-byte bank groups of the 64-bank LDS.
 __device__ __forceinline__ int swz(int row, int k) {
-  return row * 32 + (((k >> 3) ^ ((row >> 2) & 3)) << 3) + (k & 7);
+  return row * kBK + (((k >> 3) ^ (row & 7) ^ ((row >> 3) & 1)) << 3) + (k & 7);
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima).
@@ -97,24 +100,29 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   constexpr bool GATED = EPI == kEpiSwiglu;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* sA = smem;                      // [S][256][32]
-  uint16_t* sB = smem + kStages * kStageA;  // [S][256][32]
+  uint16_t* sA = smem;                      // [2][256][64]
+  uint16_t* sB = smem + kStages * kStageA;  // [2][256][64]
   const int Kd = p.Kd;
+  const int nk = Kd / kBK;  // K-tiles
   const int tid = threadIdx.x;
   // wavefront index as a scalar: the LDS destinations of the DMA (M0) are then pure SALU math
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int half = wave >> 2;  // rows 128*half .. +128 of the tile; also the ping-pong group
+  const int half = wave >> 2;    // rows 128*half .. +128 of the tile; also the ping-pong group
   const int quarter = wave & 3;  // weight rows 64*quarter .. +64 of the tile
 
-  // ---- DMA assignment. A 1 KB block holds 16 rows of 32 elements; lane i fills its 16-byte
-  // slot i: row i/4 of the block, physical chunk i%4, which holds the logical chunk that swz()
-  // places there ((row/4)%4 == i/16 inside a 16-row block). Wave w fills blocks w and w+8.
-  const int lrow = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  uint32_t aoff[kDmaA];
+  // ---- DMA assignment. A 1 KB block holds 8 rows of 64 elements; lane i fills its 16-byte slot
+  // i: row i/8 of the block, physical chunk i%8, which holds the logical chunk that swz() places
+  // there. A stage: the wavefront (half, quarter) fills blocks 16*half + quarter + 4i, i < MIV,
+  // which together with the other quarters of its half are exactly the rows of its live
+  // fragments (fragment i = blocks 16*half + 4i .. +4). B stage: wavefront w fills blocks w+8i.
+  // Every block index used here is congruent to the quarter mod 2, so a row's (row / 8) % 2 is
+  // quarter % 2, and its row % 8 is lane / 8.
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ lrow ^ (quarter & 1);
+  uint32_t aoff[MV];
 #pragma unroll
-  for (int i = 0; i < kDmaA; ++i) {
-    const int r = r0 + (wave + 8 * i) * 16 + lrow;
+  for (int i = 0; i < MIV; ++i) {
+    const int r = r0 + (16 * half + quarter + 4 * i) * 8 + lrow;
     int src = 0;
     if (r < r1) src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
     if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) src = 0;
@@ -127,7 +135,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   const uint16_t* bsrc[kDmaB];
 #pragma unroll
   for (int i = 0; i < kDmaB; ++i) {
-    const int b = (wave + 8 * i) * 16 + lrow;  // weight-tile row 0..255
+    const int b = (wave + 8 * i) * 8 + lrow;  // weight-tile row 0..255
     int row;
     const uint16_t* Wm = W0;
     if (GATED) {
@@ -142,8 +150,9 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   }
   auto dma_tile = [&](int kt, int stage) {
 #pragma unroll
-    for (int i = 0; i < kDmaA; ++i)
-      lds_dma16(p.A + aoff[i] + kt * kBK, sA + stage * kStageA + (wave + 8 * i) * 512);
+    for (int i = 0; i < MIV; ++i)
+      lds_dma16(p.A + aoff[i] + kt * kBK,
+                sA + stage * kStageA + (16 * half + quarter + 4 * i) * 512);
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i)
       lds_dma16(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
@@ -157,62 +166,66 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = Kd / kBK;
   const int fr = lane & 31, fk = (lane >> 5) * 8;
-  // LDS offset of this lane's fragment row fr at K-step ks inside a 32-row-aligned block: the
-  // swizzle term depends only on fr, so one offset per K-step serves every fragment and stage.
-  const int lds_off0 = swz(fr, fk), lds_off1 = swz(fr, 16 + fk);
+  // LDS offset of this lane's fragment row fr at 16-wide K-step ks inside a 32-row-aligned
+  // block: the swizzle term depends only on fr (row bases are multiples of 32), so one offset
+  // per K-step serves every fragment and stage.
+  int lds_off[kBK / 16];
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) lds_off[ks] = swz(fr, ks * 16 + fk);
   u32x4_t af[2][MV], bf[2][2];
-  auto fetch = [&](int stage) {
+  // fragments of the 32-wide K slice h of a stage
+  auto fetch = [&](int stage, int h) {
     const uint16_t* a = sA + stage * kStageA + half * 128 * kBK;
     const uint16_t* b = sB + stage * kStageB + quarter * 64 * kBK;
 #pragma unroll
     for (int i = 0; i < MIV; ++i) {
-      af[0][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off0]);
-      af[1][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off1]);
+      af[0][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h]]);
+      af[1][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h + 1]]);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      bf[0][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off0]);
-      bf[1][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off1]);
+      bf[0][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h]]);
+      bf[1][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h + 1]]);
     }
   };
 
-  // ---- pipeline. Phases alternate memory (M) and compute (C); every phase ends at a workgroup
-  // barrier. Half 0 runs M0 C0 M1 C1 ...; half 1 runs the same one phase later, so the halves
-  // are always in opposite phases. M_kt issues this wavefront's DMA of K-tile kt+S-1 into the
-  // stage of K-tile kt-1 (both halves finished reading it before the barrier that opened M_kt)
-  // and reads the fragments of K-tile kt. K-tile kt must have landed before the barrier that
-  // opens half 0's M_kt: each wavefront waits for its own share there (half 0 at the end of
-  // C_{kt-1}, half 1 at the end of M_{kt-1}), when S-2 younger K-tiles of its DMA may still be
-  // in flight. Past the end of K the DMA reloads the last K-tile into the free stage (never
-  // read), so every wait count is a constant. Every wavefront passes 2 + 2*nk barriers.
-  constexpr int kInFlight = (kStages - 2) * kDmaW;
-#pragma unroll
-  for (int t = 0; t < kStages - 1; ++t) dma_tile(min(t, nk - 1), t);
-  wait_vmcnt<kInFlight>();
+  // ---- pipeline. Phases alternate memory (M) and compute (C), each covering a 32-wide K slice
+  // (two per K-tile); every phase ends at a workgroup barrier. Half 0 runs M C M C ...; half 1
+  // runs the same one phase later, so the halves are always in opposite phases. The first M of
+  // K-tile kt issues this wavefront's DMA of K-tile kt+1 into the other stage (both halves
+  // finished reading K-tile kt-1 from it before the barrier that opened this M); every M reads
+  // the fragments of its slice. K-tile kt+1 must have landed before the barrier that opens half
+  // 0's first M of it: each wavefront waits for all of its DMA there (half 0 at the end of the
+  // last C of K-tile kt, half 1 at the end of its last M). Past the end of K the DMA reloads the
+  // last K-tile into the free stage (never read). Every wavefront passes 2 + 4*nk barriers.
+  dma_tile(0, 0);
+  wait_vmcnt<0>();
   barrier_no_fence();
   if (half == 1) barrier_no_fence();
   for (int kt = 0; kt < nk; ++kt) {
-    // ---- memory phase
-    if (MIV > 0) fetch(kt % kStages);
-    dma_tile(min(kt + kStages - 1, nk - 1), (kt + kStages - 1) % kStages);
-    if (half == 1) wait_vmcnt<kInFlight>();
-    wait_lgkmcnt0();
-    barrier_no_fence();
-    // ---- compute phase
-    if (MIV > 0) {
-      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+    for (int h = 0; h < 2; ++h) {
+      // ---- memory phase
+      if (MIV > 0) fetch(kt & 1, h);
+      if (h == 0) dma_tile(min(kt + 1, nk - 1), (kt + 1) & 1);
+      if (half == 1 && h == 1) wait_vmcnt<0>();
+      wait_lgkmcnt0();
+      barrier_no_fence();
+      // ---- compute phase
+      if (MIV > 0) {
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int i = 0; i < MIV; ++i)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
-      __builtin_amdgcn_s_setprio(0);
+          for (int i = 0; i < MIV; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (half == 0 && h == 1) wait_vmcnt<0>();
+      barrier_no_fence();
     }
-    if (half == 0) wait_vmcnt<kInFlight>();
-    barrier_no_fence();
   }
   if (half == 0) barrier_no_fence();
 
@@ -329,7 +342,8 @@ hipError_t tiled_launch(const GroupedParams& p, int nblk, int n_tiles_max, hipSt
   const hipError_t e = tiled_prepare<EPI>();
   if (e != hipSuccess) return e;
   const int grid = (n_tiles_max * nblk + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL(ffn_tiled_kernel<EPI>, dim3(grid), dim3(kThreads), kSmem, stream, p, nblk);
+  const auto kernel = ffn_tiled_kernel<EPI>;
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kSmem, stream, p, nblk);
   return hipGetLastError();
 }
 
