@@ -36,7 +36,7 @@ constexpr int kSkinnyRows = 64;
 hipError_t launch_skinny(bool gated, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 // LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
-constexpr int kTiledRows = 256;
+constexpr int kTiledRows = 320;
 enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 

@@ -14,11 +14,15 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------------------------
-// Kernel "tiled": a workgroup computes a 256-row x 256-weight-row output tile (gate/up: 128 gate
+// Kernel "tiled": a workgroup computes a 320-row x 256-weight-row output tile (gate/up: 128 gate
 // rows and the 128 matching up rows) with eight wavefronts, two per SIMD. Wavefront w owns rows
-// 128*(w/4) .. +128 and weight rows 64*(w%4) .. +64 of the tile: 4 x 2 MFMA 32x32x16 fragments,
-// 128 fp32 accumulators per lane.
-//  - K is staged 64 at a time through a two-stage LDS ring (2 x 64 KB) filled by direct
+// 160*(w/4) .. +160 and weight rows 64*(w%4) .. +64 of the tile: 5 x 2 MFMA 32x32x16 fragments,
+// 160 fp32 accumulators per lane.
+//  - The operand bytes a CU moves into LDS per FLOP, (BM + BN) / (BM * BN), bound this kernel
+//    (the global->LDS fill path, not the MFMAs, is the limit), so the tile is as large as the
+//    register file of two wavefronts per SIMD allows. 320 rows also fit a whole expert at the
+//    prefill shape (about T*k/E = 256 rows each, never more than ~310) in one row tile.
+//  - K is staged 64 at a time through a two-stage LDS ring (2 x 72 KB) filled by direct
 //    global->LDS loads (global_load_lds_dwordx4, no VGPR staging). One such instruction moves
 //    1 KB: 8 rows of 128 bytes, whole L2 lines. The DMA of K-tile kt+1 is issued at the start of
 //    K-tile kt, so it has a whole K-tile of compute to land.
@@ -26,7 +30,7 @@ namespace {
 //    per fragment) and an eighth of the weight tile, so rows past the end of a group cost neither
 //    DMA nor MFMA: ragged expert tails are cheap.
 //  - Ping-pong: the two wavefronts of a SIMD alternate between a memory phase (issue DMA, read the
-//    fragments of a 32-wide K slice from LDS into VGPRs) and a compute phase (16 MFMAs on
+//    fragments of a 32-wide K slice from LDS into VGPRs) and a compute phase (20 MFMAs on
 //    fragments already in registers, nothing else). Workgroup barriers separate the phases; the
 //    second half of the wavefronts starts one phase late, so while one wavefront of a SIMD
 //    computes, the other one moves data, and a stall of the memory pipeline (DMA issue
@@ -44,7 +48,8 @@ namespace {
 //    tiles reads each of its weight tiles from HBM once.
 //  - bf16 results are staged through LDS and written as whole 16-byte row segments.
 constexpr int kThreads = 512;
-constexpr int kBM = 256;  // rows per tile
+constexpr int kBM = 320;  // rows per tile
+constexpr int kMI = 5;    // 32-row fragments per wavefront (160 rows: half the tile)
 constexpr int kTN = 256;  // weight rows per tile (gate/up: 128 gate + 128 up)
 constexpr int kBK = 64;   // K per stage
 constexpr int kStages = 2;
@@ -94,27 +99,27 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
 // EPI = kEpiSwiglu: gate/up rows interleaved, h = bf16(silu(clamp g) * clamp u);
 // kEpiBf16: plain bf16 output (down projection); kEpiF32: fp32 output (router logits).
 // p.tiles == nullptr selects dense mode: one group of rows [0, rows_max) in kBM-row tiles.
-// Main loop and epilogue of one tile; MIV = live 32-row fragments of this wavefront (0..4).
+// Main loop and epilogue of one tile; MIV = live 32-row fragments of this wavefront (0..5).
 template <int EPI, int MIV>
 __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1) {
   constexpr bool GATED = EPI == kEpiSwiglu;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  uint16_t* sA = smem;                      // [2][256][64]
+  uint16_t* sA = smem;                      // [2][320][64]
   uint16_t* sB = smem + kStages * kStageA;  // [2][256][64]
   const int Kd = p.Kd;
   const int nk = Kd / kBK;  // K-tiles
   const int tid = threadIdx.x;
   // wavefront index as a scalar: the LDS destinations of the DMA (M0) are then pure SALU math
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int half = wave >> 2;    // rows 128*half .. +128 of the tile; also the ping-pong group
+  const int half = wave >> 2;    // rows 160*half .. +160 of the tile; also the ping-pong group
   const int quarter = wave & 3;  // weight rows 64*quarter .. +64 of the tile
 
   // ---- DMA assignment. A 1 KB block holds 8 rows of 64 elements; lane i fills its 16-byte slot
   // i: row i/8 of the block, physical chunk i%8, which holds the logical chunk that swz() places
-  // there. A stage: the wavefront (half, quarter) fills blocks 16*half + quarter + 4i, i < MIV,
+  // there. A stage: the wavefront (half, quarter) fills blocks 20*half + quarter + 4i, i < MIV,
   // which together with the other quarters of its half are exactly the rows of its live
-  // fragments (fragment i = blocks 16*half + 4i .. +4). B stage: wavefront w fills blocks w+8i.
+  // fragments (fragment i = blocks 20*half + 4i .. +4). B stage: wavefront w fills blocks w+8i.
   // Every block index used here is congruent to the quarter mod 2, so a row's (row / 8) % 2 is
   // quarter % 2, and its row % 8 is lane / 8.
   const int lrow = lane >> 3;
@@ -122,7 +127,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   uint32_t aoff[MV];
 #pragma unroll
   for (int i = 0; i < MIV; ++i) {
-    const int r = r0 + (16 * half + quarter + 4 * i) * 8 + lrow;
+    const int r = r0 + (20 * half + quarter + 4 * i) * 8 + lrow;
     int src = 0;
     if (r < r1) src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
     if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) src = 0;
@@ -152,7 +157,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
       lds_dma16(p.A + aoff[i] + kt * kBK,
-                sA + stage * kStageA + (16 * half + quarter + 4 * i) * 512);
+                sA + stage * kStageA + (20 * half + quarter + 4 * i) * 512);
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i)
       lds_dma16(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
@@ -176,7 +181,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   u32x4_t af[2][MV], bf[2][2];
   // fragments of the 32-wide K slice h of a stage
   auto fetch = [&](int stage, int h) {
-    const uint16_t* a = sA + stage * kStageA + half * 128 * kBK;
+    const uint16_t* a = sA + stage * kStageA + half * 160 * kBK;
     const uint16_t* b = sB + stage * kStageB + quarter * 64 * kBK;
 #pragma unroll
     for (int i = 0; i < MIV; ++i) {
@@ -230,7 +235,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   if (half == 0) barrier_no_fence();
 
   // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
-  const int rbase = r0 + half * 128;
+  const int rbase = r0 + half * 160;
   if (EPI == kEpiF32) {
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
@@ -245,18 +250,21 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     return;
   }
   // bf16 outputs go through LDS so that global stores are whole 16-byte row segments. Each
-  // wavefront owns a [128][C] bf16 slice of the (now idle) stage ring; its 16-byte chunks are
-  // XOR-swizzled by row so the column-wise fragment writes spread over the banks.
+  // wavefront owns two [32][C] bf16 buffers of the (now idle) stage ring, used by alternate
+  // fragment rows; their 16-byte chunks are XOR-swizzled by row so the column-wise fragment
+  // writes spread over the banks.
   constexpr int C = GATED ? 32 : 64;  // output columns of this wavefront
   constexpr int CH = C / 8;           // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;        // rows per store instruction
   __syncthreads();                    // every DMA has landed and every wavefront left the ring
-  uint16_t* ep = smem + wave * 128 * C;
+  const int col0 = GATED ? nb * 128 + quarter * 32 : nb * kTN + quarter * 64;
   auto eoff = [&](int row, int col) { return row * C + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7); };
 #pragma unroll
   for (int i = 0; i < MIV; ++i) {
+    uint16_t* ep = smem + (wave * 2 + (i & 1)) * 32 * C;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
       if (GATED) {
         ep[eoff(row, fr)] = f32_to_bf16(clamped_swiglu(acc[i][0][v], acc[i][1][v], p.limit));
       } else {
@@ -264,20 +272,17 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
         for (int j = 0; j < 2; ++j) ep[eoff(row, j * 32 + fr)] = f32_to_bf16(acc[i][j][v]);
       }
     }
-    // one fragment row at a time: keeps the scheduler from reading every accumulator out of the
-    // AGPRs at once
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the slice is private to this wavefront; its LDS accesses complete in order
-  const int col0 = GATED ? nb * 128 + quarter * 32 : nb * kTN + quarter * 64;
-  constexpr int RPI = 64 / CH;  // rows per store instruction
+    // the buffers are private to this wavefront and its LDS accesses complete in order
 #pragma unroll
-  for (int it = 0; it < MIV * 32 / RPI; ++it) {
-    const int row = it * RPI + lane / CH;
-    const int ch = lane % CH;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&ep[row * C + (((ch ^ row) & (CH - 1)) << 3)]);
-    if (rbase + row < r1)
-      *reinterpret_cast<u32x4_t*>(p.out + static_cast<size_t>(rbase + row) * p.N + col0 + ch * 8) = v;
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int row = it * RPI + lane / CH;
+      const int ch = lane % CH;
+      const u32x4_t val = *reinterpret_cast<const u32x4_t*>(&ep[row * C + (((ch ^ row) & (CH - 1)) << 3)]);
+      const int r = rbase + i * 32 + row;
+      if (r < r1) *reinterpret_cast<u32x4_t*>(p.out + static_cast<size_t>(r) * p.N + col0 + ch * 8) = val;
+    }
+    // one fragment row at a time: keeps the scheduler from reading every accumulator at once
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -315,13 +320,14 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   // 32-row fragments of this wavefront that hold rows of the group (uniform per wavefront); the
   // main loop is specialised on it so that no branch sits between the MFMAs. Every
   // specialisation passes the same barriers.
-  const int miv = min(4, max(0, (r1 - (r0 + half * 128) + 31) / 32));
+  const int miv = min(kMI, max(0, (r1 - (r0 + half * 160) + 31) / 32));
   switch (miv) {
     case 0: tiled_main<EPI, 0>(p, g, nb, r0, r1); break;
     case 1: tiled_main<EPI, 1>(p, g, nb, r0, r1); break;
     case 2: tiled_main<EPI, 2>(p, g, nb, r0, r1); break;
     case 3: tiled_main<EPI, 3>(p, g, nb, r0, r1); break;
-    default: tiled_main<EPI, 4>(p, g, nb, r0, r1); break;
+    case 4: tiled_main<EPI, 4>(p, g, nb, r0, r1); break;
+    default: tiled_main<EPI, 5>(p, g, nb, r0, r1); break;
   }
 }
 
