@@ -23,7 +23,8 @@ struct GroupedParams {
   const uint16_t* W1b;
   int32_t g_split;
   uint16_t* out;            // [rows, N] bf16
-  float* out_f32;           // [rows, N] fp32 (router logits)
+  float* out_f32;           // [rows, N] fp32 (router logits); with k_splits > 1, k_splits such planes
+  int32_t k_splits;         // dense mode only: the reduction is split into this many K ranges (0 = 1)
   int32_t N;                // output columns (I for gate/up, H for down)
   int32_t Kd;               // reduction length (H for gate/up, I for down)
   float limit;

@@ -99,16 +99,17 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
 // EPI = kEpiSwiglu: gate/up rows interleaved, h = bf16(silu(clamp g) * clamp u);
 // kEpiBf16: plain bf16 output (down projection); kEpiF32: fp32 output (router logits).
 // p.tiles == nullptr selects dense mode: one group of rows [0, rows_max) in kBM-row tiles.
-// Main loop and epilogue of one tile; MIV = live 32-row fragments of this wavefront (0..5).
+// Main loop and epilogue of one tile over the nk K-tiles from K-tile kb (fp32 output: into the
+// partial-sum plane split); MIV = live 32-row fragments of this wavefront (0..5).
 template <int EPI, int MIV>
-__device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1) {
+__device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1,
+                                           int kb, int nk, int split) {
   constexpr bool GATED = EPI == kEpiSwiglu;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sA = smem;                      // [2][320][64]
   uint16_t* sB = smem + kStages * kStageA;  // [2][256][64]
   const int Kd = p.Kd;
-  const int nk = Kd / kBK;  // K-tiles
   const int tid = threadIdx.x;
   // wavefront index as a scalar: the LDS destinations of the DMA (M0) are then pure SALU math
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -131,7 +132,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     int src = 0;
     if (r < r1) src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
     if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) src = 0;
-    aoff[i] = static_cast<uint32_t>(src) * Kd + lchunk * 8;
+    aoff[i] = static_cast<uint32_t>(src) * Kd + kb * kBK + lchunk * 8;
   }
   const size_t wst = static_cast<size_t>(p.N) * Kd;
   const uint16_t* W0 = g < p.g_split ? p.W0a + g * wst : p.W0b + (g - p.g_split) * wst;
@@ -151,7 +152,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     } else {
       row = nb * kTN + b;
     }
-    bsrc[i] = Wm + static_cast<size_t>(row) * Kd + lchunk * 8;
+    bsrc[i] = Wm + static_cast<size_t>(row) * Kd + kb * kBK + lchunk * 8;
   }
   auto dma_tile = [&](int kt, int stage) {
 #pragma unroll
@@ -243,7 +244,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       for (int v = 0; v < 16; ++v) {
         const int r = rbase + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= r1) continue;
-        float* o = p.out_f32 + static_cast<size_t>(r) * p.N + nb * kTN + quarter * 64 + fr;
+        float* o = p.out_f32 + (static_cast<size_t>(split) * p.rows_max + r) * p.N + nb * kTN + quarter * 64 + fr;
 #pragma unroll
         for (int j = 0; j < 2; ++j) o[j * 32] = acc[i][j][v];
       }
@@ -292,12 +293,17 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   // ---- work item: XCD-contiguous slices of the work list (band order inside each group)
   const bool dense = p.tiles == nullptr;
   const int n_tiles = dense ? (p.rows_max + kBM - 1) / kBM : p.tiles[0];
-  const int total = n_tiles * nblk;
+  const int splits = dense && p.k_splits > 1 ? p.k_splits : 1;
+  const int total = n_tiles * nblk * splits;
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   if (slot >= per_xcd) return;
-  const int w = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (w >= total) return;
+  const int ws = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (ws >= total) return;
+  // dense mode: the K splits of one output tile are adjacent items
+  const int split = ws % splits;
+  const int w = ws / splits;
+  const int nk = p.Kd / kBK / splits;  // K-tiles of this item
   // the group's items occupy nblk x its tile range of the work list
   const int ts = w / nblk;
   const int g = dense ? 0 : p.tiles[1 + ts];
@@ -322,12 +328,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   // specialisation passes the same barriers.
   const int miv = min(kMI, max(0, (r1 - (r0 + half * 160) + 31) / 32));
   switch (miv) {
-    case 0: tiled_main<EPI, 0>(p, g, nb, r0, r1); break;
-    case 1: tiled_main<EPI, 1>(p, g, nb, r0, r1); break;
-    case 2: tiled_main<EPI, 2>(p, g, nb, r0, r1); break;
-    case 3: tiled_main<EPI, 3>(p, g, nb, r0, r1); break;
-    case 4: tiled_main<EPI, 4>(p, g, nb, r0, r1); break;
-    default: tiled_main<EPI, 5>(p, g, nb, r0, r1); break;
+    case 0: tiled_main<EPI, 0>(p, g, nb, r0, r1, split * nk, nk, split); break;
+    case 1: tiled_main<EPI, 1>(p, g, nb, r0, r1, split * nk, nk, split); break;
+    case 2: tiled_main<EPI, 2>(p, g, nb, r0, r1, split * nk, nk, split); break;
+    case 3: tiled_main<EPI, 3>(p, g, nb, r0, r1, split * nk, nk, split); break;
+    case 4: tiled_main<EPI, 4>(p, g, nb, r0, r1, split * nk, nk, split); break;
+    default: tiled_main<EPI, 5>(p, g, nb, r0, r1, split * nk, nk, split); break;
   }
 }
 
@@ -347,7 +353,8 @@ template <int EPI>
 hipError_t tiled_launch(const GroupedParams& p, int nblk, int n_tiles_max, hipStream_t stream) {
   const hipError_t e = tiled_prepare<EPI>();
   if (e != hipSuccess) return e;
-  const int grid = (n_tiles_max * nblk + kXcds - 1) / kXcds * kXcds;
+  const int items = n_tiles_max * nblk * (p.tiles == nullptr && p.k_splits > 1 ? p.k_splits : 1);
+  const int grid = (items + kXcds - 1) / kXcds * kXcds;
   const auto kernel = ffn_tiled_kernel<EPI>;
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), kSmem, stream, p, nblk);
   return hipGetLastError();
@@ -366,8 +373,19 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
 
 bool dense_gemm_f32_supported(int N, int Kd) { return N == kTN && Kd % kBK == 0; }
 
+// The most K splits (a divisor of the K-tile count, at most 16) that keep one output tile per
+// split item within one wave of workgroups on 256 CUs.
+int dense_gemm_splits(int rows, int Kd) {
+  const int tiles = (rows + kBM - 1) / kBM;
+  const int nkt = Kd / kBK;
+  int best = 1;
+  for (int s = 2; s <= 16 && s <= nkt; ++s)
+    if (nkt % s == 0 && tiles * s <= 256) best = s;
+  return best;
+}
+
 hipError_t launch_dense_gemm_f32(const uint16_t* A, int rows, const uint16_t* W, int N, int Kd,
-                                 float* out, hipStream_t stream) {
+                                 int splits, float* out, hipStream_t stream) {
   GroupedParams p{};
   p.A = A;
   p.a_rows = rows;
@@ -379,6 +397,7 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int rows, const uint16_t* W,
   p.out_f32 = out;
   p.N = N;
   p.Kd = Kd;
+  p.k_splits = splits;
   return launch_tiled(kEpiF32, p, (rows + kBM - 1) / kBM, stream);
 }
 

@@ -61,10 +61,13 @@ struct FfnProblem {
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t const* ev = nullptr);
 
 // Dense C[rows, N] (fp32) = A[rows, Kd] . W[N, Kd]^T on the tiled MFMA kernel (router logits
-// at large T). Supported when N == 256 and Kd % 64 == 0.
+// at large T). Supported when N == 256 and Kd % 64 == 0. The reduction is split into
+// dense_gemm_splits(rows, Kd) K ranges so that the launch fills the GPU; split s writes its
+// partial sums to out + s*rows*N (fp32, no atomics), and the caller adds the planes in order.
 bool dense_gemm_f32_supported(int N, int Kd);
+int dense_gemm_splits(int rows, int Kd);
 hipError_t launch_dense_gemm_f32(const uint16_t* A, int rows, const uint16_t* W, int N, int Kd,
-                                 float* out, hipStream_t stream);
+                                 int splits, float* out, hipStream_t stream);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,

@@ -9,7 +9,8 @@
 //  1. route_gemm: x [T,H] . Wr[E,H]^T on MFMA 16x16x32 bf16 with fp32 accumulation. The hidden
 //     dimension is split S ways when T is small so that enough workgroups stream Wr; each
 //     split writes its own fp32 partial [S,T,E] (no atomics). For T >= 1024 and E = 256 the
-//     LDS-tiled MFMA kernel of the expert FFN computes the logits in one pass instead.
+//     LDS-tiled MFMA kernel of the expert FFN computes the logits instead, with its own split
+//     of the hidden dimension into S partial planes.
 //  2. route_topk: one wavefront per token. Sums the S partials in split order, adds the bias,
 //     stores the logits, then selects the top-k by (logit descending, expert ascending) with
 //     wavefront arg-max reductions. Because the renormalised weight p_j / sum_top p_i equals
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 static bool route_tiled(int T, int H, int E) { return T >= 1024 && dense_gemm_f32_supported(E, H); }
 
 int route_splits(int T, int H, int E) {
-  if (route_tiled(T, H, E)) return 1;
+  if (route_tiled(T, H, E)) return dense_gemm_splits(T, H);
   const int tiles = ((T + kRouteTokTile - 1) / kRouteTokTile) * ((E + kRouteExpTile - 1) / kRouteExpTile);
   const int kmax = H / 128;  // each split covers a multiple of 128 hidden elements
   int best = 1;
@@ -179,7 +180,7 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w
                         const float* bias, float* logits, float* topk_w, int32_t* topk_idx,
                         float* partials, int S, hipStream_t stream) {
   if (route_tiled(s.T, s.H, s.E)) {
-    const hipError_t e = launch_dense_gemm_f32(x, s.T, w_router, s.E, s.H, partials, stream);
+    const hipError_t e = launch_dense_gemm_f32(x, s.T, w_router, s.E, s.H, S, partials, stream);
     if (e != hipSuccess) return e;
   } else {
     dim3 g1((s.T + kRouteTokTile - 1) / kRouteTokTile, (s.E + kRouteExpTile - 1) / kRouteExpTile, S);

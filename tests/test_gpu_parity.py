@@ -53,6 +53,12 @@ SMALL = {
                                            I=256, scale=2.827, seed=23),
 }
 
+# routing only: the tiled router with its hidden dimension split 12 ways (2 K-tiles per split)
+ROUTE_ONLY = {
+    "tiled_router_t2000_h1536_e256_k8": Workload("tiled_router_t2000_h1536_e256_k8", T=2000, H=1536,
+                                                 E=256, K=8, I=256, scale=2.827, seed=24),
+}
+
 
 # ----------------------------------------------------------------------------- end to end, small
 @pytest.mark.parametrize("name", list(SMALL))
@@ -130,10 +136,10 @@ def _ws(n):
 
 
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8", "no_renorm_t128",
-                                  "tiled_router_t1030_e256_k8"])
+                                  "tiled_router_t1030_e256_k8", "tiled_router_t2000_h1536_e256_k8"])
 def test_moe_route(name):
     _require_gpu()
-    wl = SMALL[name]
+    wl = {**SMALL, **ROUTE_ONLY}[name]
     dev = generate(wl, DEV)
     hw = P.host(dev)
     s = moe.Shape.of(wl)
