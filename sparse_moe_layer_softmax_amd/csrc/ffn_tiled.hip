@@ -23,8 +23,8 @@ namespace {
 //    register file of two wavefronts per SIMD allows. 320 rows also fit a whole expert at the
 //    prefill shape (about T*k/E = 256 rows each, never more than ~310) in one row tile.
 //  - K is staged 64 at a time through a two-stage LDS ring (2 x 72 KB) filled by direct
-//    global->LDS loads (global_load_lds_dwordx4, no VGPR staging). One such instruction moves
-//    1 KB: 8 rows of 128 bytes, whole L2 lines. The DMA of K-tile kt+1 is issued at the start of
+//    global->LDS loads (global_load_lds_dwordx4, no VGPR staging; non-temporal for the weights).
+//    One such instruction moves 1 KB: 8 rows of 128 bytes, whole L2 lines. The DMA of K-tile kt+1 is issued at the start of
 //    K-tile kt, so it has a whole K-tile of compute to land.
 //  - Each wavefront loads the activation rows of its own live 32-row fragments (one instruction
 //    per fragment) and an eighth of the weight tile, so rows past the end of a group cost neither
@@ -91,9 +91,13 @@ __device__ __forceinline__ void barrier_no_fence() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Global->LDS DMA of 16 bytes per lane. STREAM marks the load non-temporal (cache policy NT): used
+// for weight tiles, which few workgroups share and which otherwise displace the activation rows
+// that the n-blocks of a band re-read from L2.
+template <bool STREAM = false>
 __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, STREAM ? 2 : 0);
 }
 
 // EPI = kEpiSwiglu: gate/up rows interleaved, h = bf16(silu(clamp g) * clamp u);
@@ -161,7 +165,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
                 sA + stage * kStageA + (20 * half + quarter + 4 * i) * 512);
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i)
-      lds_dma16(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
+      lds_dma16<true>(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
   };
 
   f32x16_t acc[MV][2];
