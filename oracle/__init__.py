@@ -59,6 +59,12 @@ def _declare(L):
     L.oracle_combine.argtypes = [_I, _I, _I, _P, _P, _P, _P, _P]
     L.oracle_layer_forward.argtypes = [_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 9 + [_I] + [_P] * 12
     L.oracle_layer_dense.argtypes = [_I, _I, _I, _I, _I, _D] + [_P] * 11
+    L.oracle_double_from_e4m3.argtypes = [ctypes.c_uint8]
+    L.oracle_double_from_e4m3.restype = _D
+    L.oracle_gateup_rows_fp8.argtypes = [_I, _I, _I, _D] + [_P] * 6
+    L.oracle_down_rows_fp8.argtypes = [_I, _I, _I] + [_P] * 4
+    L.oracle_layer_forward_fp8.argtypes = [_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 15 + [_I] + [_P] * 12
+    L.oracle_layer_dense_fp8.argtypes = [_I, _I, _I, _I, _I, _D] + [_P] * 17
     L.oracle_num_threads.restype = _I
 
 
@@ -221,6 +227,103 @@ def layer_dense(x, wg, wu, wd, topk_idx, topk_w, slot_to_row, *, sg=None, su=Non
     lib().oracle_layer_dense(T, H, E, K, I, float(limit), _ptr(x), _ptr(wg), _ptr(wu), _ptr(wd),
                              _ptr(sg), _ptr(su), _ptr(sd), _ptr(topk_idx), _ptr(topk_w),
                              _ptr(slot_to_row), _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------------------- FP8 expert weights
+class Fp8:
+    """An FP8 weight matrix (or stack of matrices): E4M3 codes ``q`` (uint8, [..., rows, cols]) and
+    one fp32 scale per row ``scale`` ([..., rows]); weight value = scale * e4m3(code)."""
+
+    def __init__(self, q, scale):
+        self.q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+        self.scale = np.ascontiguousarray(np.asarray(scale, dtype=np.float32))
+        assert self.scale.shape == self.q.shape[:-1]
+
+    @property
+    def shape(self):
+        return self.q.shape
+
+
+def double_from_e4m3(code: int) -> float:
+    return lib().oracle_double_from_e4m3(int(code))
+
+
+def gateup_rows_fp8(x_rows, wg: Fp8, wu: Fp8, limit):
+    x_rows = _u16(x_rows)
+    n, H = x_rows.shape
+    I = wg.q.shape[0]
+    h = np.zeros((n, I), dtype=np.uint16)
+    if n:
+        lib().oracle_gateup_rows_fp8(n, H, I, float(limit), _ptr(x_rows), _ptr(wg.q), _ptr(wg.scale),
+                                     _ptr(wu.q), _ptr(wu.scale), _ptr(h))
+    return h
+
+
+def down_rows_fp8(h, wd: Fp8):
+    h = _u16(h)
+    n, I = h.shape
+    H = wd.q.shape[0]
+    y = np.zeros((n, H), dtype=np.uint16)
+    if n:
+        lib().oracle_down_rows_fp8(n, H, I, _ptr(h), _ptr(wd.q), _ptr(wd.scale), _ptr(y))
+    return y
+
+
+def expert_ffn_rows_fp8(x_rows, wg: Fp8, wu: Fp8, wd: Fp8, limit):
+    h = gateup_rows_fp8(x_rows, wg, wu, limit)
+    return h, down_rows_fp8(h, wd)
+
+
+def _fp8_ptrs(*ws):
+    out = []
+    for w in ws:
+        out += [None, None] if w is None else [_ptr(w.q), _ptr(w.scale)]
+    return out
+
+
+def layer_forward_fp8(x, wr, wg: Fp8, wu: Fp8, wd: Fp8, K, *, bias=None, sg=None, su=None,
+                      sd=None, scale=1.0, limit=10.0, capacity=0, norm_topk=True, logits=None):
+    """layer_forward with FP8 expert weights (routed and shared); returns the same dict."""
+    x, wr = _u16(x), _u16(wr)
+    T, H = x.shape
+    E, I = wg.q.shape[0], wg.q.shape[1]
+    use_logits = logits is not None
+    lg = _f32(logits).copy() if use_logits else np.zeros((T, E), dtype=np.float32)
+    r = dict(
+        logits=lg,
+        topk_idx=np.zeros((T, K), dtype=np.int32),
+        topk_w=np.zeros((T, K), dtype=np.float32),
+        counts=np.zeros(E, dtype=np.int32),
+        offsets=np.zeros(E + 1, dtype=np.int32),
+        row_to_slot=np.zeros(T * K, dtype=np.int32),
+        slot_to_row=np.zeros(T * K, dtype=np.int32),
+        h_routed=np.zeros((T * K, I), dtype=np.uint16),
+        y_routed=np.zeros((T * K, H), dtype=np.uint16),
+        out=np.zeros((T, H), dtype=np.uint16),
+    )
+    if sg is not None:
+        r["h_shared"] = np.zeros((T, I), dtype=np.uint16)
+        r["y_shared"] = np.zeros((T, H), dtype=np.uint16)
+    lib().oracle_layer_forward_fp8(
+        T, H, E, K, I, int(bool(norm_topk)), float(scale), float(limit), int(capacity),
+        _ptr(x), _ptr(wr), _ptr(_f32(bias)), *_fp8_ptrs(wg, wu, wd, sg, su, sd), int(use_logits),
+        _ptr(lg), _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+        _ptr(r["row_to_slot"]), _ptr(r["slot_to_row"]), _ptr(r["h_routed"]), _ptr(r["y_routed"]),
+        _ptr(r.get("h_shared")), _ptr(r.get("y_shared")), _ptr(r["out"]))
+    return r
+
+
+def layer_dense_fp8(x, wg: Fp8, wu: Fp8, wd: Fp8, topk_idx, topk_w, slot_to_row, *, sg=None,
+                    su=None, sd=None, limit=10.0):
+    x = _u16(x)
+    topk_idx, topk_w, slot_to_row = _i32(topk_idx), _f32(topk_w), _i32(slot_to_row)
+    T, H = x.shape
+    E, I = wg.q.shape[0], wg.q.shape[1]
+    K = topk_idx.shape[1]
+    out = np.zeros((T, H), dtype=np.uint16)
+    lib().oracle_layer_dense_fp8(T, H, E, K, I, float(limit), _ptr(x), *_fp8_ptrs(wg, wu, wd, sg, su, sd),
+                                 _ptr(topk_idx), _ptr(topk_w), _ptr(slot_to_row), _ptr(out))
     return out
 
 

@@ -39,6 +39,179 @@ inline double clamped_swiglu(double g, double u, double limit) {
   return g / (1.0 + std::exp(-g)) * u;
 }
 
+// OCP 8-bit floating point, E4M3 encoding: sign bit, 4 exponent bits (bias 7), 3 mantissa
+// bits; exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN and there are no
+// infinities, so the largest finite magnitude is 1.75 * 2^8 = 448.
+inline double e4m3(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  if (e == 15 && m == 7) return std::nan("");
+  const double v = e == 0 ? std::ldexp(static_cast<double>(m), -9)
+                          : std::ldexp(static_cast<double>(8 + m), e - 10);  // (1 + m/8) 2^(e-7)
+  return (c & 0x80) ? -v : v;
+}
+
+// Weight matrices [rows][cols] row-major: bf16 bits, or FP8 E4M3 codes with one fp32 scale per
+// row (weight value = scale[row] * e4m3(code)).
+struct Bf16W {
+  const uint16_t* p;
+  int cols;
+  double operator()(size_t r, size_t c) const { return bf(p[r * cols + c]); }
+};
+struct Fp8W {
+  const uint8_t* q;
+  const float* scale;
+  int cols;
+  double operator()(size_t r, size_t c) const {
+    return static_cast<double>(scale[r]) * e4m3(q[r * cols + c]);
+  }
+};
+
+// Expert weights of a layer: routed gate/up [E][I][H], down [E][H][I], shared [I][H], [H][I].
+struct Bf16Experts {
+  const uint16_t *wg, *wu, *wd, *sg, *su, *sd;
+  int H, I;
+  bool shared() const { return sg != nullptr; }
+  Bf16W gate(int e) const { return {wg + static_cast<size_t>(e) * I * H, H}; }
+  Bf16W up(int e) const { return {wu + static_cast<size_t>(e) * I * H, H}; }
+  Bf16W down(int e) const { return {wd + static_cast<size_t>(e) * H * I, I}; }
+  Bf16W sgate() const { return {sg, H}; }
+  Bf16W sup() const { return {su, H}; }
+  Bf16W sdown() const { return {sd, I}; }
+};
+struct Fp8Experts {
+  const uint8_t *qg, *qu, *qd, *sqg, *squ, *sqd;      // codes
+  const float *cg, *cu, *cd, *scg, *scu, *scd;        // per-row scales
+  int H, I;
+  bool shared() const { return sqg != nullptr; }
+  Fp8W gate(int e) const { return {qg + static_cast<size_t>(e) * I * H, cg + static_cast<size_t>(e) * I, H}; }
+  Fp8W up(int e) const { return {qu + static_cast<size_t>(e) * I * H, cu + static_cast<size_t>(e) * I, H}; }
+  Fp8W down(int e) const { return {qd + static_cast<size_t>(e) * H * I, cd + static_cast<size_t>(e) * H, I}; }
+  Fp8W sgate() const { return {sqg, scg, H}; }
+  Fp8W sup() const { return {squ, scu, H}; }
+  Fp8W sdown() const { return {sqd, scd, I}; }
+};
+
+// SwiGLU gate/up half of one expert on n gathered rows (see the header).
+template <class W>
+static void gateup_impl(int n, int H, int I, double limit, const uint16_t* x_rows, W wg, W wu,
+                        uint16_t* h) {
+#pragma omp parallel for schedule(static)
+  for (long ri = 0; ri < static_cast<long>(n) * I; ++ri) {
+    const long r = ri / I, i = ri % I;
+    const uint16_t* xr = x_rows + static_cast<size_t>(r) * H;
+    double g = 0.0, u = 0.0;
+    for (int k = 0; k < H; ++k) {
+      const double xv = bf(xr[k]);
+      g += xv * wg(i, k);
+      u += xv * wu(i, k);
+    }
+    h[static_cast<size_t>(r) * I + i] = oracle_bf16_from_double(clamped_swiglu(g, u, limit));
+  }
+}
+
+// Down projection of one expert (see the header).
+template <class W>
+static void down_impl(int n, int H, int I, const uint16_t* h, W wd, uint16_t* y) {
+#pragma omp parallel for schedule(static)
+  for (long rc = 0; rc < static_cast<long>(n) * H; ++rc) {
+    const long r = rc / H, c = rc % H;
+    const uint16_t* hr = h + static_cast<size_t>(r) * I;
+    double s = 0.0;
+    for (int i = 0; i < I; ++i) s += bf(hr[i]) * wd(c, i);
+    y[static_cast<size_t>(r) * H + c] = oracle_bf16_from_double(s);
+  }
+}
+
+// One expert's FFN over n gathered rows (gate/up then down).
+template <class W>
+static void expert_rows(int n, int H, int I, double limit, const uint16_t* x_rows, W wg, W wu,
+                        W wd, uint16_t* h_out, uint16_t* y_out) {
+  if (n == 0) return;
+  std::vector<uint16_t> hbuf;
+  uint16_t* h = h_out;
+  if (!h) {
+    hbuf.resize(static_cast<size_t>(n) * I);
+    h = hbuf.data();
+  }
+  gateup_impl(n, H, I, limit, x_rows, wg, wu, h);
+  down_impl(n, H, I, h, wd, y_out);
+}
+
+template <class X>
+static void layer_impl(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                       double limit, int capacity, const uint16_t* x, const uint16_t* wr,
+                       const float* bias, const X& w, int use_logits, float* logits,
+                       int32_t* topk_idx, float* topk_w, int32_t* counts, int32_t* offsets,
+                       int32_t* row_to_slot, int32_t* slot_to_row, uint16_t* h_routed,
+                       uint16_t* y_routed, uint16_t* h_shared, uint16_t* y_shared,
+                       uint16_t* out) {
+  // 1. router projection (skipped when the caller supplies the fp32 logits)
+  if (!use_logits) oracle_router_logits(T, H, E, x, wr, bias, nullptr, 0, logits);
+  // 2-4. softmax, top-k, renormalisation, routed scaling
+  oracle_route_from_logits(T, E, K, norm_topk, scale, logits, topk_idx, topk_w, nullptr);
+  // 5. dispatch
+  oracle_dispatch(T, K, E, capacity, topk_idx, counts, offsets, row_to_slot, slot_to_row);
+  // 6. routed experts, expert-major ([Hy3-explainer] 2.1: each expert runs on its gathered rows)
+  for (int e = 0; e < E; ++e) {
+    const int n = counts[e];
+    if (n == 0) continue;
+    std::vector<uint16_t> xg(static_cast<size_t>(n) * H);
+    for (int i = 0; i < n; ++i) {
+      const int t = row_to_slot[offsets[e] + i] / K;
+      std::memcpy(&xg[static_cast<size_t>(i) * H], x + static_cast<size_t>(t) * H,
+                  sizeof(uint16_t) * H);
+    }
+    expert_rows(n, H, I, limit, xg.data(), w.gate(e), w.up(e), w.down(e),
+                h_routed ? h_routed + static_cast<size_t>(offsets[e]) * I : nullptr,
+                y_routed + static_cast<size_t>(offsets[e]) * H);
+  }
+  // 7. shared expert on every token, weight 1 ([Hy4-deep-dive]: always active)
+  std::vector<uint16_t> ysbuf;
+  uint16_t* ys = y_shared;
+  if (w.shared()) {
+    if (!ys) {
+      ysbuf.resize(static_cast<size_t>(T) * H);
+      ys = ysbuf.data();
+    }
+    expert_rows(T, H, I, limit, x, w.sgate(), w.sup(), w.sdown(), h_shared, ys);
+  } else {
+    ys = nullptr;
+  }
+  // 8. combine
+  oracle_combine(T, K, H, topk_w, slot_to_row, y_routed, ys, out);
+}
+
+template <class X>
+static void dense_impl(int T, int H, int E, int K, int I, double limit, const uint16_t* x,
+                       const X& w, const int32_t* topk_idx, const float* topk_w,
+                       const int32_t* slot_to_row, uint16_t* out) {
+  // Every expert on every token: y_all[e][t][:]
+  std::vector<uint16_t> y_all(static_cast<size_t>(E) * T * H);
+  for (int e = 0; e < E; ++e)
+    expert_rows(T, H, I, limit, x, w.gate(e), w.up(e), w.down(e), nullptr,
+                &y_all[static_cast<size_t>(e) * T * H]);
+  std::vector<uint16_t> ys;
+  if (w.shared()) {
+    ys.resize(static_cast<size_t>(T) * H);
+    expert_rows(T, H, I, limit, x, w.sgate(), w.sup(), w.sdown(), nullptr, ys.data());
+  }
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    for (int c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < K; ++j) {
+        const size_t s = static_cast<size_t>(t) * K + j;
+        const double mask = slot_to_row[s] >= 0 ? 1.0 : 0.0;
+        const int e = topk_idx[s];
+        acc += mask * static_cast<double>(topk_w[s]) *
+               bf(y_all[(static_cast<size_t>(e) * T + t) * H + c]);
+      }
+      if (w.shared()) acc += bf(ys[static_cast<size_t>(t) * H + c]);
+      out[static_cast<size_t>(t) * H + c] = oracle_bf16_from_double(acc);
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,34 +327,27 @@ void oracle_dispatch(int T, int K, int E, int capacity, const int32_t* topk_idx,
   }
 }
 
+
 void oracle_gateup_rows(int n, int H, int I, double limit, const uint16_t* x_rows,
                         const uint16_t* wg, const uint16_t* wu, uint16_t* h) {
-#pragma omp parallel for schedule(static)
-  for (long ri = 0; ri < static_cast<long>(n) * I; ++ri) {
-    const long r = ri / I, i = ri % I;
-    const uint16_t* xr = x_rows + static_cast<size_t>(r) * H;
-    const uint16_t* gr = wg + static_cast<size_t>(i) * H;
-    const uint16_t* ur = wu + static_cast<size_t>(i) * H;
-    double g = 0.0, u = 0.0;
-    for (int k = 0; k < H; ++k) {
-      const double xv = bf(xr[k]);
-      g += xv * bf(gr[k]);
-      u += xv * bf(ur[k]);
-    }
-    h[static_cast<size_t>(r) * I + i] = oracle_bf16_from_double(clamped_swiglu(g, u, limit));
-  }
+  gateup_impl(n, H, I, limit, x_rows, Bf16W{wg, H}, Bf16W{wu, H}, h);
 }
 
 void oracle_down_rows(int n, int H, int I, const uint16_t* h, const uint16_t* wd, uint16_t* y) {
-#pragma omp parallel for schedule(static)
-  for (long rc = 0; rc < static_cast<long>(n) * H; ++rc) {
-    const long r = rc / H, c = rc % H;
-    const uint16_t* hr = h + static_cast<size_t>(r) * I;
-    const uint16_t* dr = wd + static_cast<size_t>(c) * I;
-    double s = 0.0;
-    for (int i = 0; i < I; ++i) s += bf(hr[i]) * bf(dr[i]);
-    y[static_cast<size_t>(r) * H + c] = oracle_bf16_from_double(s);
-  }
+  down_impl(n, H, I, h, Bf16W{wd, I}, y);
+}
+
+double oracle_double_from_e4m3(uint8_t code) { return e4m3(code); }
+
+void oracle_gateup_rows_fp8(int n, int H, int I, double limit, const uint16_t* x_rows,
+                            const uint8_t* qg, const float* cg, const uint8_t* qu,
+                            const float* cu, uint16_t* h) {
+  gateup_impl(n, H, I, limit, x_rows, Fp8W{qg, cg, H}, Fp8W{qu, cu, H}, h);
+}
+
+void oracle_down_rows_fp8(int n, int H, int I, const uint16_t* h, const uint8_t* qd,
+                          const float* cd, uint16_t* y) {
+  down_impl(n, H, I, h, Fp8W{qd, cd, I}, y);
 }
 
 void oracle_combine(int T, int K, int H, const float* topk_w, const int32_t* slot_to_row,
@@ -202,21 +368,6 @@ void oracle_combine(int T, int K, int H, const float* topk_w, const int32_t* slo
   }
 }
 
-// One expert's FFN over n gathered rows (gate/up then down), reusing the two halves above.
-static void expert_rows(int n, int H, int I, double limit, const uint16_t* x_rows,
-                        const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
-                        uint16_t* h_out, uint16_t* y_out) {
-  if (n == 0) return;
-  std::vector<uint16_t> hbuf;
-  uint16_t* h = h_out;
-  if (!h) {
-    hbuf.resize(static_cast<size_t>(n) * I);
-    h = hbuf.data();
-  }
-  oracle_gateup_rows(n, H, I, limit, x_rows, wg, wu, h);
-  oracle_down_rows(n, H, I, h, wd, y_out);
-}
-
 void oracle_layer_forward(int T, int H, int E, int K, int I, int norm_topk, double scale,
                           double limit, int capacity, const uint16_t* x, const uint16_t* wr,
                           const float* bias, const uint16_t* wg, const uint16_t* wu,
@@ -226,41 +377,27 @@ void oracle_layer_forward(int T, int H, int E, int K, int I, int norm_topk, doub
                           int32_t* row_to_slot, int32_t* slot_to_row, uint16_t* h_routed,
                           uint16_t* y_routed, uint16_t* h_shared, uint16_t* y_shared,
                           uint16_t* out) {
-  // 1. router projection (skipped when the caller supplies the fp32 logits)
-  if (!use_logits) oracle_router_logits(T, H, E, x, wr, bias, nullptr, 0, logits);
-  // 2-4. softmax, top-k, renormalisation, routed scaling
-  oracle_route_from_logits(T, E, K, norm_topk, scale, logits, topk_idx, topk_w, nullptr);
-  // 5. dispatch
-  oracle_dispatch(T, K, E, capacity, topk_idx, counts, offsets, row_to_slot, slot_to_row);
-  // 6. routed experts, expert-major ([Hy3-explainer] 2.1: each expert runs on its gathered rows)
-  const size_t wstride = static_cast<size_t>(I) * H;
-  for (int e = 0; e < E; ++e) {
-    const int n = counts[e];
-    if (n == 0) continue;
-    std::vector<uint16_t> xg(static_cast<size_t>(n) * H);
-    for (int i = 0; i < n; ++i) {
-      const int t = row_to_slot[offsets[e] + i] / K;
-      std::memcpy(&xg[static_cast<size_t>(i) * H], x + static_cast<size_t>(t) * H,
-                  sizeof(uint16_t) * H);
-    }
-    expert_rows(n, H, I, limit, xg.data(), wg + e * wstride, wu + e * wstride, wd + e * wstride,
-                h_routed ? h_routed + static_cast<size_t>(offsets[e]) * I : nullptr,
-                y_routed + static_cast<size_t>(offsets[e]) * H);
-  }
-  // 7. shared expert on every token, weight 1 ([Hy4-deep-dive]: always active)
-  std::vector<uint16_t> ysbuf;
-  uint16_t* ys = y_shared;
-  if (sg) {
-    if (!ys) {
-      ysbuf.resize(static_cast<size_t>(T) * H);
-      ys = ysbuf.data();
-    }
-    expert_rows(T, H, I, limit, x, sg, su, sd, h_shared, ys);
-  } else {
-    ys = nullptr;
-  }
-  // 8. combine
-  oracle_combine(T, K, H, topk_w, slot_to_row, y_routed, ys, out);
+  layer_impl(T, H, E, K, I, norm_topk, scale, limit, capacity, x, wr, bias,
+             Bf16Experts{wg, wu, wd, sg, su, sd, H, I}, use_logits, logits, topk_idx, topk_w,
+             counts, offsets, row_to_slot, slot_to_row, h_routed, y_routed, h_shared, y_shared,
+             out);
+}
+
+void oracle_layer_forward_fp8(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                              double limit, int capacity, const uint16_t* x, const uint16_t* wr,
+                              const float* bias, const uint8_t* qg, const float* cg,
+                              const uint8_t* qu, const float* cu, const uint8_t* qd,
+                              const float* cd, const uint8_t* sqg, const float* scg,
+                              const uint8_t* squ, const float* scu, const uint8_t* sqd,
+                              const float* scd, int use_logits, float* logits,
+                              int32_t* topk_idx, float* topk_w, int32_t* counts,
+                              int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                              uint16_t* h_routed, uint16_t* y_routed, uint16_t* h_shared,
+                              uint16_t* y_shared, uint16_t* out) {
+  layer_impl(T, H, E, K, I, norm_topk, scale, limit, capacity, x, wr, bias,
+             Fp8Experts{qg, qu, qd, sqg, squ, sqd, cg, cu, cd, scg, scu, scd, H, I}, use_logits,
+             logits, topk_idx, topk_w, counts, offsets, row_to_slot, slot_to_row, h_routed,
+             y_routed, h_shared, y_shared, out);
 }
 
 void oracle_layer_dense(int T, int H, int E, int K, int I, double limit, const uint16_t* x,
@@ -268,32 +405,20 @@ void oracle_layer_dense(int T, int H, int E, int K, int I, double limit, const u
                         const uint16_t* sg, const uint16_t* su, const uint16_t* sd,
                         const int32_t* topk_idx, const float* topk_w,
                         const int32_t* slot_to_row, uint16_t* out) {
-  // Every expert on every token: y_all[e][t][:]
-  const size_t wstride = static_cast<size_t>(I) * H;
-  std::vector<uint16_t> y_all(static_cast<size_t>(E) * T * H);
-  for (int e = 0; e < E; ++e)
-    expert_rows(T, H, I, limit, x, wg + e * wstride, wu + e * wstride, wd + e * wstride, nullptr,
-                &y_all[static_cast<size_t>(e) * T * H]);
-  std::vector<uint16_t> ys;
-  if (sg) {
-    ys.resize(static_cast<size_t>(T) * H);
-    expert_rows(T, H, I, limit, x, sg, su, sd, nullptr, ys.data());
-  }
-#pragma omp parallel for schedule(static)
-  for (int t = 0; t < T; ++t) {
-    for (int c = 0; c < H; ++c) {
-      double acc = 0.0;
-      for (int j = 0; j < K; ++j) {
-        const size_t s = static_cast<size_t>(t) * K + j;
-        const double mask = slot_to_row[s] >= 0 ? 1.0 : 0.0;
-        const int e = topk_idx[s];
-        acc += mask * static_cast<double>(topk_w[s]) *
-               bf(y_all[(static_cast<size_t>(e) * T + t) * H + c]);
-      }
-      if (sg) acc += bf(ys[static_cast<size_t>(t) * H + c]);
-      out[static_cast<size_t>(t) * H + c] = oracle_bf16_from_double(acc);
-    }
-  }
+  dense_impl(T, H, E, K, I, limit, x, Bf16Experts{wg, wu, wd, sg, su, sd, H, I}, topk_idx,
+             topk_w, slot_to_row, out);
+}
+
+void oracle_layer_dense_fp8(int T, int H, int E, int K, int I, double limit, const uint16_t* x,
+                            const uint8_t* qg, const float* cg, const uint8_t* qu,
+                            const float* cu, const uint8_t* qd, const float* cd,
+                            const uint8_t* sqg, const float* scg, const uint8_t* squ,
+                            const float* scu, const uint8_t* sqd, const float* scd,
+                            const int32_t* topk_idx, const float* topk_w,
+                            const int32_t* slot_to_row, uint16_t* out) {
+  dense_impl(T, H, E, K, I, limit, x,
+             Fp8Experts{qg, qu, qd, sqg, squ, sqd, cg, cu, cd, scg, scu, scd, H, I}, topk_idx,
+             topk_w, slot_to_row, out);
 }
 
 }  // extern "C"

@@ -106,6 +106,47 @@ void oracle_layer_dense(int T, int H, int E, int K, int I, double limit, const u
                         const int32_t* topk_idx, const float* topk_w,
                         const int32_t* slot_to_row, uint16_t* out);
 
+/* ---- FP8 expert weights. The pages deploy an FP8 checkpoint but define no format; the reading
+ * used here: every expert weight matrix ([Hy4-config] shapes) is stored as OCP FP8 E4M3 codes
+ * (uint8, row-major) with one fp32 scale per row (output channel), the weight value being
+ * scale[row] * e4m3(code). Router weights and activations stay bf16. */
+
+/* Exact value of an E4M3 code: sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+ * holds subnormals m * 2^-9; S.1111.111 is NaN (no infinities; largest finite 448). */
+double oracle_double_from_e4m3(uint8_t code);
+
+/* oracle_gateup_rows / oracle_down_rows with FP8 weights: qg, qu [I,H] codes with scales cg, cu
+ * [I]; qd [H,I] codes with scales cd [H]. Dot products in double over w = scale * e4m3(code). */
+void oracle_gateup_rows_fp8(int n, int H, int I, double limit, const uint16_t* x_rows,
+                            const uint8_t* qg, const float* cg, const uint8_t* qu,
+                            const float* cu, uint16_t* h);
+void oracle_down_rows_fp8(int n, int H, int I, const uint16_t* h, const uint8_t* qd,
+                          const float* cd, uint16_t* y);
+
+/* oracle_layer_forward with FP8 expert weights: routed qg, qu [E,I,H] (scales cg, cu [E,I]) and
+ * qd [E,H,I] (scales cd [E,H]); shared sqg, squ [I,H] (scales scg, scu [I]) and sqd [H,I]
+ * (scales scd [H]), NULL = no shared expert. Everything else as oracle_layer_forward. */
+void oracle_layer_forward_fp8(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                              double limit, int capacity, const uint16_t* x, const uint16_t* wr,
+                              const float* bias, const uint8_t* qg, const float* cg,
+                              const uint8_t* qu, const float* cu, const uint8_t* qd,
+                              const float* cd, const uint8_t* sqg, const float* scg,
+                              const uint8_t* squ, const float* scu, const uint8_t* sqd,
+                              const float* scd, int use_logits, float* logits,
+                              int32_t* topk_idx, float* topk_w, int32_t* counts,
+                              int32_t* offsets, int32_t* row_to_slot, int32_t* slot_to_row,
+                              uint16_t* h_routed, uint16_t* y_routed, uint16_t* h_shared,
+                              uint16_t* y_shared, uint16_t* out);
+
+/* oracle_layer_dense with FP8 expert weights (same weight arguments as above). */
+void oracle_layer_dense_fp8(int T, int H, int E, int K, int I, double limit, const uint16_t* x,
+                            const uint8_t* qg, const float* cg, const uint8_t* qu,
+                            const float* cu, const uint8_t* qd, const float* cd,
+                            const uint8_t* sqg, const float* scg, const uint8_t* squ,
+                            const float* scu, const uint8_t* sqd, const float* scd,
+                            const int32_t* topk_idx, const float* topk_w,
+                            const int32_t* slot_to_row, uint16_t* out);
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int oracle_num_threads(void);
 

@@ -15,6 +15,12 @@ Recipe: every tensor is drawn as float32 N(0, std^2) from its own torch generato
 ``1000 * workload.seed + tensor_id`` and rounded to bf16 (round-to-nearest-even). Routed expert
 weights are drawn one expert at a time. The optional router bias (Zipf-like popularity) is
 ``b_e = zipf * ln(1/(e+1))``, computed in float64 on the host and stored as float32.
+
+FP8 workloads (``fp8=True``) store every expert weight matrix, routed and shared, as OCP FP8 E4M3
+codes with one fp32 scale per row: the row is drawn as above in float32, its scale is
+max|w| / 448 (448 being the largest finite E4M3 value), and the codes are torch's round-to-nearest
+conversion of w / scale. This is checkpoint preparation, not part of the layer: the layer only
+ever reads the codes and scales.
 """
 from __future__ import annotations
 
@@ -46,6 +52,7 @@ class Workload:
     router_std: float = 0.02
     zipf: float = 0.0           # router bias b_e = zipf * ln(1/(e+1)); 0 = no bias
     seed: int = 0
+    fp8: bool = False           # expert weights as FP8 E4M3 codes + per-row fp32 scales
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -72,6 +79,10 @@ WORKLOADS = {
     "hy4_skew_t65536": Workload(
         "hy4_skew_t65536", T=65536, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
         w_std=0.006, router_std=0.006, zipf=1.2, seed=4),
+    # the decode batch with FP8 expert weights (the pages' deployment checkpoint is FP8)
+    "hy4_decode_t64_fp8": Workload(
+        "hy4_decode_t64_fp8", T=64, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, seed=5, fp8=True),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -94,10 +105,21 @@ def _randn_bf16(shape, std, gen, device):
         torch.bfloat16)
 
 
+def _randn_fp8(shape, std, gen, device):
+    """(E4M3 codes as uint8, fp32 per-row scale) of a float32 N(0, std^2) matrix."""
+    w = torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * std
+    scale = w.abs().amax(dim=-1) / 448.0
+    scale = torch.where(scale > 0, scale, torch.ones_like(scale))
+    q = (w / scale.unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q, scale
+
+
 def generate(wl: Workload, device="cpu", shared: bool = True):
     """Return a dict of torch tensors on ``device``:
     x [T,H], w_router [E,H], router_bias [E] fp32 or None, w_gate/w_up [E,I,H], w_down [E,H,I],
-    s_gate/s_up [I,H], s_down [H,I] (None without a shared expert). bf16 unless noted."""
+    s_gate/s_up [I,H], s_down [H,I] (None without a shared expert). bf16 unless noted. For FP8
+    workloads the expert weights are uint8 E4M3 codes and each has a ``<name>_scale`` fp32 tensor
+    of its leading dimensions ([E,I], [E,H], [I], [H])."""
     dev = torch.device(device)
     out = {}
     out["x"] = _randn_bf16((wl.T, wl.H), wl.x_std, _gen(wl, "x", dev), dev)
@@ -106,16 +128,28 @@ def generate(wl: Workload, device="cpu", shared: bool = True):
     out["router_bias"] = None if b is None else b.to(dev)
     for name, shp in (("w_gate", (wl.I, wl.H)), ("w_up", (wl.I, wl.H)), ("w_down", (wl.H, wl.I))):
         g = _gen(wl, name, dev)
-        w = torch.empty((wl.E,) + shp, dtype=torch.bfloat16, device=dev)
-        for e in range(wl.E):
-            w[e] = _randn_bf16(shp, wl.w_std, g, dev)
+        if wl.fp8:
+            w = torch.empty((wl.E,) + shp, dtype=torch.uint8, device=dev)
+            sc = torch.empty((wl.E, shp[0]), dtype=torch.float32, device=dev)
+            for e in range(wl.E):
+                w[e], sc[e] = _randn_fp8(shp, wl.w_std, g, dev)
+            out[name + "_scale"] = sc
+        else:
+            w = torch.empty((wl.E,) + shp, dtype=torch.bfloat16, device=dev)
+            for e in range(wl.E):
+                w[e] = _randn_bf16(shp, wl.w_std, g, dev)
         out[name] = w
-    if shared and wl.n_shared:
-        out["s_gate"] = _randn_bf16((wl.I, wl.H), wl.w_std, _gen(wl, "s_gate", dev), dev)
-        out["s_up"] = _randn_bf16((wl.I, wl.H), wl.w_std, _gen(wl, "s_up", dev), dev)
-        out["s_down"] = _randn_bf16((wl.H, wl.I), wl.w_std, _gen(wl, "s_down", dev), dev)
-    else:
-        out["s_gate"] = out["s_up"] = out["s_down"] = None
+    for name, shp in (("s_gate", (wl.I, wl.H)), ("s_up", (wl.I, wl.H)), ("s_down", (wl.H, wl.I))):
+        if shared and wl.n_shared:
+            g = _gen(wl, name, dev)
+            if wl.fp8:
+                out[name], out[name + "_scale"] = _randn_fp8(shp, wl.w_std, g, dev)
+            else:
+                out[name] = _randn_bf16(shp, wl.w_std, g, dev)
+        else:
+            out[name] = None
+            if wl.fp8:
+                out[name + "_scale"] = None
     return out
 
 
