@@ -4,7 +4,8 @@
 One step = one moe_layer_forward (router GEMM + softmax/top-k/renorm/scale, dispatch, routed and
 shared SwiGLU expert FFNs, combine) over one batch of synthetic, seeded inputs already resident
 in HBM. Default workload: the Hy4-shape decode batch (T=64, H=6144, 256 experts, top-8, one
-shared expert, intermediate 2048, bf16). Prints one JSON line.
+shared expert, intermediate 2048, bf16); ``--workload hy4_decode_t64_fp8`` runs the same batch
+with FP8 E4M3 expert weights (per-row fp32 scales). Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain device copy, for scaling HBM counters
@@ -40,14 +41,20 @@ def algorithmic(wl, counts):
     T, H, E, K, I, S = wl.T, wl.H, wl.E, wl.K, wl.I, wl.n_shared
     R = int(counts.sum())
     touched = int((counts > 0).sum())
+    # bytes of one expert's gate+up and down weights: bf16, or one-byte E4M3 codes plus one fp32
+    # scale per weight row
+    if wl.fp8:
+        w_gu, w_dn = 2 * H * I + 4 * 2 * I, H * I + 4 * H
+    else:
+        w_gu, w_dn = 4 * H * I, 2 * H * I
     layer_flops = 2 * T * H * E + 6 * H * I * (R + S * T)
-    layer_bytes = (touched + S) * 6 * H * I + 2 * E * H + 2 * 2 * T * H + 4 * T * E + 8 * T * K
+    layer_bytes = (touched + S) * (w_gu + w_dn) + 2 * E * H + 2 * 2 * T * H + 4 * T * E + 8 * T * K
     # gate/up grouped GEMM launch: its weights, x in, h out
     gu_flops = 4 * H * I * (R + S * T)
-    gu_bytes = (touched + S) * 4 * H * I + 2 * T * H + 2 * (R + S * T) * I
+    gu_bytes = (touched + S) * w_gu + 2 * T * H + 2 * (R + S * T) * I
     # down grouped GEMM launch: its weights, h in, y out
     dn_flops = 2 * H * I * (R + S * T)
-    dn_bytes = (touched + S) * 2 * H * I + 2 * (R + S * T) * I + 2 * (R + S * T) * H
+    dn_bytes = (touched + S) * w_dn + 2 * (R + S * T) * I + 2 * (R + S * T) * H
     return dict(R=R, touched=touched, layer_flops=layer_flops, layer_bytes=layer_bytes,
                 gu_flops=gu_flops, gu_bytes=gu_bytes, dn_flops=dn_flops, dn_bytes=dn_bytes)
 
@@ -102,8 +109,16 @@ def cpu_baseline(wl, dev, n_tok):
     lg = oracle.router_logits(x, wr, bias)
     idx, _ = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
     experts = sorted(set(int(e) for e in idx.ravel()))
-    W = {e: (as_u16(dev["w_gate"][e]), as_u16(dev["w_up"][e]), as_u16(dev["w_down"][e])) for e in experts}
-    SW = (as_u16(dev["s_gate"]), as_u16(dev["s_up"]), as_u16(dev["s_down"])) if wl.n_shared else None
+    def host_w(name, e=None):
+        t = dev[name] if e is None else dev[name][e]
+        if wl.fp8:
+            sc = dev[name + "_scale"] if e is None else dev[name + "_scale"][e]
+            return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
+        return as_u16(t)
+
+    ffn = oracle.expert_ffn_rows_fp8 if wl.fp8 else oracle.expert_ffn_rows
+    W = {e: tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down")) for e in experts}
+    SW = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
     t0 = time.perf_counter()
     lg = oracle.router_logits(x, wr, bias)
     idx, w = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
@@ -111,8 +126,8 @@ def cpu_baseline(wl, dev, n_tok):
     y = np.zeros((len(toks) * wl.K, wl.H), np.uint16)
     for e in experts:  # expert-major, as the oracle's layer does
         a, b = offsets[e], offsets[e + 1]
-        _, y[a:b] = oracle.expert_ffn_rows(x[r2s[a:b] // wl.K], *W[e], wl.limit)
-    ys = oracle.expert_ffn_rows(x, *SW, wl.limit)[1] if SW else None
+        _, y[a:b] = ffn(x[r2s[a:b] // wl.K], *W[e], wl.limit)
+    ys = ffn(x, *SW, wl.limit)[1] if SW else None
     oracle.combine(w, s2r, y, ys)
     dt = time.perf_counter() - t0
     return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
@@ -153,8 +168,7 @@ def main():
     torch.cuda.set_device(0)
     dev = generate_inputs(wl)
     shape = moe.Shape.of(wl)
-    layer = moe.MoELayer(shape, dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
-                         dev["s_gate"], dev["s_up"], dev["s_down"], dev["router_bias"])
+    layer = moe.MoELayer.from_inputs(shape, dev)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -174,10 +188,8 @@ def main():
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    wr, b, wg, wu, wd, sg, su, sd = layer.w
     for i in range(args.steps):
-        moe.moe_layer_forward_profiled(shape, dev["x"], wr, b, wg, wu, wd, sg, su, sd, out,
-                                       layer.ws, handles[i], stream)
+        layer.forward(dev["x"], out, stream=stream, phase_events=handles[i])
     stop.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / args.steps
@@ -190,8 +202,11 @@ def main():
     gu_s = phase_ms["gate_up_gemm"] / 1e3
     dn_s = phase_ms["down_gemm"] / 1e3
     rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s)
-    tiled = wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
-    kname = "ffn_tiled_kernel<kEpiSwiglu>" if tiled else "ffn_skinny_kernel<true>"
+    # the tiled MFMA kernel takes bf16 weights with at least 64 rows per group on average; FP8
+    # weights always stream through the skinny kernel
+    tiled = not wl.fp8 and wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
+    kname = ("ffn_tiled_kernel<kEpiSwiglu>" if tiled else
+             "ffn_skinny_kernel<true, %s>" % ("true" if wl.fp8 else "false"))
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
@@ -213,7 +228,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I,
                    "n_shared": wl.n_shared, "routed_scaling": wl.scale, "swiglu_limit": wl.limit,
-                   "capacity": wl.capacity, "parallelism": "none (1 GPU)"},
+                   "capacity": wl.capacity, "parallelism": "none (1 GPU)",
+                   "expert_weights": "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16"},
         "roofline": rf,
         "layer": {"algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"],
                   "hbm_GBs": round(alg["layer_bytes"] / layer_s / 1e9, 1),

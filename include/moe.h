@@ -187,6 +187,42 @@ int moe_layer_forward_profiled(const moe_shape* shape, const uint16_t* x,
                                void* ws, size_t ws_bytes, hipStream_t stream,
                                hipEvent_t const* phase_events);
 
+/* ---------------------------------------------------------------- FP8 expert weights
+ * The pages deploy the model from an FP8 checkpoint ("Tencent Hunyuan Hy4 Preview deep
+ * technical analysis", deployment commands; Hy4 config walkthrough, dtype notes) but define no
+ * weight format. Format used here: each expert weight matrix (routed and shared gate, up, down)
+ * is stored as OCP FP8 E4M3 codes (uint8, same [rows, cols] layout as the bf16 weights) plus
+ * one fp32 scale per row (output channel); the weight value is scale[row] * e4m3(code). The
+ * router weights, activations and every stored intermediate stay bf16 exactly as in the bf16
+ * entry points, whose definitions these follow; the codes must not be NaN (0x7F, 0xFF).
+ * Each projection is computed as scale[col] * sum_k a[k] * e4m3(code[col,k]) with the products
+ * summed in fp32, then rounded where the bf16 path rounds.
+ *
+ * moe_expert_ffn_fp8: moe_expert_ffn with
+ *   w_gate, w_up [G,I,H] E4M3 codes, w_gate_scale, w_up_scale [G,I] fp32,
+ *   w_down [G,H,I] E4M3 codes, w_down_scale [G,H] fp32.
+ * ws: moe_expert_ffn_workspace_size(shape, G, rows_max) bytes (the same as for bf16).           */
+int moe_expert_ffn_fp8(const moe_shape* shape, int32_t n_groups, int32_t rows_max,
+                       const uint16_t* x, const int32_t* row_to_slot,
+                       const int32_t* group_offsets, const uint8_t* w_gate,
+                       const float* w_gate_scale, const uint8_t* w_up, const float* w_up_scale,
+                       const uint8_t* w_down, const float* w_down_scale, uint16_t* h,
+                       uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward_profiled with FP8 expert weights:
+ *   w_gate, w_up [E,I,H] codes + [E,I] scales;  w_down [E,H,I] codes + [E,H] scales
+ *   s_gate, s_up [I,H] codes + [I] scales;      s_down [H,I] codes + [H] scales (all NULL iff
+ *                                               n_shared == 0)
+ * Workspace, layout, outputs and phase_events (may be NULL) as for the bf16 layer.            */
+int moe_layer_forward_fp8(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                          const float* bias, const uint8_t* w_gate, const float* w_gate_scale,
+                          const uint8_t* w_up, const float* w_up_scale, const uint8_t* w_down,
+                          const float* w_down_scale, const uint8_t* s_gate,
+                          const float* s_gate_scale, const uint8_t* s_up,
+                          const float* s_up_scale, const uint8_t* s_down,
+                          const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream, hipEvent_t const* phase_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ EXPORTED = (
     "moe_strerror", "moe_route_workspace_size", "moe_route", "moe_permute_workspace_size",
     "moe_permute", "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "moe_layer_forward",
-    "moe_layer_forward_profiled",
+    "moe_layer_forward_profiled", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
 )
 MOE_LAYER_PHASE_EVENTS = 7
 
@@ -93,6 +93,8 @@ def _load():
         "moe_layer_workspace_layout": ([sp, ctypes.POINTER(moe_layer_ws_layout)], ctypes.c_int),
         "moe_layer_forward": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P], ctypes.c_int),
         "moe_layer_forward_profiled": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P, P], ctypes.c_int),
+        "moe_expert_ffn_fp8": ([sp, I32, I32] + [P] * 12 + [S, P], ctypes.c_int),
+        "moe_layer_forward_fp8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -210,23 +212,73 @@ def moe_layer_forward_profiled(shape: Shape, x, w_router, bias, w_gate, w_up, w_
         _stream(stream), phase_events), "moe_layer_forward_profiled")
 
 
+def moe_expert_ffn_fp8(shape: Shape, n_groups: int, rows_max: int, x, row_to_slot, group_offsets,
+                       w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale, h, y, ws,
+                       stream=None):
+    """moe_expert_ffn with FP8 E4M3 weight codes (uint8) and per-row fp32 scales."""
+    _check(library().moe_expert_ffn_fp8(
+        ctypes.byref(shape.c()), n_groups, rows_max, _p(x), _p(row_to_slot), _p(group_offsets),
+        _p(w_gate), _p(w_gate_scale), _p(w_up), _p(w_up_scale), _p(w_down), _p(w_down_scale),
+        _p(h), _p(y), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_expert_ffn_fp8")
+
+
+def moe_layer_forward_fp8(shape: Shape, x, w_router, bias, w_gate, w_gate_scale, w_up, w_up_scale,
+                          w_down, w_down_scale, s_gate, s_gate_scale, s_up, s_up_scale, s_down,
+                          s_down_scale, out, ws, phase_events=None, stream=None):
+    """moe_layer_forward with FP8 expert weights; phase_events as for moe_layer_forward_profiled."""
+    _check(library().moe_layer_forward_fp8(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_gate_scale),
+        _p(w_up), _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(s_gate), _p(s_gate_scale),
+        _p(s_up), _p(s_up_scale), _p(s_down), _p(s_down_scale), _p(out), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream), phase_events),
+        "moe_layer_forward_fp8")
+
+
 # ----------------------------------------------------------------------------- conveniences
+_WEIGHTS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
+
+
 class MoELayer:
-    """Holds device weights and a workspace; ``forward(x)`` runs moe_layer_forward."""
+    """Holds device weights and a workspace; ``forward(x)`` runs moe_layer_forward (bf16 expert
+    weights) or moe_layer_forward_fp8 (uint8 E4M3 expert weights; ``scales`` then maps each weight
+    name of _WEIGHTS to its fp32 per-row scale tensor)."""
 
     def __init__(self, shape: Shape, w_router, w_gate, w_up, w_down, s_gate=None, s_up=None,
-                 s_down=None, router_bias=None):
+                 s_down=None, router_bias=None, scales=None):
         self.shape = shape
         self.w = (w_router, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
+        self.fp8 = w_gate.dtype == torch.uint8
+        self.scales = scales or {}
+        if self.fp8:
+            for n, t in zip(_WEIGHTS, (w_gate, w_up, w_down, s_gate, s_up, s_down)):
+                if t is not None and self.scales.get(n) is None:
+                    raise ValueError("FP8 weight %s needs a scale tensor" % n)
         self.device = w_router.device
         self.ws = _ws(moe_layer_workspace_size(shape), self.device)
         self.layout = moe_layer_workspace_layout(shape)
 
-    def forward(self, x, out=None, stream=None):
+    @classmethod
+    def from_inputs(cls, shape: Shape, d: dict):
+        """Build from a ``workloads.generate`` dict (bf16 or FP8 expert weights)."""
+        scales = {n: d.get(n + "_scale") for n in _WEIGHTS}
+        return cls(shape, d["w_router"], d["w_gate"], d["w_up"], d["w_down"], d["s_gate"], d["s_up"],
+                   d["s_down"], d["router_bias"], scales=scales)
+
+    def forward(self, x, out=None, stream=None, phase_events=None):
         if out is None:
             out = torch.empty((self.shape.T, self.shape.H), dtype=torch.bfloat16, device=self.device)
         wr, b, wg, wu, wd, sg, su, sd = self.w
-        moe_layer_forward(self.shape, x, wr, b, wg, wu, wd, sg, su, sd, out, self.ws, stream)
+        if self.fp8:
+            sc = self.scales
+            moe_layer_forward_fp8(self.shape, x, wr, b, wg, sc["w_gate"], wu, sc["w_up"], wd,
+                                  sc["w_down"], sg, sc.get("s_gate"), su, sc.get("s_up"), sd,
+                                  sc.get("s_down"), out, self.ws, phase_events, stream)
+        elif phase_events is not None:
+            moe_layer_forward_profiled(self.shape, x, wr, b, wg, wu, wd, sg, su, sd, out, self.ws,
+                                       phase_events, stream)
+        else:
+            moe_layer_forward(self.shape, x, wr, b, wg, wu, wd, sg, su, sd, out, self.ws, stream)
         return out
 
     def intermediate(self, name: str, dtype, shape):

@@ -100,6 +100,168 @@ inline bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 25
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
+// One set of expert weights (gate, up, down): bf16, or FP8 E4M3 codes with per-row scales.
+struct Weights {
+  bool w8;
+  const uint16_t *gate, *up, *down;
+  const uint8_t *qgate, *qup, *qdown;
+  const float *sgate, *sup, *sdown;
+  static Weights bf16(const uint16_t* g, const uint16_t* u, const uint16_t* d) {
+    Weights w{};
+    w.gate = g;
+    w.up = u;
+    w.down = d;
+    return w;
+  }
+  static Weights fp8(const uint8_t* g, const float* gs, const uint8_t* u, const float* us,
+                     const uint8_t* d, const float* ds) {
+    Weights w{};
+    w.w8 = true;
+    w.qgate = g;
+    w.sgate = gs;
+    w.qup = u;
+    w.sup = us;
+    w.qdown = d;
+    w.sdown = ds;
+    return w;
+  }
+  // every pointer of the set given
+  bool complete() const {
+    return w8 ? (qgate && sgate && qup && sup && qdown && sdown) : (gate && up && down);
+  }
+  // no pointer of the set given
+  bool empty() const {
+    return !gate && !up && !down && !qgate && !sgate && !qup && !sup && !qdown && !sdown;
+  }
+};
+
+// the *_a (groups < g_split) or *_b weights of an FFN problem
+void set_weights(moe::FfnProblem& p, const Weights& w, bool a) {
+  p.w8 = w.w8;
+  (a ? p.gate_a : p.gate_b) = w.gate;
+  (a ? p.up_a : p.up_b) = w.up;
+  (a ? p.down_a : p.down_b) = w.down;
+  (a ? p.qgate_a : p.qgate_b) = w.qgate;
+  (a ? p.qup_a : p.qup_b) = w.qup;
+  (a ? p.qdown_a : p.qdown_b) = w.qdown;
+  (a ? p.sgate_a : p.sgate_b) = w.sgate;
+  (a ? p.sup_a : p.sup_b) = w.sup;
+  (a ? p.sdown_a : p.sdown_b) = w.sdown;
+}
+
+int expert_ffn_impl(const moe_shape* s, int32_t n_groups, int32_t rows_max, const uint16_t* x,
+                    const int32_t* row_to_slot, const int32_t* group_offsets, const Weights& wt,
+                    uint16_t* h, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!x || !wt.complete() || !y || !ws) return MOE_ERR_INVALID_ARG;
+  if (n_groups < 1 || n_groups > 1024 || rows_max < 1) return MOE_ERR_INVALID_ARG;
+  if (!row_to_slot && rows_max > s->T) return MOE_ERR_INVALID_ARG;
+  if (!group_offsets && n_groups != 1) return MOE_ERR_INVALID_ARG;
+  const FfnWs w = ffn_ws(*s, n_groups, rows_max, h == nullptr);
+  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  const int32_t* offs = group_offsets;
+  if (!offs) {
+    int32_t* o = reinterpret_cast<int32_t*>(at(ws, w.offsets));
+    rc = hip_status(moe::launch_single_group_offsets(o, rows_max, stream));
+    if (rc != MOE_OK) return rc;
+    offs = o;
+  }
+  moe::FfnProblem p{};
+  p.x = x;
+  p.T = s->T;
+  p.gather = row_to_slot;
+  p.n_ident = row_to_slot ? 0 : INT_MAX;
+  p.topk = s->K;
+  p.offsets = offs;
+  p.n_groups = n_groups;
+  p.rows_max = rows_max;
+  p.g_split = 0;
+  set_weights(p, wt, false);
+  p.H = s->H;
+  p.I = s->I;
+  p.limit = s->swiglu_limit;
+  p.h = h ? h : reinterpret_cast<uint16_t*>(at(ws, w.h));
+  p.y = y;
+  p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  return hip_status(moe::launch_ffn(p, stream));
+}
+
+int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, const float* bias,
+               const Weights& routed, const Weights& shared_w, uint16_t* out, void* ws,
+               size_t ws_bytes, hipStream_t stream, hipEvent_t const* ev) {
+  auto mark = [&](int i) {
+    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
+  };
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!x || !w_router || !routed.complete() || !out || !ws) return MOE_ERR_INVALID_ARG;
+  const bool shared = s->n_shared == 1;
+  if (shared != shared_w.complete()) return MOE_ERR_INVALID_ARG;
+  if (!shared && !shared_w.empty()) return MOE_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(out) & 15u) return MOE_ERR_INVALID_ARG;
+  const LayerWs w = layer_ws(*s);
+  if (ws_bytes < w.pub.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+
+  float* logits = reinterpret_cast<float*>(at(ws, w.pub.logits));
+  float* topk_w = reinterpret_cast<float*>(at(ws, w.pub.topk_w));
+  int32_t* topk_idx = reinterpret_cast<int32_t*>(at(ws, w.pub.topk_idx));
+  int32_t* counts = reinterpret_cast<int32_t*>(at(ws, w.pub.counts));
+  int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, w.pub.offsets));
+  int32_t* r2s = reinterpret_cast<int32_t*>(at(ws, w.pub.row_to_slot));
+  int32_t* s2r = reinterpret_cast<int32_t*>(at(ws, w.pub.slot_to_row));
+  uint16_t* h = reinterpret_cast<uint16_t*>(at(ws, w.pub.h));
+  uint16_t* y = reinterpret_cast<uint16_t*>(at(ws, w.pub.y));
+  int32_t* ext = reinterpret_cast<int32_t*>(at(ws, w.ext_offsets));
+
+  mark(0);
+  const RouteWs rw = route_ws(*s);
+  rc = hip_status(moe::launch_route(*s, x, w_router, bias, logits, topk_w, topk_idx,
+                                    reinterpret_cast<float*>(at(ws, w.route + rw.partials)), rw.S,
+                                    stream));
+  if (rc != MOE_OK) return rc;
+  mark(1);
+
+  const PermuteWs pw = permute_ws(*s);
+  const int n_ident = shared ? s->T : 0;
+  rc = hip_status(moe::launch_permute(
+      *s, topk_idx, counts, offsets, r2s, s2r,
+      reinterpret_cast<int32_t*>(at(ws, w.permute + pw.block_counts)),
+      reinterpret_cast<int32_t*>(at(ws, w.permute + pw.block_base)), shared ? ext : nullptr,
+      n_ident, stream));
+  if (rc != MOE_OK) return rc;
+  mark(2);
+
+  // routed experts and the shared expert in one grouped launch per projection:
+  // group 0 = shared expert over rows [0, T) (identity), groups 1..E = routed experts
+  moe::FfnProblem p{};
+  p.x = x;
+  p.T = s->T;
+  p.gather = r2s;
+  p.n_ident = n_ident;
+  p.topk = s->K;
+  p.offsets = shared ? ext : offsets;
+  p.n_groups = s->E + (shared ? 1 : 0);
+  p.rows_max = n_ident + s->T * s->K;
+  p.g_split = shared ? 1 : 0;
+  if (shared) set_weights(p, shared_w, true);
+  set_weights(p, routed, false);
+  p.H = s->H;
+  p.I = s->I;
+  p.limit = s->swiglu_limit;
+  p.h = h;
+  p.y = y;
+  p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  rc = hip_status(moe::launch_ffn(p, stream, ev ? ev + 3 : nullptr));
+  if (rc != MOE_OK) return rc;
+
+  const uint16_t* y_routed = y + static_cast<size_t>(n_ident) * s->H;
+  rc = hip_status(moe::launch_combine(*s, y_routed, topk_w, s2r, shared ? y : nullptr, out,
+                                      stream));
+  mark(6);
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -161,41 +323,19 @@ int moe_expert_ffn(const moe_shape* s, int32_t n_groups, int32_t rows_max, const
                    const int32_t* row_to_slot, const int32_t* group_offsets,
                    const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                    uint16_t* h, uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int rc = check_shape(s);
-  if (rc != MOE_OK) return rc;
-  if (!x || !w_gate || !w_up || !w_down || !y || !ws) return MOE_ERR_INVALID_ARG;
-  if (n_groups < 1 || n_groups > 1024 || rows_max < 1) return MOE_ERR_INVALID_ARG;
-  if (!row_to_slot && rows_max > s->T) return MOE_ERR_INVALID_ARG;
-  if (!group_offsets && n_groups != 1) return MOE_ERR_INVALID_ARG;
-  const FfnWs w = ffn_ws(*s, n_groups, rows_max, h == nullptr);
-  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
-  const int32_t* offs = group_offsets;
-  if (!offs) {
-    int32_t* o = reinterpret_cast<int32_t*>(at(ws, w.offsets));
-    rc = hip_status(moe::launch_single_group_offsets(o, rows_max, stream));
-    if (rc != MOE_OK) return rc;
-    offs = o;
-  }
-  moe::FfnProblem p{};
-  p.x = x;
-  p.T = s->T;
-  p.gather = row_to_slot;
-  p.n_ident = row_to_slot ? 0 : INT_MAX;
-  p.topk = s->K;
-  p.offsets = offs;
-  p.n_groups = n_groups;
-  p.rows_max = rows_max;
-  p.g_split = 0;
-  p.gate_b = w_gate;
-  p.up_b = w_up;
-  p.down_b = w_down;
-  p.H = s->H;
-  p.I = s->I;
-  p.limit = s->swiglu_limit;
-  p.h = h ? h : reinterpret_cast<uint16_t*>(at(ws, w.h));
-  p.y = y;
-  p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
-  return hip_status(moe::launch_ffn(p, stream));
+  return expert_ffn_impl(s, n_groups, rows_max, x, row_to_slot, group_offsets,
+                         Weights::bf16(w_gate, w_up, w_down), h, y, ws, ws_bytes, stream);
+}
+
+int moe_expert_ffn_fp8(const moe_shape* s, int32_t n_groups, int32_t rows_max,
+                       const uint16_t* x, const int32_t* row_to_slot,
+                       const int32_t* group_offsets, const uint8_t* w_gate,
+                       const float* w_gate_scale, const uint8_t* w_up, const float* w_up_scale,
+                       const uint8_t* w_down, const float* w_down_scale, uint16_t* h,
+                       uint16_t* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return expert_ffn_impl(s, n_groups, rows_max, x, row_to_slot, group_offsets,
+                         Weights::fp8(w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale),
+                         h, y, ws, ws_bytes, stream);
 }
 
 int moe_combine(const moe_shape* s, const uint16_t* y_routed, const float* topk_w,
@@ -238,80 +378,22 @@ int moe_layer_forward_profiled(const moe_shape* s, const uint16_t* x, const uint
                                const uint16_t* s_up, const uint16_t* s_down, uint16_t* out,
                                void* ws, size_t ws_bytes, hipStream_t stream,
                                hipEvent_t const* ev) {
-  auto mark = [&](int i) {
-    if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
-  };
-  int rc = check_shape(s);
-  if (rc != MOE_OK) return rc;
-  if (!x || !w_router || !w_gate || !w_up || !w_down || !out || !ws) return MOE_ERR_INVALID_ARG;
-  const bool shared = s->n_shared == 1;
-  if (shared != (s_gate && s_up && s_down)) return MOE_ERR_INVALID_ARG;
-  if (!shared && (s_gate || s_up || s_down)) return MOE_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(out) & 15u) return MOE_ERR_INVALID_ARG;
-  const LayerWs w = layer_ws(*s);
-  if (ws_bytes < w.pub.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  return layer_impl(s, x, w_router, bias, Weights::bf16(w_gate, w_up, w_down),
+                    Weights::bf16(s_gate, s_up, s_down), out, ws, ws_bytes, stream, ev);
+}
 
-  float* logits = reinterpret_cast<float*>(at(ws, w.pub.logits));
-  float* topk_w = reinterpret_cast<float*>(at(ws, w.pub.topk_w));
-  int32_t* topk_idx = reinterpret_cast<int32_t*>(at(ws, w.pub.topk_idx));
-  int32_t* counts = reinterpret_cast<int32_t*>(at(ws, w.pub.counts));
-  int32_t* offsets = reinterpret_cast<int32_t*>(at(ws, w.pub.offsets));
-  int32_t* r2s = reinterpret_cast<int32_t*>(at(ws, w.pub.row_to_slot));
-  int32_t* s2r = reinterpret_cast<int32_t*>(at(ws, w.pub.slot_to_row));
-  uint16_t* h = reinterpret_cast<uint16_t*>(at(ws, w.pub.h));
-  uint16_t* y = reinterpret_cast<uint16_t*>(at(ws, w.pub.y));
-  int32_t* ext = reinterpret_cast<int32_t*>(at(ws, w.ext_offsets));
-
-  mark(0);
-  const RouteWs rw = route_ws(*s);
-  rc = hip_status(moe::launch_route(*s, x, w_router, bias, logits, topk_w, topk_idx,
-                                    reinterpret_cast<float*>(at(ws, w.route + rw.partials)), rw.S,
-                                    stream));
-  if (rc != MOE_OK) return rc;
-  mark(1);
-
-  const PermuteWs pw = permute_ws(*s);
-  const int n_ident = shared ? s->T : 0;
-  rc = hip_status(moe::launch_permute(
-      *s, topk_idx, counts, offsets, r2s, s2r,
-      reinterpret_cast<int32_t*>(at(ws, w.permute + pw.block_counts)),
-      reinterpret_cast<int32_t*>(at(ws, w.permute + pw.block_base)), shared ? ext : nullptr,
-      n_ident, stream));
-  if (rc != MOE_OK) return rc;
-  mark(2);
-
-  // routed experts and the shared expert in one grouped launch per projection:
-  // group 0 = shared expert over rows [0, T) (identity), groups 1..E = routed experts
-  moe::FfnProblem p{};
-  p.x = x;
-  p.T = s->T;
-  p.gather = r2s;
-  p.n_ident = n_ident;
-  p.topk = s->K;
-  p.offsets = shared ? ext : offsets;
-  p.n_groups = s->E + (shared ? 1 : 0);
-  p.rows_max = n_ident + s->T * s->K;
-  p.g_split = shared ? 1 : 0;
-  p.gate_a = s_gate;
-  p.up_a = s_up;
-  p.down_a = s_down;
-  p.gate_b = w_gate;
-  p.up_b = w_up;
-  p.down_b = w_down;
-  p.H = s->H;
-  p.I = s->I;
-  p.limit = s->swiglu_limit;
-  p.h = h;
-  p.y = y;
-  p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
-  rc = hip_status(moe::launch_ffn(p, stream, ev ? ev + 3 : nullptr));
-  if (rc != MOE_OK) return rc;
-
-  const uint16_t* y_routed = y + static_cast<size_t>(n_ident) * s->H;
-  rc = hip_status(moe::launch_combine(*s, y_routed, topk_w, s2r, shared ? y : nullptr, out,
-                                      stream));
-  mark(6);
-  return rc;
+int moe_layer_forward_fp8(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                          const float* bias, const uint8_t* w_gate, const float* w_gate_scale,
+                          const uint8_t* w_up, const float* w_up_scale, const uint8_t* w_down,
+                          const float* w_down_scale, const uint8_t* s_gate,
+                          const float* s_gate_scale, const uint8_t* s_up,
+                          const float* s_up_scale, const uint8_t* s_down,
+                          const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
+                          hipStream_t stream, hipEvent_t const* ev) {
+  return layer_impl(s, x, w_router, bias,
+                    Weights::fp8(w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale),
+                    Weights::fp8(s_gate, s_gate_scale, s_up, s_up_scale, s_down, s_down_scale),
+                    out, ws, ws_bytes, stream, ev);
 }
 
 }  // extern "C"

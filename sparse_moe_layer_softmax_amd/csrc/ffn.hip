@@ -75,8 +75,9 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
-  // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA.
-  const bool tiled = q.rows_max >= 64 * q.n_groups;
+  // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA. FP8
+  // weights always take the weight-streaming kernel (its W8 form), which handles any row count.
+  const bool tiled = !q.w8 && q.rows_max >= 64 * q.n_groups;
   const int bm = tiled ? kTiledRows : kSkinnyRows;
   const int max_tiles = max_tiles_for(q.rows_max, q.n_groups, bm);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, q.offsets, q.n_groups, bm,
@@ -101,11 +102,19 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.W0b = q.gate_b;
   p.W1a = q.up_a;
   p.W1b = q.up_b;
+  p.Q0a = q.qgate_a;
+  p.Q0b = q.qgate_b;
+  p.Q1a = q.qup_a;
+  p.Q1b = q.qup_b;
+  p.S0a = q.sgate_a;
+  p.S0b = q.sgate_b;
+  p.S1a = q.sup_a;
+  p.S1b = q.sup_b;
   p.out = q.h;
   p.N = q.I;
   p.Kd = q.H;
   hipError_t e = tiled ? launch_tiled(kEpiSwiglu, p, max_tiles, stream)
-                       : launch_skinny(true, p, max_tiles, stream);
+                       : launch_skinny(true, q.w8, p, max_tiles, stream);
   if (e != hipSuccess) return e;
   mark(1);
 
@@ -117,10 +126,17 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.W0a = q.down_a;
   p.W0b = q.down_b;
   p.W1a = p.W1b = nullptr;
+  p.Q0a = q.qdown_a;
+  p.Q0b = q.qdown_b;
+  p.Q1a = p.Q1b = nullptr;
+  p.S0a = q.sdown_a;
+  p.S0b = q.sdown_b;
+  p.S1a = p.S1b = nullptr;
   p.out = q.y;
   p.N = q.H;
   p.Kd = q.I;
-  e = tiled ? launch_tiled(kEpiBf16, p, max_tiles, stream) : launch_skinny(false, p, max_tiles, stream);
+  e = tiled ? launch_tiled(kEpiBf16, p, max_tiles, stream)
+            : launch_skinny(false, q.w8, p, max_tiles, stream);
   if (e != hipSuccess) return e;
   mark(2);
   return hipGetLastError();

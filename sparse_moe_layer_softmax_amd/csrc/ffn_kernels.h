@@ -21,6 +21,16 @@ struct GroupedParams {
   const uint16_t* W0b;      // ... for groups >= g_split
   const uint16_t* W1a;      // up weights (gated only)
   const uint16_t* W1b;
+  // FP8 weights (the weight-streaming kernel's W8 form): E4M3 codes laid out like W*, and one fp32
+  // scale per weight row (Sa: [N] for groups < g_split, Sb: [groups, N] for the others)
+  const uint8_t* Q0a;
+  const uint8_t* Q0b;
+  const uint8_t* Q1a;
+  const uint8_t* Q1b;
+  const float* S0a;
+  const float* S0b;
+  const float* S1a;
+  const float* S1b;
   int32_t g_split;
   uint16_t* out;            // [rows, N] bf16
   float* out_f32;           // [rows, N] fp32 (router logits); with k_splits > 1, k_splits such planes
@@ -34,7 +44,8 @@ struct GroupedParams {
 // Weight-streaming kernel for few rows per group (ffn_skinny.hip): row tiles of kSkinnyRows.
 constexpr int kSkinnyRows = 64;
 // gated: gate/up + SwiGLU over N = I columns (64 per workgroup); else down (128 per workgroup).
-hipError_t launch_skinny(bool gated, const GroupedParams& p, int max_tiles, hipStream_t stream);
+// w8: the weights are the FP8 Q*/S* operands.
+hipError_t launch_skinny(bool gated, bool w8, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 // LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
 constexpr int kTiledRows = 320;

@@ -50,6 +50,11 @@ struct FfnProblem {
   int32_t rows_max;           // bound on offsets[G]
   int32_t g_split;            // groups < g_split take the *_a weights, others *_b
   const uint16_t *gate_a, *gate_b, *up_a, *up_b, *down_a, *down_b;
+  // FP8 expert weights (w8): E4M3 codes in place of the bf16 weights above, with one fp32 scale
+  // per weight row (scale_* of the *_a weights is [N], of the *_b weights [G - g_split, N]).
+  bool w8;
+  const uint8_t *qgate_a, *qgate_b, *qup_a, *qup_b, *qdown_a, *qdown_b;
+  const float *sgate_a, *sgate_b, *sup_a, *sup_b, *sdown_a, *sdown_b;
   int32_t H, I;
   float limit;
   uint16_t* h;                // [rows_max, I]

@@ -75,10 +75,64 @@ def margin_ok(probs: np.ndarray, K: int, thresh: float = 1e-4) -> np.ndarray:
     return (srt[:, K - 1] - srt[:, K]) >= thresh
 
 
-def propagated_h_diff(h_gpu_u16, h_orc_u16, wd_u16):
+_E4M3 = None
+
+
+def weight_f64(w) -> np.ndarray:
+    """Float64 values of a weight matrix: bf16 bit patterns, or an oracle.Fp8 (scale * e4m3)."""
+    global _E4M3
+    if isinstance(w, oracle.Fp8):
+        if _E4M3 is None:
+            _E4M3 = np.array([oracle.double_from_e4m3(c) for c in range(256)])
+        return _E4M3[w.q] * w.scale.astype(np.float64)[..., None]
+    return f64(w)
+
+
+def is_fp8(hw: dict) -> bool:
+    return hw["w_gate"].dtype == np.uint8
+
+
+def routed_weights(hw: dict, e: int):
+    """(gate, up, down) of routed expert e in the oracle's form (bf16 arrays or oracle.Fp8)."""
+    names = ("w_gate", "w_up", "w_down")
+    if is_fp8(hw):
+        return tuple(oracle.Fp8(hw[n][e], hw[n + "_scale"][e]) for n in names)
+    return tuple(hw[n][e] for n in names)
+
+
+def shared_weights(hw: dict):
+    names = ("s_gate", "s_up", "s_down")
+    if hw["s_gate"] is None:
+        return None, None, None
+    if is_fp8(hw):
+        return tuple(oracle.Fp8(hw[n], hw[n + "_scale"]) for n in names)
+    return tuple(hw[n] for n in names)
+
+
+def all_routed(hw: dict):
+    names = ("w_gate", "w_up", "w_down")
+    if is_fp8(hw):
+        return tuple(oracle.Fp8(hw[n], hw[n + "_scale"]) for n in names)
+    return tuple(hw[n] for n in names)
+
+
+def ffn_rows(x_rows, w3, limit):
+    """Oracle expert FFN of the given rows: (h, y)."""
+    if isinstance(w3[0], oracle.Fp8):
+        return oracle.expert_ffn_rows_fp8(x_rows, *w3, limit)
+    return oracle.expert_ffn_rows(x_rows, *w3, limit)
+
+
+def down_rows(h, wd):
+    if isinstance(wd, oracle.Fp8):
+        return oracle.down_rows_fp8(h, wd)
+    return oracle.down_rows(h, wd)
+
+
+def propagated_h_diff(h_gpu_u16, h_orc_u16, wd):
     """sum_i |h_gpu - h_oracle|_i * |Wd[c, i]| for each row and output column c."""
     dh = np.abs(f64(h_gpu_u16) - f64(h_orc_u16))
-    return dh @ np.abs(f64(wd_u16)).T
+    return dh @ np.abs(weight_f64(wd)).T
 
 
 def propagated_y_diff(topk_w, slot_to_row, y_gpu_u16, y_orc_u16, ys_gpu_u16=None, ys_orc_u16=None):
@@ -112,8 +166,7 @@ def host(wts: dict) -> dict:
 def run_layer_gpu(wl, dev: dict):
     """moe_layer_forward on the GPU; returns host copies of out and every intermediate."""
     shape = moe.Shape.of(wl)
-    layer = moe.MoELayer(shape, dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
-                         dev["s_gate"], dev["s_up"], dev["s_down"], dev["router_bias"])
+    layer = moe.MoELayer.from_inputs(shape, dev)
     out = layer.forward(dev["x"])
     torch.cuda.synchronize()
     T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
@@ -138,10 +191,11 @@ def run_layer_gpu(wl, dev: dict):
 
 def oracle_same_logits(wl, hw: dict, logits: np.ndarray) -> dict:
     """Oracle steps 2-9 from the given fp32 logits (router projection skipped)."""
-    return oracle.layer_forward(
-        hw["x"], hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], wl.K,
-        bias=hw["router_bias"], sg=hw["s_gate"], su=hw["s_up"], sd=hw["s_down"], scale=wl.scale,
-        limit=wl.limit, capacity=wl.capacity, norm_topk=wl.norm_topk, logits=logits)
+    fwd = oracle.layer_forward_fp8 if is_fp8(hw) else oracle.layer_forward
+    sg, su, sd = shared_weights(hw)
+    return fwd(hw["x"], hw["w_router"], *all_routed(hw), wl.K, bias=hw["router_bias"], sg=sg, su=su,
+               sd=sd, scale=wl.scale, limit=wl.limit, capacity=wl.capacity,
+               norm_topk=wl.norm_topk, logits=logits)
 
 
 def compare_layer(wl, hw: dict, g: dict, r: dict, check_routing_bits: bool = True):
@@ -162,16 +216,17 @@ def compare_layer(wl, hw: dict, g: dict, r: dict, check_routing_bits: bool = Tru
         a, b = int(off[e]), int(off[e + 1])
         if a == b:
             continue
-        wd = hw["w_down"][e]
-        assert_bf16_close(g["y_routed"][a:b], oracle.down_rows(g["h_routed"][a:b], wd),
+        wd = routed_weights(hw, e)[2]
+        assert_bf16_close(g["y_routed"][a:b], down_rows(g["h_routed"][a:b], wd),
                           "y_routed expert %d (chained)" % e)
         assert_bf16_close(g["y_routed"][a:b], r["y_routed"][a:b], "y_routed expert %d (end to end)" % e,
                           extra=propagated_h_diff(g["h_routed"][a:b], r["h_routed"][a:b], wd))
     if wl.n_shared:
         assert_bf16_close(g["h_shared"], r["h_shared"], "h_shared")
-        assert_bf16_close(g["y_shared"], oracle.down_rows(g["h_shared"], hw["s_down"]), "y_shared (chained)")
+        sd = shared_weights(hw)[2]
+        assert_bf16_close(g["y_shared"], down_rows(g["h_shared"], sd), "y_shared (chained)")
         assert_bf16_close(g["y_shared"], r["y_shared"], "y_shared (end to end)",
-                          extra=propagated_h_diff(g["h_shared"], r["h_shared"], hw["s_down"]))
+                          extra=propagated_h_diff(g["h_shared"], r["h_shared"], sd))
     # out, chained: the oracle's combine of the GPU's own rows, bare tolerance
     chained = oracle.combine(g["topk_w"], g["slot_to_row"], g["y_routed"], g["y_shared"])
     assert_bf16_close(g["out"], chained, "out (chained)")

@@ -23,7 +23,7 @@ def m():
 def _declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_header_declares_the_entry_points():
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol(m):
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (moe_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (moe_[a-z0-9_]+)\b", out))
     assert set(_declared_functions()) <= exported
     assert set(m.EXPORTED) == set(_declared_functions())
 
@@ -123,3 +123,22 @@ def test_binding_raises_on_errors(m):
     with pytest.raises(m.MoeError) as ei:
         m.moe_combine(s, 16, 16, 16, None, 16, stream=0)
     assert ei.value.code == m.MOE_ERR_INVALID_ARG
+
+
+def test_fp8_entry_point_errors(m):
+    lib = m.library()
+    sc = ctypes.byref(m.Shape(**HY4).c())
+    ffn8 = lib.moe_expert_ffn_fp8
+    # codes without their scales, or scales without codes
+    assert ffn8(sc, 1, 64, 16, None, None, 16, None, 16, 16, 16, 16, 16, 16, 256, 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    assert ffn8(sc, 1, 64, 16, None, None, 16, 16, 16, 16, None, 16, 16, 16, 256, 1 << 30, None) == m.MOE_ERR_INVALID_ARG
+    assert ffn8(sc, 1, 64, 16, None, None, 16, 16, 16, 16, 16, 16, 16, 16, 256, 64, None) == m.MOE_ERR_WORKSPACE
+    lf8 = lib.moe_layer_forward_fp8
+    w = [16] * 6
+    # shared expert present (n_shared = 1) but one shared scale missing
+    assert lf8(sc, 16, 16, None, *w, 16, 16, 16, None, 16, 16, 16, 256, 1 << 40, None, None) == m.MOE_ERR_INVALID_ARG
+    # no shared expert, yet a shared pointer given
+    s0 = ctypes.byref(m.Shape(**dict(HY4, n_shared=0)).c())
+    assert lf8(s0, 16, 16, None, *w, None, None, None, None, None, 16, 16, 256, 1 << 40, None, None) == m.MOE_ERR_INVALID_ARG
+    assert lf8(sc, 16, 16, None, *w, *w, 16, 256, 1024, None, None) == m.MOE_ERR_WORKSPACE
+    assert lf8(sc, 16, 16, None, *w[:5], None, *w, 16, 256, 1 << 40, None, None) == m.MOE_ERR_INVALID_ARG

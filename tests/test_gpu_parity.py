@@ -53,6 +53,22 @@ SMALL = {
                                            I=256, scale=2.827, seed=23),
 }
 
+# FP8 expert weights (E4M3 codes, per-row fp32 scales); every FFN shape runs the weight-streaming
+# kernel, so these span one and many 64-row tiles per group, ragged tails and the clamp
+SMALL.update({
+    "fp8_tiny_t128_h512_e32_k2": BASE.with_(name="fp8_tiny_t128_h512_e32_k2", fp8=True, seed=40),
+    "fp8_ragged_t130_h256_e256_k8": SMALL["ragged_t130_h256_e256_k8"].with_(
+        name="fp8_ragged_t130_h256_e256_k8", fp8=True, seed=41),
+    "fp8_no_shared_t128": BASE.with_(name="fp8_no_shared_t128", n_shared=0, fp8=True, seed=42),
+    "fp8_multi_tile_t300_e16_k4": SMALL["multi_tile_t300_e16_k4"].with_(
+        name="fp8_multi_tile_t300_e16_k4", fp8=True, seed=43),
+    "fp8_bands_t3000_e4_k2": SMALL["bands_t3000_e4_k2"].with_(name="fp8_bands_t3000_e4_k2",
+                                                              fp8=True, seed=44),
+    "fp8_clamp_forced_t128": BASE.with_(name="fp8_clamp_forced_t128", x_std=30.0, fp8=True, seed=45),
+    "fp8_capacity_drops_t200_e8_k2": SMALL["capacity_drops_t200_e8_k2"].with_(
+        name="fp8_capacity_drops_t200_e8_k2", fp8=True, seed=46),
+})
+
 # routing only: the tiled router with its hidden dimension split 12 ways (2 K-tiles per split)
 ROUTE_ONLY = {
     "tiled_router_t2000_h1536_e256_k8": Workload("tiled_router_t2000_h1536_e256_k8", T=2000, H=1536,
@@ -78,9 +94,9 @@ def test_layer_forward_small(name):
     idx_i, _, probs = oracle.route_from_logits(lo, wl.K, wl.scale, wl.norm_topk, want_probs=True)
     ok = P.margin_ok(probs, wl.K)
     np.testing.assert_array_equal(g["topk_idx"][ok], idx_i[ok])
-    if name == "capacity_drops_t200_e8_k2":
+    if name.endswith("capacity_drops_t200_e8_k2"):
         assert (g["slot_to_row"] < 0).sum() > 0, "this case must drop slots"
-    if name == "clamp_forced_t128":
+    if name.endswith("clamp_forced_t128"):
         hv = P.f64(g["h_routed"][: int(g["offsets"][-1])])
         assert np.abs(hv).max() > 50, "this case must reach the clamp"
 
@@ -191,8 +207,31 @@ def test_moe_permute(T, K, E, C):
         assert rc.max() <= C
 
 
+def _expert_ffn(s, n_groups, rows_max, x, r2s, offsets, w3, h, y, ws):
+    """moe_expert_ffn or moe_expert_ffn_fp8, by the weights' type; w3 = (gate, up, down) as
+    device tensors, each a bf16 tensor or a (uint8 codes, fp32 scales) pair."""
+    if isinstance(w3[0], tuple):
+        (qg, cg), (qu, cu), (qd, cd) = w3
+        moe.moe_expert_ffn_fp8(s, n_groups, rows_max, x, r2s, offsets, qg, cg, qu, cu, qd, cd, h, y, ws)
+    else:
+        moe.moe_expert_ffn(s, n_groups, rows_max, x, r2s, offsets, *w3, h, y, ws)
+
+
+def _dev_weights(dev, names, lead=False):
+    def one(n):
+        t = dev[n][None] if lead else dev[n]
+        if t.dtype == torch.uint8:
+            sc = dev[n + "_scale"]
+            return (t, sc[None] if lead else sc)
+        return t
+    return tuple(one(n) for n in names)
+
+
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8",
-                                  "clamp_forced_t128", "multi_tile_t300_e16_k4", "bands_t3000_e4_k2"])
+                                  "clamp_forced_t128", "multi_tile_t300_e16_k4", "bands_t3000_e4_k2",
+                                  "fp8_tiny_t128_h512_e32_k2", "fp8_ragged_t130_h256_e256_k8",
+                                  "fp8_clamp_forced_t128", "fp8_multi_tile_t300_e16_k4",
+                                  "fp8_bands_t3000_e4_k2"])
 def test_moe_expert_ffn_routed_and_identity(name):
     _require_gpu()
     wl = SMALL[name]
@@ -205,9 +244,9 @@ def test_moe_expert_ffn_routed_and_identity(name):
     TK = wl.T * wl.K
     h = torch.empty((TK, wl.I), dtype=torch.bfloat16, device=DEV)
     y = torch.empty((TK, wl.H), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_ffn(s, wl.E, TK, dev["x"], torch.from_numpy(r2s).to(DEV),
-                       torch.from_numpy(offsets).to(DEV), dev["w_gate"], dev["w_up"], dev["w_down"],
-                       h, y, _ws(moe.moe_expert_ffn_workspace_size(s, wl.E, TK)))
+    _expert_ffn(s, wl.E, TK, dev["x"], torch.from_numpy(r2s).to(DEV),
+                torch.from_numpy(offsets).to(DEV), _dev_weights(dev, ("w_gate", "w_up", "w_down")),
+                h, y, _ws(moe.moe_expert_ffn_workspace_size(s, wl.E, TK)))
     torch.cuda.synchronize()
     R = int(offsets[-1])
     hg, yg = as_u16(h)[:R], as_u16(y)[:R]
@@ -216,28 +255,30 @@ def test_moe_expert_ffn_routed_and_identity(name):
         if a == b:
             continue
         xr = hw["x"][r2s[a:b] // wl.K]
-        rh, ry = oracle.expert_ffn_rows(xr, hw["w_gate"][e], hw["w_up"][e], hw["w_down"][e], wl.limit)
+        w3 = P.routed_weights(hw, e)
+        rh, ry = P.ffn_rows(xr, w3, wl.limit)
         P.assert_bf16_close(hg[a:b], rh, "h expert %d" % e)
-        P.assert_bf16_close(yg[a:b], oracle.down_rows(hg[a:b], hw["w_down"][e]), "y expert %d (chained)" % e)
+        P.assert_bf16_close(yg[a:b], P.down_rows(hg[a:b], w3[2]), "y expert %d (chained)" % e)
         P.assert_bf16_close(yg[a:b], ry, "y expert %d (end to end)" % e,
-                            extra=P.propagated_h_diff(hg[a:b], rh, hw["w_down"][e]))
+                            extra=P.propagated_h_diff(hg[a:b], rh, w3[2]))
     # identity rows, one group, no offsets: the shared-expert form, once with h kept in the
     # workspace and once with h returned; both runs must agree bit for bit
-    sg, su, sd = dev["s_gate"][None], dev["s_up"][None], dev["s_down"][None]
+    sw = _dev_weights(dev, ("s_gate", "s_up", "s_down"), lead=True)
     ys = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
-    moe.moe_expert_ffn(s, 1, wl.T, dev["x"], None, None, sg, su, sd, None, ys,
-                       _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
+    _expert_ffn(s, 1, wl.T, dev["x"], None, None, sw, None, ys,
+                _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
     hs = torch.empty((wl.T, wl.I), dtype=torch.bfloat16, device=DEV)
     ys2 = torch.empty_like(ys)
-    moe.moe_expert_ffn(s, 1, wl.T, dev["x"], None, None, sg, su, sd, hs, ys2,
-                       _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
+    _expert_ffn(s, 1, wl.T, dev["x"], None, None, sw, hs, ys2,
+                _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
     torch.cuda.synchronize()
     assert torch.equal(ys, ys2)
-    rhs, rys = oracle.expert_ffn_rows(hw["x"], hw["s_gate"], hw["s_up"], hw["s_down"], wl.limit)
+    s3 = P.shared_weights(hw)
+    rhs, rys = P.ffn_rows(hw["x"], s3, wl.limit)
     P.assert_bf16_close(as_u16(hs), rhs, "identity-row h")
-    P.assert_bf16_close(as_u16(ys), oracle.down_rows(as_u16(hs), hw["s_down"]), "identity-row y (chained)")
+    P.assert_bf16_close(as_u16(ys), P.down_rows(as_u16(hs), s3[2]), "identity-row y (chained)")
     P.assert_bf16_close(as_u16(ys), rys, "identity-row y (end to end)",
-                        extra=P.propagated_h_diff(as_u16(hs), rhs, hw["s_down"]))
+                        extra=P.propagated_h_diff(as_u16(hs), rhs, s3[2]))
 
 
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "capacity_drops_t200_e8_k2", "no_shared_t128"])
@@ -260,7 +301,8 @@ def test_moe_combine(name):
 
 
 # ----------------------------------------------------------------------------- full sizes, sampled
-FULL = ["hy4_decode_t64", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2", "hy4_skew_t65536"]
+FULL = ["hy4_decode_t64", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2", "hy4_skew_t65536",
+        "hy4_decode_t64_fp8"]
 
 
 @pytest.mark.timeout(600)
@@ -271,8 +313,7 @@ def test_full_size_sampled(name):
     print("\n[full-size] %s T=%d H=%d E=%d K=%d I=%d" % (name, wl.T, wl.H, wl.E, wl.K, wl.I), flush=True)
     dev = generate(wl, DEV)
     shape = moe.Shape.of(wl)
-    layer = moe.MoELayer(shape, dev["w_router"], dev["w_gate"], dev["w_up"], dev["w_down"],
-                         dev["s_gate"], dev["s_up"], dev["s_down"], dev["router_bias"])
+    layer = moe.MoELayer.from_inputs(shape, dev)
     out = layer.forward(dev["x"])
     torch.cuda.synchronize()
     T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
@@ -321,9 +362,16 @@ def test_full_size_sampled(name):
 
     cache = {}
 
+    def host_w(n, e=None):
+        t = dev[n] if e is None else dev[n][e]
+        if t.dtype == torch.uint8:
+            sc = dev[n + "_scale"] if e is None else dev[n + "_scale"][e]
+            return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
+        return as_u16(t)
+
     def expert(e):
         if e not in cache:
-            cache[e] = (as_u16(dev["w_gate"][e]), as_u16(dev["w_up"][e]), as_u16(dev["w_down"][e]))
+            cache[e] = tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down"))
         return cache[e]
 
     for i, t in enumerate(toks):
@@ -335,22 +383,23 @@ def test_full_size_sampled(name):
         ry = np.zeros((max(R, 1), H), np.uint16)
         for n, j in enumerate(kept):
             wg_, wu_, wd_ = expert(int(g_idx[t, j]))
-            rh1, ry1 = oracle.expert_ffn_rows(x_s[i:i + 1], wg_, wu_, wd_, wl.limit)
+            rh1, ry1 = P.ffn_rows(x_s[i:i + 1], (wg_, wu_, wd_), wl.limit)
             P.assert_bf16_close(gh[n:n + 1], rh1, "h token %d slot %d" % (t, j))
-            P.assert_bf16_close(gy[n:n + 1], oracle.down_rows(gh[n:n + 1], wd_),
+            P.assert_bf16_close(gy[n:n + 1], P.down_rows(gh[n:n + 1], wd_),
                                 "y token %d slot %d (chained)" % (t, j))
             P.assert_bf16_close(gy[n:n + 1], ry1, "y token %d slot %d (end to end)" % (t, j),
                                 extra=P.propagated_h_diff(gh[n:n + 1], rh1, wd_))
             ry[rows[j]] = ry1[0]
         ys_r = None
         if wl.n_shared:
-            sd_ = as_u16(dev["s_down"])
-            rhs, ys_r = oracle.expert_ffn_rows(x_s[i:i + 1], as_u16(dev["s_gate"]), as_u16(dev["s_up"]),
-                                               sd_, wl.limit)
+            if "shared" not in cache:
+                cache["shared"] = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down"))
+            sd_ = cache["shared"][2]
+            rhs, ys_r = P.ffn_rows(x_s[i:i + 1], cache["shared"], wl.limit)
             ghs = as_u16(h_all[int(t):int(t) + 1])
             gys = as_u16(y_all[int(t):int(t) + 1])
             P.assert_bf16_close(ghs, rhs, "h_shared token %d" % t)
-            P.assert_bf16_close(gys, oracle.down_rows(ghs, sd_), "y_shared token %d (chained)" % t)
+            P.assert_bf16_close(gys, P.down_rows(ghs, sd_), "y_shared token %d (chained)" % t)
             P.assert_bf16_close(gys, ys_r, "y_shared token %d (end to end)" % t,
                                 extra=P.propagated_h_diff(ghs, rhs, sd_))
         g_out = as_u16(out[int(t):int(t) + 1])
