@@ -7,8 +7,10 @@
 // Row tiles of up to 64 rows (MFMA 16x16x32 in 16-row sub-blocks; only the occupied sub-blocks
 // are computed). Each wavefront owns 16 output columns of the gate AND the up projection (so the
 // SwiGLU epilogue pairs them in registers), or 32 columns of the down projection. Weight
-// fragments are loaded straight from HBM with 16-byte loads in MFMA operand order: at a few rows
-// per expert (decode) the layer is a weight stream and this kernel runs at HBM speed.
+// fragments come straight from HBM into registers, each load instruction reading whole 128-byte
+// lines of 8 weight rows non-temporally, and a DPP row rotate moves every chunk to the lane whose
+// MFMA operand holds it: at a few rows per expert (decode) the layer is a weight stream and this
+// kernel runs at HBM speed.
 //
 // W8 form (FP8 expert weights, E4M3 codes with one fp32 scale per weight row): each lane loads
 // 16 codes at a time, converts them exactly to bf16 in registers (every E4M3 value is a bf16
@@ -33,8 +35,38 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
-__device__ __forceinline__ u32x4_t ld16b(const uint8_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
+// Weight loads bypass cache retention: each weight line is read once per launch.
+constexpr bool kWeightNT = true;
+
+__device__ __forceinline__ u32x4_t ldw(const uint8_t* p) {
+  const u32x4_t* q = reinterpret_cast<const u32x4_t*>(p);
+  if (kWeightNT) return __builtin_nontemporal_load(q);
+  return *q;
+}
+
+// One 128-byte line of each of a fragment's 16 weight rows, as two loads: L0 (this lane's chunk
+// in fragment rows 0-7) and L1 (rows 8-15, hoff bytes on).
+struct LineRaw {
+  u32x4_t l0, l1;
+};
+
+__device__ __forceinline__ LineRaw load_line(const uint8_t* p, size_t hoff) {
+  return LineRaw{ldw(p), ldw(p + hoff)};
+}
+
+// Hands every lane r (= lane % 16) its own row's chunks G (f0) and G + 4 (f1). Lanes r < 8 of a
+// 16-lane row hold their chunk G in L0 and receive chunk G + 4 from lane r + 8's L0; lanes r >= 8
+// hold chunk G + 4 in L1 and receive chunk G from lane r - 8's L1. row_ror:8 (DPP control 0x128)
+// pairs r with r + 8 mod 16; the bank mask picks the receiving half (banks 0-1: r < 8, banks 2-3:
+// r >= 8).
+__device__ __forceinline__ void exchange_line(const LineRaw& w, u32x4_t& f0, u32x4_t& f1) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    f0[d] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(w.l0[d]), static_cast<int>(w.l1[d]), 0x128, 0xF, 0xC, false));
+    f1[d] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
+        static_cast<int>(w.l1[d]), static_cast<int>(w.l0[d]), 0x128, 0xF, 0x3, false));
+  }
 }
 
 template <bool GATED, int NS, bool W8>
@@ -44,10 +76,10 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
   const int lr = lane & 15;
   const int lk = W8 ? (lane >> 4) * 16 : (lane >> 4) * 8;  // this lane's first K element
   const int Kd = p.Kd;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   const uint16_t* ap[NS];
   bool av[NS];
+  u32x4_t am[NS];  // all ones for rows of the tile, zero past it
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int r = r0 + 16 * s + lr;
@@ -59,29 +91,40 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
       src = 0;
     }
     ap[s] = p.A + static_cast<size_t>(src) * Kd + lk;
+    const uint32_t m = av[s] ? ~0u : 0u;
+    am[s] = u32x4_t{m, m, m, m};
   }
 
-  const size_t wst = static_cast<size_t>(p.N) * Kd;
-  // weight rows of this lane's two B fragments (gate and up, or down columns col0 and col0 + 16)
-  const size_t row0 = static_cast<size_t>(col0 + lr) * Kd + lk;
-  const size_t row1 = static_cast<size_t>(GATED ? col0 + lr : col0 + 16 + lr) * Kd + lk;
-  const uint16_t* b0 = nullptr;
-  const uint16_t* b1 = nullptr;
-  const uint8_t* q0 = nullptr;
-  const uint8_t* q1 = nullptr;
+  // Weight fragments. Each 16-row B fragment is read in 128-byte lines: load L0 covers rows 0-7
+  // of the fragment, load L1 rows 8-15, every row with one whole line (lanes r and r + 8 of each
+  // 16-lane row take its 16-byte chunks G and G + 4, G = lane / 16). A rotate by 8 inside each
+  // 16-lane row then hands every lane r its own row's chunks G and G + 4, which is what MFMA
+  // operands u (even) and u + 1 need. Whole-line loads let the weights stream non-temporally.
+  const int lo8 = lr & 7;
+  const size_t rowb = W8 ? static_cast<size_t>(Kd) : 2 * static_cast<size_t>(Kd);  // row bytes
+  const size_t wst = static_cast<size_t>(p.N) * rowb;                            // matrix bytes
+  const size_t cb = 16 * ((lane >> 4) + 4 * (lr >> 3));
+  const uint8_t* M0;
+  const uint8_t* M1;
   if (W8) {
-    const uint8_t* Q0 = g < p.g_split ? p.Q0a + g * wst : p.Q0b + (g - p.g_split) * wst;
-    const uint8_t* Q1 = Q0;
-    if (GATED) Q1 = g < p.g_split ? p.Q1a + g * wst : p.Q1b + (g - p.g_split) * wst;
-    q0 = Q0 + row0;
-    q1 = Q1 + row1;
+    M0 = g < p.g_split ? p.Q0a + g * wst : p.Q0b + (g - p.g_split) * wst;
+    M1 = GATED ? (g < p.g_split ? p.Q1a + g * wst : p.Q1b + (g - p.g_split) * wst) : M0;
   } else {
-    const uint16_t* W0 = g < p.g_split ? p.W0a + g * wst : p.W0b + (g - p.g_split) * wst;
-    const uint16_t* W1 = W0;
-    if (GATED) W1 = g < p.g_split ? p.W1a + g * wst : p.W1b + (g - p.g_split) * wst;
-    b0 = W0 + row0;
-    b1 = W1 + row1;
+    const uint8_t* W0a = reinterpret_cast<const uint8_t*>(p.W0a);
+    const uint8_t* W0b = reinterpret_cast<const uint8_t*>(p.W0b);
+    M0 = g < p.g_split ? W0a + g * wst : W0b + (g - p.g_split) * wst;
+    M1 = M0;
+    if (GATED) {
+      const uint8_t* W1a = reinterpret_cast<const uint8_t*>(p.W1a);
+      const uint8_t* W1b = reinterpret_cast<const uint8_t*>(p.W1b);
+      M1 = g < p.g_split ? W1a + g * wst : W1b + (g - p.g_split) * wst;
+    }
   }
+  // this lane's L0 address in the fragment of gate (or down columns col0..) and of up (or down
+  // columns col0 + 16..); L1 is 8 rows further
+  const uint8_t* w0 = M0 + static_cast<size_t>(col0 + lo8) * rowb + cb;
+  const uint8_t* w1 = M1 + static_cast<size_t>(GATED ? col0 + lo8 : col0 + 16 + lo8) * rowb + cb;
+  const size_t hoff = 8 * rowb;
 
   f32x4_t acc0[NS], acc1[NS];
 #pragma unroll
@@ -90,34 +133,59 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
     acc1[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
   constexpr int U = 4;
-  for (int k = 0; k < Kd; k += 32 * U) {
-    u32x4_t bb0[U], bb1[U], aa[NS][U];
-    if (W8) {
-      const u32x4_t c0 = ld16b(q0 + k), c1 = ld16b(q0 + k + 64);
-      const u32x4_t d0 = ld16b(q1 + k), d1 = ld16b(q1 + k + 64);
-      bb0[0] = e4m3x8_to_bf16(c0[0], c0[1]);
-      bb0[1] = e4m3x8_to_bf16(c0[2], c0[3]);
-      bb0[2] = e4m3x8_to_bf16(c1[0], c1[1]);
-      bb0[3] = e4m3x8_to_bf16(c1[2], c1[3]);
-      bb1[0] = e4m3x8_to_bf16(d0[0], d0[1]);
-      bb1[1] = e4m3x8_to_bf16(d0[2], d0[3]);
-      bb1[2] = e4m3x8_to_bf16(d1[0], d1[1]);
-      bb1[3] = e4m3x8_to_bf16(d1[2], d1[3]);
-    } else {
+  // one iteration covers 128 K elements: two 128-byte lines of each bf16 weight row, one line of
+  // each FP8 row
+  // The next iteration's weight lines are loaded before this iteration's MFMAs (the last
+  // iteration reloads its own lines, which stay in bounds and go unused).
+  constexpr int LN = W8 ? 1 : 2;
+  constexpr size_t KB = W8 ? 128 : 256;  // weight bytes per row and iteration
+  LineRaw r0w[LN], r1w[LN];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        bb0[u] = ld16(b0 + k + 32 * u);
-        bb1[u] = ld16(b1 + k + 32 * u);
-      }
+  for (int ln = 0; ln < LN; ++ln) {
+    r0w[ln] = load_line(w0 + 128 * ln, hoff);
+    r1w[ln] = load_line(w1 + 128 * ln, hoff);
+  }
+  for (int k = 0; k < Kd; k += 128) {
+    const size_t kb = W8 ? static_cast<size_t>(k) : 2 * static_cast<size_t>(k);
+    const size_t kn = k + 128 < Kd ? kb + KB : kb;
+    LineRaw n0w[LN], n1w[LN];
+#pragma unroll
+    for (int ln = 0; ln < LN; ++ln) {
+      n0w[ln] = load_line(w0 + kn + 128 * ln, hoff);
+      n1w[ln] = load_line(w1 + kn + 128 * ln, hoff);
     }
-    // activations at the same K elements as the weight operands of MFMA u
+    // activations at the same K elements as the weight operands of MFMA u; rows past the tile
+    // read a valid row and are masked to zero, so the loads need no branch
+    u32x4_t aa[NS][U];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int ko = W8 ? 64 * (u >> 1) + 8 * (u & 1) : 32 * u;
-        aa[s][u] = av[s] ? ld16(ap[s] + k + ko) : zero;
+        const u32x4_t t = ld16(ap[s] + k + ko);
+        aa[s][u] = t & am[s];
       }
+    u32x4_t f0[2 * LN], f1[2 * LN];  // [2 * line + half]: chunk G (half 0) or G + 4 (half 1)
+#pragma unroll
+    for (int ln = 0; ln < LN; ++ln) {
+      exchange_line(r0w[ln], f0[2 * ln], f0[2 * ln + 1]);
+      exchange_line(r1w[ln], f1[2 * ln], f1[2 * ln + 1]);
+      r0w[ln] = n0w[ln];
+      r1w[ln] = n1w[ln];
+    }
+    u32x4_t bb0[U], bb1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (W8) {  // MFMA u takes codes 8(u%2)..+8 of chunk half u/2
+        const u32x4_t& c = f0[u >> 1];
+        const u32x4_t& d = f1[u >> 1];
+        bb0[u] = e4m3x8_to_bf16(c[2 * (u & 1)], c[2 * (u & 1) + 1]);
+        bb1[u] = e4m3x8_to_bf16(d[2 * (u & 1)], d[2 * (u & 1) + 1]);
+      } else {
+        bb0[u] = f0[u];
+        bb1[u] = f1[u];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
