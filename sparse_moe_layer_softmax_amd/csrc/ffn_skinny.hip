@@ -77,6 +77,14 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
   const int lk = W8 ? (lane >> 4) * 16 : (lane >> 4) * 8;  // this lane's first K element
   const int Kd = p.Kd;
 
+  // activation row of tile row r (identity rows first, then gathered tokens); -1 if malformed
+  auto source = [&](int r) {
+    const int src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
+    return static_cast<unsigned>(src) < static_cast<unsigned>(p.a_rows) ? src : -1;
+  };
+  // lanes of rows past the tile load the tile's first row (a segment the same instruction
+  // already reads) and mask it to zero, rather than a fixed row that every workgroup would hit
+  const int src0 = max(source(r0), 0);
   const uint16_t* ap[NS];
   bool av[NS];
   u32x4_t am[NS];  // all ones for rows of the tile, zero past it
@@ -84,11 +92,13 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
   for (int s = 0; s < NS; ++s) {
     const int r = r0 + 16 * s + lr;
     av[s] = r < r1;
-    int src = 0;
-    if (av[s]) src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
-    if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) {  // malformed gather
-      av[s] = false;
-      src = 0;
+    int src = src0;
+    if (av[s]) {
+      src = source(r);
+      if (src < 0) {  // malformed gather
+        av[s] = false;
+        src = src0;
+      }
     }
     ap[s] = p.A + static_cast<size_t>(src) * Kd + lk;
     const uint32_t m = av[s] ? ~0u : 0u;
