@@ -81,7 +81,7 @@ def recorded_traffic(workload, kernel):
         return None
     for line in open(path):
         f = line.split()
-        if len(f) != 6 or line.startswith("#") or f[0] != workload or f[1] != kernel:
+        if len(f) != 6 or line.startswith("#") or f[0] != workload or f[1] != kernel.replace(" ", ""):
             continue
         src = os.path.join(root, f[2])
         if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != f[3]:
@@ -90,10 +90,11 @@ def recorded_traffic(workload, kernel):
     return None
 
 
-def cpu_baseline(wl, dev, n_tok):
+def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
     """The CPU oracle, timed on a bounded sample of the workload's tokens (every step of the
-    layer for those tokens: router logits, routing, their routed and shared expert FFNs, combine).
-    Weights are copied to host memory before the clock starts."""
+    layer for those tokens: router logits, routing, their routed and shared expert FFNs, combine),
+    repeated until at least min_seconds have passed. Weights are copied to host memory before the
+    clock starts."""
     import numpy as np
     import torch
 
@@ -119,21 +120,27 @@ def cpu_baseline(wl, dev, n_tok):
     ffn = oracle.expert_ffn_rows_fp8 if wl.fp8 else oracle.expert_ffn_rows
     W = {e: tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down")) for e in experts}
     SW = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
+    reps = 0
     t0 = time.perf_counter()
-    lg = oracle.router_logits(x, wr, bias)
-    idx, w = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
-    counts, offsets, r2s, s2r = oracle.dispatch(idx, wl.E, 0)
-    y = np.zeros((len(toks) * wl.K, wl.H), np.uint16)
-    for e in experts:  # expert-major, as the oracle's layer does
-        a, b = offsets[e], offsets[e + 1]
-        _, y[a:b] = ffn(x[r2s[a:b] // wl.K], *W[e], wl.limit)
-    ys = ffn(x, *SW, wl.limit)[1] if SW else None
-    oracle.combine(w, s2r, y, ys)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(toks) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "seconds": round(dt, 3),
-            "sample": "%d of the workload's %d tokens (all steps of the layer for them; %d distinct "
-                      "routed experts + shared), fp64 C++ oracle" % (len(toks), wl.T, len(experts))}
+    while True:
+        lg = oracle.router_logits(x, wr, bias)
+        idx, w = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
+        counts, offsets, r2s, s2r = oracle.dispatch(idx, wl.E, 0)
+        y = np.zeros((len(toks) * wl.K, wl.H), np.uint16)
+        for e in experts:  # expert-major, as the oracle's layer does
+            a, b = offsets[e], offsets[e + 1]
+            _, y[a:b] = ffn(x[r2s[a:b] // wl.K], *W[e], wl.limit)
+        ys = ffn(x, *SW, wl.limit)[1] if SW else None
+        oracle.combine(w, s2r, y, ys)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    return {"value": round(reps * len(toks) / dt, 3), "unit": "tokens/s",
+            "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d of the workload's %d tokens, %d pass(es): all steps of the layer for them "
+                      "(%d distinct routed experts + shared), fp64 C++ oracle"
+                      % (len(toks), wl.T, reps, len(experts))}
 
 
 def copy_calibration():
@@ -242,7 +249,7 @@ def main():
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }
     if not args.no_cpu_baseline:
-        n_tok = args.cpu_tokens or (16 if wl.T <= 64 else 8)
+        n_tok = args.cpu_tokens or min(wl.T, 64)
         res["cpu_baseline"] = cpu_baseline(wl, dev, n_tok)
     else:
         res["cpu_baseline"] = None

@@ -8,7 +8,8 @@ Shapes and distributions follow the Hy4 preview configuration (hidden 6144, 256 
 top-8, one shared expert, expert intermediate 2048, routed_scaling_factor 2.827,
 swiglu_limit 10, initializer_range 0.006, bf16) described in the Hy4 config.json walkthrough
 (lshu.cn, section "MoE routed experts: 256 choose 8" and "length, vocabulary and training
-details"), and the Hy3 router sketch's top-2 / 32-expert / hidden-7168 / capacity_factor 1.25
+details"; its architecture overview gives the first layer's dense FFN intermediate size 18432),
+and the Hy3 router sketch's top-2 / 32-expert / hidden-7168 / capacity_factor 1.25
 variant (Hy3 deep-dive, `SparseMoERouter`).
 
 Recipe: every tensor is drawn as float32 N(0, std^2) from its own torch generator seeded with
@@ -79,6 +80,11 @@ WORKLOADS = {
     "hy4_skew_t65536": Workload(
         "hy4_skew_t65536", T=65536, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
         w_std=0.006, router_std=0.006, zipf=1.2, seed=4),
+    # the dense FFN of the stack's first layer (intermediate 18432) as the E = 1, k = 1 layer with
+    # no shared expert, over a prefill batch
+    "dense_ffn_t8192_h6144_i18432": Workload(
+        "dense_ffn_t8192_h6144_i18432", T=8192, H=6144, E=1, K=1, I=18432, n_shared=0, scale=1.0,
+        limit=10.0, w_std=0.006, router_std=0.006, seed=6),
     # the decode batch with FP8 expert weights (the pages' deployment checkpoint is FP8)
     "hy4_decode_t64_fp8": Workload(
         "hy4_decode_t64_fp8", T=64, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,

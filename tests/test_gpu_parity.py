@@ -48,6 +48,9 @@ SMALL = {
     # several 8-tile bands in one group (about 1500 rows per expert), ragged last tiles
     "bands_t3000_e4_k2": Workload("bands_t3000_e4_k2", T=3000, H=256, E=4, K=2, I=256, scale=2.827,
                                   seed=22),
+    # a dense SwiGLU FFN (E = 1, k = 1, no shared expert) with a wide intermediate on the tiled path
+    "dense_ffn_t700_h512_i2304": Workload("dense_ffn_t700_h512_i2304", T=700, H=512, E=1, K=1,
+                                          I=2304, n_shared=0, seed=25),
     # router on the tiled MFMA path (T >= 1024, E = 256), ragged T
     "tiled_router_t1030_e256_k8": Workload("tiled_router_t1030_e256_k8", T=1030, H=256, E=256, K=8,
                                            I=256, scale=2.827, seed=23),
@@ -302,7 +305,7 @@ def test_moe_combine(name):
 
 # ----------------------------------------------------------------------------- full sizes, sampled
 FULL = ["hy4_decode_t64", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2", "hy4_skew_t65536",
-        "hy4_decode_t64_fp8"]
+        "hy4_decode_t64_fp8", "dense_ffn_t8192_h6144_i18432"]
 
 
 @pytest.mark.timeout(600)
