@@ -65,6 +65,7 @@ def _declare(L):
     L.oracle_down_rows_fp8.argtypes = [_I, _I, _I] + [_P] * 4
     L.oracle_layer_forward_fp8.argtypes = [_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 15 + [_I] + [_P] * 12
     L.oracle_layer_dense_fp8.argtypes = [_I, _I, _I, _I, _I, _D] + [_P] * 17
+    L.oracle_router_train_stats.argtypes = [_I, _I, _I, _P, _P, _D, _P, _P, _P, _P, _P]
     L.oracle_num_threads.restype = _I
 
 
@@ -325,6 +326,36 @@ def layer_dense_fp8(x, wg: Fp8, wu: Fp8, wd: Fp8, topk_idx, topk_w, slot_to_row,
     lib().oracle_layer_dense_fp8(T, H, E, K, I, float(limit), _ptr(x), *_fp8_ptrs(wg, wu, wd, sg, su, sd),
                                  _ptr(topk_idx), _ptr(topk_w), _ptr(slot_to_row), _ptr(out))
     return out
+
+
+# ---------------------------------------------------------------------------- training side
+def router_logits_noisy(x, wr, bias=None, noise=None):
+    """Router logits with the training noise added to the scores before the softmax (Hy4
+    deep-dive MoERouter, training branch). The noise is drawn by the caller (the page draws
+    N(0, 0.01^2) per score) and passed in; logits and noise are added in float64 and rounded to
+    float32."""
+    lg = router_logits(x, wr, bias)
+    if noise is None:
+        return lg
+    return (lg.astype(np.float64) + _f32(noise).astype(np.float64)).astype(np.float32)
+
+
+def router_train_stats(logits, topk_idx, decay=0.9, ema_counts=None, ema_tokens=None):
+    """Training-side router statistics (Hy3 deep-dive SparseMoERouter training branch): returns
+    dict(prob_mean [E], load_frac [E], aux_loss, ema_counts [E] or None, ema_tokens or None),
+    all float64; ema_* are the updated averages when initial values are given."""
+    logits, topk_idx = _f32(logits), _i32(topk_idx)
+    T, E = logits.shape
+    K = topk_idx.shape[1]
+    pm = np.zeros(E)
+    lf = np.zeros(E)
+    aux = np.zeros(1)
+    ec = None if ema_counts is None else np.ascontiguousarray(np.asarray(ema_counts, np.float64)).copy()
+    et = None if ema_tokens is None else np.array([float(ema_tokens)])
+    lib().oracle_router_train_stats(T, E, K, _ptr(logits), _ptr(topk_idx), float(decay), _ptr(pm),
+                                    _ptr(lf), _ptr(aux), _ptr(ec), _ptr(et))
+    return dict(prob_mean=pm, load_frac=lf, aux_loss=float(aux[0]), ema_counts=ec,
+                ema_tokens=None if et is None else float(et[0]))
 
 
 def bf16_to_f64(a: np.ndarray) -> np.ndarray:

@@ -240,6 +240,44 @@ uint16_t oracle_bf16_from_double(double v) {
 
 double oracle_double_from_bf16(uint16_t b) { return bf(b); }
 
+// Training-side router statistics, following the training branch of the Hy3 deep-dive's
+// SparseMoERouter: P is the token mean of the softmax probabilities, f the share of the T*K
+// selections that went to each expert (counted from the top-k indices, before any capacity
+// limit), the load-balancing loss is E * sum_e P[e] f[e], and the expert-count and token-count
+// buffers move as exponential moving averages with the given decay (0.9 on the page).
+void oracle_router_train_stats(int T, int E, int K, const float* logits, const int32_t* topk_idx,
+                               double decay, double* prob_mean, double* load_frac, double* aux,
+                               double* ema_counts, double* ema_tokens) {
+  std::vector<double> p(static_cast<size_t>(T) * E);
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + static_cast<size_t>(t) * E;
+    double m = l[0];
+    for (int e = 1; e < E; ++e) m = l[e] > m ? l[e] : m;
+    double z = 0.0;
+    double* pt = p.data() + static_cast<size_t>(t) * E;
+    for (int e = 0; e < E; ++e) {
+      pt[e] = std::exp(static_cast<double>(l[e]) - m);
+      z += pt[e];
+    }
+    for (int e = 0; e < E; ++e) pt[e] /= z;
+  }
+  std::vector<double> counts(E, 0.0);
+  for (size_t i = 0; i < static_cast<size_t>(T) * K; ++i) counts[topk_idx[i]] += 1.0;
+  double sum = 0.0;
+  for (int e = 0; e < E; ++e) {
+    double pe = 0.0;
+    for (int t = 0; t < T; ++t) pe += p[static_cast<size_t>(t) * E + e];
+    prob_mean[e] = pe / T;
+    load_frac[e] = counts[e] / (static_cast<double>(T) * K);
+    sum += prob_mean[e] * load_frac[e];
+  }
+  *aux = sum * E;
+  if (ema_counts)
+    for (int e = 0; e < E; ++e) ema_counts[e] = ema_counts[e] * decay + counts[e] * (1.0 - decay);
+  if (ema_tokens) *ema_tokens = *ema_tokens * decay + static_cast<double>(T) * (1.0 - decay);
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -147,6 +147,18 @@ void oracle_layer_dense_fp8(int T, int H, int E, int K, int I, double limit, con
                             const int32_t* topk_idx, const float* topk_w,
                             const int32_t* slot_to_row, uint16_t* out);
 
+/* Training-side router statistics (Hy3 deep-dive, SparseMoERouter training branch and its
+ * load-balancing loss): from fp32 logits [T,E] (bias and noise already added) and the top-k
+ * indices [T,K]:
+ *   prob_mean[e] = (1/T) sum_t softmax(logits[t])[e]
+ *   load_frac[e] = #{(t,j): topk_idx[t,j] = e} / (T*K)        (before any capacity limit)
+ *   aux          = E * sum_e prob_mean[e] * load_frac[e]
+ *   ema_counts[e] = decay*ema_counts[e] + (1-decay)*count[e]  (in/out, may be NULL)
+ *   ema_tokens    = decay*ema_tokens + (1-decay)*T            (in/out, may be NULL)       */
+void oracle_router_train_stats(int T, int E, int K, const float* logits, const int32_t* topk_idx,
+                               double decay, double* prob_mean, double* load_frac, double* aux,
+                               double* ema_counts, double* ema_tokens);
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int oracle_num_threads(void);
 
