@@ -91,6 +91,29 @@ int moe_route(const moe_shape* shape, const uint16_t* x, const uint16_t* w_route
               const float* bias, float* logits, float* topk_w, int32_t* topk_idx, void* ws,
               size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- router, training: moe_route_train
+ * moe_route in training mode, plus the router statistics of the training branch.
+ *   noise [T,E] fp32 or NULL   added to the logits before the softmax and the top-k (Hy4
+ *                               deep-dive `MoERouter`: N(0, 0.01^2) scores noise in training;
+ *                               the caller draws it, so runs are reproducible)
+ *   logits, topk_w, topk_idx    as in moe_route (logits include the noise; NULL logits are kept
+ *                               in the workspace)
+ * Statistics (Hy3 deep-dive `SparseMoERouter`, training branch and load-balancing loss):
+ *   prob_mean [E] fp32 out      P_e = (1/T) sum_t softmax(logits[t])[e]
+ *   load_frac [E] fp32 out      f_e = #{(t,j): topk_idx[t,j] = e} / (T*K), before any capacity
+ *   aux_loss  [1] fp32 out      E * sum_e P_e f_e
+ *   ema_counts [E] fp32 in/out or NULL   ema_decay * ema + (1 - ema_decay) * count_e
+ *   ema_tokens [1] fp32 in/out or NULL   ema_decay * ema + (1 - ema_decay) * T
+ *   ema_decay                   in [0, 1] (0.9 on the page), else MOE_ERR_INVALID_ARG
+ * Reductions run in a fixed order: the same inputs give the same bits on every run.
+ * ws: moe_route_train_workspace_size(shape) bytes, 256-byte aligned.                          */
+size_t moe_route_train_workspace_size(const moe_shape* shape);
+int moe_route_train(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                    const float* bias, const float* noise, float* logits, float* topk_w,
+                    int32_t* topk_idx, float* prob_mean, float* load_frac, float* aux_loss,
+                    float* ema_counts, float* ema_tokens, float ema_decay, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- dispatch: moe_permute
  * Token-to-expert dispatch (Hy3 explainer 2.1: the rows of each expert gathered together).
  * A slot is (t, j), id s = t*K + j. Rows are grouped by expert, ascending expert id; inside an

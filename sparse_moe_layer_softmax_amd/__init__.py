@@ -27,6 +27,7 @@ EXPORTED = (
     "moe_permute", "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "moe_layer_forward",
     "moe_layer_forward_profiled", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
+    "moe_route_train_workspace_size", "moe_route_train",
 )
 MOE_LAYER_PHASE_EVENTS = 7
 
@@ -94,6 +95,8 @@ def _load():
         "moe_layer_forward": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P], ctypes.c_int),
         "moe_layer_forward_profiled": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P, P], ctypes.c_int),
         "moe_expert_ffn_fp8": ([sp, I32, I32] + [P] * 12 + [S, P], ctypes.c_int),
+        "moe_route_train_workspace_size": ([sp], S),
+        "moe_route_train": ([sp] + [P] * 12 + [ctypes.c_float, P, S, P], ctypes.c_int),
         "moe_layer_forward_fp8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
@@ -173,6 +176,20 @@ def moe_route(shape: Shape, x, w_router, bias, logits, topk_w, topk_idx, ws, str
     _check(library().moe_route(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(logits),
                          _p(topk_w), _p(topk_idx), _p(ws), ws.numel() if ws is not None else 0,
                          _stream(stream)), "moe_route")
+
+
+def moe_route_train_workspace_size(shape: Shape) -> int:
+    return library().moe_route_train_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_route_train(shape: Shape, x, w_router, bias, noise, logits, topk_w, topk_idx, prob_mean,
+                    load_frac, aux_loss, ema_counts, ema_tokens, ws, ema_decay=0.9, stream=None):
+    """moe_route in training mode (score noise) plus P, f, the load-balancing loss and the EMAs."""
+    _check(library().moe_route_train(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(noise), _p(logits), _p(topk_w),
+        _p(topk_idx), _p(prob_mean), _p(load_frac), _p(aux_loss), _p(ema_counts), _p(ema_tokens),
+        float(ema_decay), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_route_train")
 
 
 def moe_permute(shape: Shape, topk_idx, counts, offsets, row_to_slot, slot_to_row, ws,

@@ -216,7 +216,7 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
 
   mark(0);
   const RouteWs rw = route_ws(*s);
-  rc = hip_status(moe::launch_route(*s, x, w_router, bias, logits, topk_w, topk_idx,
+  rc = hip_status(moe::launch_route(*s, x, w_router, bias, nullptr, logits, topk_w, topk_idx,
                                     reinterpret_cast<float*>(at(ws, w.route + rw.partials)), rw.S,
                                     stream));
   if (rc != MOE_OK) return rc;
@@ -290,8 +290,60 @@ int moe_route(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, c
   if (!x || !w_router || !topk_w || !topk_idx || !ws) return MOE_ERR_INVALID_ARG;
   const RouteWs w = route_ws(*s);
   if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
-  return hip_status(moe::launch_route(*s, x, w_router, bias, logits, topk_w, topk_idx,
+  return hip_status(moe::launch_route(*s, x, w_router, bias, nullptr, logits, topk_w, topk_idx,
                                       reinterpret_cast<float*>(at(ws, w.partials)), w.S, stream));
+}
+
+namespace {
+struct RouteTrainWs {
+  RouteWs route;
+  size_t base_route, logits, part_p, part_c, total;
+};
+RouteTrainWs route_train_ws(const moe_shape& s) {
+  RouteTrainWs w{};
+  w.route = route_ws(s);
+  size_t o = 0;
+  auto take = [&](size_t n) {
+    const size_t at = o;
+    o += align_up(n);
+    return at;
+  };
+  const size_t nb = static_cast<size_t>(moe::router_stats_blocks(s.T));
+  w.base_route = take(w.route.total);
+  w.logits = take(sizeof(float) * static_cast<size_t>(s.T) * s.E);
+  w.part_p = take(sizeof(float) * nb * s.E);
+  w.part_c = take(sizeof(int32_t) * nb * s.E);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t moe_route_train_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return route_train_ws(*s).total;
+}
+
+int moe_route_train(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                    const float* bias, const float* noise, float* logits, float* topk_w,
+                    int32_t* topk_idx, float* prob_mean, float* load_frac, float* aux_loss,
+                    float* ema_counts, float* ema_tokens, float ema_decay, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!x || !w_router || !topk_w || !topk_idx || !prob_mean || !load_frac || !aux_loss || !ws)
+    return MOE_ERR_INVALID_ARG;
+  if (!(ema_decay >= 0.f && ema_decay <= 1.f)) return MOE_ERR_INVALID_ARG;  // also rejects NaN
+  const RouteTrainWs w = route_train_ws(*s);
+  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  float* lg = logits ? logits : reinterpret_cast<float*>(at(ws, w.logits));
+  rc = hip_status(moe::launch_route(
+      *s, x, w_router, bias, noise, lg, topk_w, topk_idx,
+      reinterpret_cast<float*>(at(ws, w.base_route + w.route.partials)), w.route.S, stream));
+  if (rc != MOE_OK) return rc;
+  return hip_status(moe::launch_router_stats(
+      *s, lg, topk_idx, reinterpret_cast<float*>(at(ws, w.part_p)),
+      reinterpret_cast<int32_t*>(at(ws, w.part_c)), ema_decay, prob_mean, load_frac, aux_loss,
+      ema_counts, ema_tokens, stream));
 }
 
 size_t moe_permute_workspace_size(const moe_shape* s) {

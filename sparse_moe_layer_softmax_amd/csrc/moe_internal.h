@@ -15,10 +15,19 @@ inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a
 // ---- router (route.hip)
 // Split of the hidden dimension used by the router GEMM (a divisor of H/128).
 int route_splits(int T, int H, int E);
-// partials: [S, T, E] fp32 scratch. logits may be NULL.
+// partials: [S, T, E] fp32 scratch. noise ([T,E] fp32, added to the logits) and logits may be
+// NULL.
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w_router,
-                        const float* bias, float* logits, float* topk_w, int32_t* topk_idx,
-                        float* partials, int S, hipStream_t stream);
+                        const float* bias, const float* noise, float* logits, float* topk_w,
+                        int32_t* topk_idx, float* partials, int S, hipStream_t stream);
+
+// ---- training-side router statistics (router_train.hip)
+// Blocks of the partial-sum pass (part_p [n, E] fp32 and part_c [n, E] int32 scratch).
+int router_stats_blocks(int T);
+hipError_t launch_router_stats(const moe_shape& s, const float* logits, const int32_t* topk_idx,
+                               float* part_p, int32_t* part_c, float decay, float* prob_mean,
+                               float* load_frac, float* aux_loss, float* ema_counts,
+                               float* ema_tokens, hipStream_t stream);
 
 // ---- dispatch (permute.hip)
 // Slots handled by one dispatch block, and the number of blocks.

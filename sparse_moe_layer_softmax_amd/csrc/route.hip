@@ -11,8 +11,9 @@
 //     split writes its own fp32 partial [S,T,E] (no atomics). For T >= 1024 and E = 256 the
 //     LDS-tiled MFMA kernel of the expert FFN computes the logits instead, with its own split
 //     of the hidden dimension into S partial planes.
-//  2. route_topk: one wavefront per token. Sums the S partials in split order, adds the bias,
-//     stores the logits, then selects the top-k by (logit descending, expert ascending) with
+//  2. route_topk: one wavefront per token. Sums the S partials in split order, adds the bias
+//     and, in training, the caller's score noise (Hy4 deep-dive `MoERouter`: noise on the scores
+//     before the softmax), stores the logits, then selects the top-k by (logit descending, expert ascending) with
 //     wavefront arg-max reductions. Because the renormalised weight p_j / sum_top p_i equals
 //     e^{l_j - l_max} / sum_top e^{l_i - l_max}, only the k selected exponentials are needed
 //     when norm_topk_prob is set; otherwise the full softmax denominator is reduced.
@@ -77,7 +78,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ part, int S, const float* __restrict__ bias,
-    float* __restrict__ logits, float* __restrict__ topk_w, int32_t* __restrict__ topk_idx,
+    const float* __restrict__ noise, float* __restrict__ logits, float* __restrict__ topk_w, int32_t* __restrict__ topk_idx,
     int T, int E, int K, int norm_topk, float scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
@@ -102,6 +103,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
       }
       for (; z < S; ++z) s += src[z * plane];
       if (bias) s += bias[e];
+      if (noise) s += noise[static_cast<size_t>(t) * E + e];
       v[q] = s;
       if (logits) logits[static_cast<size_t>(t) * E + e] = s;
     }
@@ -177,8 +179,8 @@ int route_splits(int T, int H, int E) {
 }
 
 hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w_router,
-                        const float* bias, float* logits, float* topk_w, int32_t* topk_idx,
-                        float* partials, int S, hipStream_t stream) {
+                        const float* bias, const float* noise, float* logits, float* topk_w,
+                        int32_t* topk_idx, float* partials, int S, hipStream_t stream) {
   if (route_tiled(s.T, s.H, s.E)) {
     const hipError_t e = launch_dense_gemm_f32(x, s.T, w_router, s.E, s.H, S, partials, stream);
     if (e != hipSuccess) return e;
@@ -188,7 +190,7 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w
                        s.H, s.E, s.H / S);
   }
   hipLaunchKernelGGL(route_topk_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream, partials, S,
-                     bias, logits, topk_w, topk_idx, s.T, s.E, s.K, s.norm_topk_prob,
+                     bias, noise, logits, topk_w, topk_idx, s.T, s.E, s.K, s.norm_topk_prob,
                      s.routed_scaling);
   return hipGetLastError();
 }

@@ -142,3 +142,20 @@ def test_fp8_entry_point_errors(m):
     assert lf8(s0, 16, 16, None, *w, None, None, None, None, None, 16, 16, 256, 1 << 40, None, None) == m.MOE_ERR_INVALID_ARG
     assert lf8(sc, 16, 16, None, *w, *w, 16, 256, 1024, None, None) == m.MOE_ERR_WORKSPACE
     assert lf8(sc, 16, 16, None, *w[:5], None, *w, 16, 256, 1 << 40, None, None) == m.MOE_ERR_INVALID_ARG
+
+
+def test_route_train_errors(m):
+    lib = m.library()
+    s = m.Shape(**HY4)
+    sc = ctypes.byref(s.c())
+    assert m.moe_route_train_workspace_size(s) > m.moe_route_workspace_size(s)
+    n = m.moe_route_train_workspace_size(s)
+    rt = lib.moe_route_train
+    ok = [16, 16, None, None, None, 16, 16, 16, 16, 16, None, None]
+    assert rt(sc, *ok, 0.9, 256, n - 1, None) == m.MOE_ERR_WORKSPACE
+    bad = list(ok)
+    bad[9] = None  # aux_loss
+    assert rt(sc, *bad, 0.9, 256, n, None) == m.MOE_ERR_INVALID_ARG
+    assert rt(sc, *ok, 1.5, 256, n, None) == m.MOE_ERR_INVALID_ARG
+    assert rt(sc, *ok, float("nan"), 256, n, None) == m.MOE_ERR_INVALID_ARG
+    assert rt(sc, *ok, 0.9, 256 + 8, n, None) == m.MOE_ERR_WORKSPACE  # misaligned
