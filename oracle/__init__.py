@@ -14,19 +14,20 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "moe_oracle.cpp")
+_SRCS = [os.path.join(_HERE, "moe_oracle.cpp"), os.path.join(_HERE, "moe_oracle_bwd.cpp")]
 _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 _lib = None
 
 
 def build(force: bool = False) -> str:
     """Compile the oracle with g++ (OpenMP, no fast-math, no FMA contraction)."""
+    deps = _SRCS + [os.path.join(_HERE, "moe_oracle.h")]
     if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
-        os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "moe_oracle.h"))
+        os.path.getmtime(f) for f in deps
     ):
         tmp = _LIB_PATH + ".tmp%d" % os.getpid()
         cmd = ["g++", "-O2", "-std=c++17", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
-               _SRC, "-o", tmp]
+               *_SRCS, "-o", tmp]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -66,6 +67,13 @@ def _declare(L):
     L.oracle_layer_forward_fp8.argtypes = [_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 15 + [_I] + [_P] * 12
     L.oracle_layer_dense_fp8.argtypes = [_I, _I, _I, _I, _I, _D] + [_P] * 17
     L.oracle_router_train_stats.argtypes = [_I, _I, _I, _P, _P, _D, _P, _P, _P, _P, _P]
+    L.oracle_combine_bwd.argtypes = [_I, _I, _I, _I] + [_P] * 6
+    L.oracle_down_bwd_rows.argtypes = [_I, _I, _I, _I, _P, _P, _P]
+    L.oracle_swiglu_bwd_rows.argtypes = [_I, _I, _I, _D, _I] + [_P] * 6
+    L.oracle_gateup_dgrad_rows.argtypes = [_I, _I, _I, _I] + [_P] * 5
+    L.oracle_wgrad.argtypes = [_I, _I, _I, _P, _P, _P]
+    L.oracle_router_bwd.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _D, _P]
+    L.oracle_layer_backward.argtypes = [_I] * 6 + [_D, _D, _I] + [_P] * 16 + [_D] + [_P] * 15
     L.oracle_num_threads.restype = _I
 
 
@@ -356,6 +364,108 @@ def router_train_stats(logits, topk_idx, decay=0.9, ema_counts=None, ema_tokens=
                                     _ptr(lf), _ptr(aux), _ptr(ec), _ptr(et))
     return dict(prob_mean=pm, load_frac=lf, aux_loss=float(aux[0]), ema_counts=ec,
                 ema_tokens=None if et is None else float(et[0]))
+
+
+# ---------------------------------------------------------------------------- backward pass
+def _f64(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float64)
+
+
+def combine_bwd(topk_w, slot_to_row, y_rows, dout, round_bf16=True):
+    """(dy_rows [R,H], d_topk_w [T,K]) of the combine; y_rows [R,H] as float64 values."""
+    topk_w, slot_to_row, dout = _f32(topk_w), _i32(slot_to_row), _u16(dout)
+    T, K = topk_w.shape
+    H = dout.shape[1]
+    y_rows = _f64(y_rows)
+    dy = np.zeros_like(y_rows)
+    dw = np.zeros((T, K))
+    lib().oracle_combine_bwd(T, K, H, int(round_bf16), _ptr(topk_w), _ptr(slot_to_row),
+                             _ptr(y_rows), _ptr(dout), _ptr(dy), _ptr(dw))
+    return dy, dw
+
+
+def down_bwd_rows(dy, wd, round_bf16=True):
+    dy, wd = _f64(dy), _u16(wd)
+    n, H = dy.shape
+    I = wd.shape[1]
+    dh = np.zeros((n, I))
+    if n:
+        lib().oracle_down_bwd_rows(n, H, I, int(round_bf16), _ptr(dy), _ptr(wd), _ptr(dh))
+    return dh
+
+
+def swiglu_bwd_rows(x_rows, wg, wu, dh, limit, round_bf16=True):
+    x_rows, wg, wu, dh = _u16(x_rows), _u16(wg), _u16(wu), _f64(dh)
+    n, H = x_rows.shape
+    I = wg.shape[0]
+    dg, du = np.zeros((n, I)), np.zeros((n, I))
+    if n:
+        lib().oracle_swiglu_bwd_rows(n, H, I, float(limit), int(round_bf16), _ptr(x_rows), _ptr(wg),
+                                     _ptr(wu), _ptr(dh), _ptr(dg), _ptr(du))
+    return dg, du
+
+
+def gateup_dgrad_rows(dg, du, wg, wu, round_bf16=True):
+    dg, du, wg, wu = _f64(dg), _f64(du), _u16(wg), _u16(wu)
+    n, I = dg.shape
+    H = wg.shape[1]
+    dx = np.zeros((n, H))
+    if n:
+        lib().oracle_gateup_dgrad_rows(n, H, I, int(round_bf16), _ptr(dg), _ptr(du), _ptr(wg),
+                                       _ptr(wu), _ptr(dx))
+    return dx
+
+
+def wgrad(A, B):
+    """A^T B over rows, float64 (weight gradients)."""
+    A, B = _f64(A), _f64(B)
+    n, M = A.shape
+    N = B.shape[1]
+    out = np.zeros((M, N))
+    lib().oracle_wgrad(n, M, N, _ptr(A), _ptr(B), _ptr(out))
+    return out
+
+
+def router_bwd(logits, topk_idx, d_topk_w, scale=1.0, norm_topk=True, d_aux=0.0):
+    logits, topk_idx, d_topk_w = _f32(logits), _i32(topk_idx), _f64(d_topk_w)
+    T, E = logits.shape
+    K = topk_idx.shape[1]
+    dl = np.zeros((T, E))
+    lib().oracle_router_bwd(T, E, K, int(bool(norm_topk)), float(scale), _ptr(logits),
+                            _ptr(topk_idx), _ptr(d_topk_w), float(d_aux), _ptr(dl))
+    return dl
+
+
+def layer_backward(x, wr, wg, wu, wd, fwd, dout, *, sg=None, su=None, sd=None, scale=1.0,
+                   limit=10.0, norm_topk=True, d_aux=0.0, round_bf16=True):
+    """Backward of layer_forward. ``fwd`` holds the forward's logits, topk_idx, topk_w, counts,
+    offsets, row_to_slot, slot_to_row (a layer_forward result). Returns a dict of float64
+    arrays: d_topk_w, d_logits, dx, d_wr, d_wg, d_wu, d_wd, (d_sg, d_su, d_sd), dh_rows,
+    dg_rows, du_rows, dx_rows, dx_router."""
+    x, wr, wg, wu, wd, dout = _u16(x), _u16(wr), _u16(wg), _u16(wu), _u16(wd), _u16(dout)
+    T, H = x.shape
+    E, I = wg.shape[0], wg.shape[1]
+    K = fwd["topk_idx"].shape[1]
+    off = _i32(fwd["offsets"])
+    R = int(off[-1])
+    r = dict(d_topk_w=np.zeros((T, K)), d_logits=np.zeros((T, E)), dx=np.zeros((T, H)),
+             d_wr=np.zeros((E, H)), d_wg=np.zeros((E, I, H)), d_wu=np.zeros((E, I, H)),
+             d_wd=np.zeros((E, H, I)), dh_rows=np.zeros((R, I)), dg_rows=np.zeros((R, I)),
+             du_rows=np.zeros((R, I)), dx_rows=np.zeros((R, H)), dx_router=np.zeros((T, H)))
+    if sg is not None:
+        sg, su, sd = _u16(sg), _u16(su), _u16(sd)
+        r.update(d_sg=np.zeros((I, H)), d_su=np.zeros((I, H)), d_sd=np.zeros((H, I)))
+    keep = [_f32(fwd["logits"]), _i32(fwd["topk_idx"]), _f32(fwd["topk_w"]), _i32(fwd["counts"]),
+            off, _i32(fwd["row_to_slot"]), _i32(fwd["slot_to_row"])]
+    lib().oracle_layer_backward(
+        T, H, E, K, I, int(bool(norm_topk)), float(scale), float(limit), int(round_bf16),
+        _ptr(x), _ptr(wr), _ptr(wg), _ptr(wu), _ptr(wd), _ptr(sg), _ptr(su), _ptr(sd),
+        *[_ptr(a) for a in keep], _ptr(dout), float(d_aux),
+        _ptr(r["d_topk_w"]), _ptr(r["d_logits"]), _ptr(r["dx"]), _ptr(r["d_wr"]), _ptr(r["d_wg"]),
+        _ptr(r["d_wu"]), _ptr(r["d_wd"]), _ptr(r.get("d_sg")), _ptr(r.get("d_su")),
+        _ptr(r.get("d_sd")), _ptr(r["dh_rows"]), _ptr(r["dg_rows"]), _ptr(r["du_rows"]),
+        _ptr(r["dx_rows"]), _ptr(r["dx_router"]))
+    return r
 
 
 def bf16_to_f64(a: np.ndarray) -> np.ndarray:

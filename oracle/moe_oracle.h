@@ -159,6 +159,48 @@ void oracle_router_train_stats(int T, int E, int K, const float* logits, const i
                                double decay, double* prob_mean, double* load_frac, double* aux,
                                double* ema_counts, double* ema_tokens);
 
+/* ---- backward pass (moe_oracle_bwd.cpp). Intermediate tensors are double arrays; with
+ * round_bf16 set, values the GPU stores in bf16 are rounded to bf16 at the same points.
+ * Row arrays are in the forward's dispatch order (rows grouped by expert).                  */
+/* dy[row(t,j)] = w_j * dout[t]; d_topk_w[t,j] = <dout[t], y[row(t,j)]> (0 for dropped slots) */
+void oracle_combine_bwd(int T, int K, int H, int round_bf16, const float* topk_w,
+                        const int32_t* slot_to_row, const double* y_rows, const uint16_t* dout,
+                        double* dy_rows, double* d_topk_w);
+/* dh[r,i] = sum_c dy[r,c] Wd[c,i]   (Wd [H,I] bf16)                                          */
+void oracle_down_bwd_rows(int n, int H, int I, int round_bf16, const double* dy,
+                          const uint16_t* wd, double* dh);
+/* recompute g = x Wg^T, u = x Wu^T; dg = dh * clamp(u) * silu'(clamp(g)) * [|g| <= L],
+ * du = dh * silu(clamp(g)) * [|u| <= L]  (no masks when L <= 0)                             */
+void oracle_swiglu_bwd_rows(int n, int H, int I, double limit, int round_bf16,
+                            const uint16_t* x_rows, const uint16_t* wg, const uint16_t* wu,
+                            const double* dh, double* dg, double* du);
+/* dx[r,c] = sum_i dg[r,i] Wg[i,c] + du[r,i] Wu[i,c]                                          */
+void oracle_gateup_dgrad_rows(int n, int H, int I, int round_bf16, const double* dg,
+                              const double* du, const uint16_t* wg, const uint16_t* wu,
+                              double* dx);
+/* out[m,c] = sum_r A[r,m] B[r,c]   (weight gradients)                                        */
+void oracle_wgrad(int n, int M, int N, const double* A, const double* B, double* out);
+/* routing-weight gradients (+ d_aux times the load-balancing loss) to logit gradients         */
+void oracle_router_bwd(int T, int E, int K, int norm_topk, double scale, const float* logits,
+                       const int32_t* topk_idx, const double* d_topk_w, double d_aux,
+                       double* d_logits);
+/* The whole backward from the forward's routing (logits, top-k, dispatch) and dout [T,H] bf16.
+ * Outputs (double): d_topk_w [T,K], d_logits [T,E], dx [T,H], d_wr [E,H], d_wg/d_wu [E,I,H],
+ * d_wd [E,H,I], d_sg/d_su [I,H], d_sd [H,I] (shared; unused when sg is NULL); optional row
+ * intermediates dh/dg/du [R,I], dx_rows [R,H] and dx_router [T,H] (NULL to skip).            */
+void oracle_layer_backward(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                           double limit, int round_bf16, const uint16_t* x, const uint16_t* wr,
+                           const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                           const uint16_t* sg, const uint16_t* su, const uint16_t* sd,
+                           const float* logits, const int32_t* topk_idx, const float* topk_w,
+                           const int32_t* counts, const int32_t* offsets,
+                           const int32_t* row_to_slot, const int32_t* slot_to_row,
+                           const uint16_t* dout, double d_aux, double* d_topk_w,
+                           double* d_logits, double* dx, double* d_wr, double* d_wg,
+                           double* d_wu, double* d_wd, double* d_sg, double* d_su, double* d_sd,
+                           double* dh_rows, double* dg_rows, double* du_rows, double* dx_rows,
+                           double* dx_router);
+
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int oracle_num_threads(void);
 
