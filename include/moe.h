@@ -246,6 +246,52 @@ int moe_layer_forward_fp8(const moe_shape* shape, const uint16_t* x, const uint1
                           const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
                           hipStream_t stream, hipEvent_t const* phase_events);
 
+/* ================================================================ backward pass (training)
+ * The routers on the pages are trained (Hy3 deep-dive `SparseMoERouter`: training branch with a
+ * load-balancing loss and count EMAs; Hy4 deep-dive `MoERouter`: noise on the scores in
+ * training). The pages print no backward; this is the derivative of moe_layer_forward:
+ *   combine   dy_row = bf16(w_j dout[t]) for each kept slot; d w_j = <dout[t], y_row>
+ *   down      dh = bf16(dy Wd)
+ *   SwiGLU    g = x Wg^T, u = x Wu^T recomputed in fp32; dg = bf16(dh clamp(u) silu'(clamp g)
+ *             [-L <= g <= L]), du = bf16(dh silu(clamp g) [-L <= u <= L]) (no masks for L <= 0)
+ *   gate/up   dx_row = bf16(dg Wg + du Wu)
+ *   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x per expert (and the shared expert, whose
+ *             dy is dout), fp32 sums over the expert's rows; an expert without rows gets zeros
+ *   routing   d logits through the renormalisation and routed scaling (top-k choice fixed) and
+ *             the softmax, plus d_aux times the gradient of E sum_e P_e f_e with f held fixed
+ *             (f counted from the top-k indices, before capacity); dWr = dl^T x (fp32),
+ *             dx_router = dl Wr (fp32)
+ *   dx        bf16( sum over the token's kept slots in slot order of dx_row, + the shared
+ *             row's dx_row, + dx_router )
+ * Inputs: the layer's bf16 weights (FP8 weights are not supported here), x, and the workspace
+ * of a moe_layer_forward call with the same shape and inputs (fwd_ws, its logits, routing,
+ * dispatch, h and y are read), d_out [T,H] bf16, d_aux (0 for no loss term).
+ * Outputs: d_x [T,H] bf16; d_w_router [E,H], d_w_gate/d_w_up [E,I,H], d_w_down [E,H,I] fp32;
+ * d_s_gate/d_s_up [I,H], d_s_down [H,I] fp32 (NULL iff n_shared = 0); d_topk_w [T,K] and
+ * d_logits [T,E] fp32 or NULL (then kept in the workspace). d_out and d_x 16-byte aligned.
+ * Every reduction runs in a fixed order: the same inputs give the same bits on every run.
+ * ws: moe_layer_backward_workspace_size(shape) bytes, 256-byte aligned.                        */
+typedef struct moe_bwd_ws_layout {
+  size_t dy;        /* [T + T*K, H] bf16: output gradient per layer row (shared rows first)  */
+  size_t dh;        /* [T + T*K, I] bf16                                                       */
+  size_t dgu;       /* [T + T*K, 2I] bf16: dg in columns [0, I), du in [I, 2I)                 */
+  size_t dx_rows;   /* [T + T*K, H] bf16: per-row input gradient                               */
+  size_t dx_router; /* [T, H] fp32                                                             */
+  size_t d_topk_w;  /* [T, K] fp32 (used when the caller passes no d_topk_w)                   */
+  size_t d_logits;  /* [T, E] fp32 (used when the caller passes no d_logits)                   */
+  size_t total;     /* bytes                                                                   */
+} moe_bwd_ws_layout;
+size_t moe_layer_backward_workspace_size(const moe_shape* shape);
+int moe_layer_backward_workspace_layout(const moe_shape* shape, moe_bwd_ws_layout* layout);
+int moe_layer_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                       const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                       const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                       const void* fwd_ws, size_t fwd_ws_bytes, const uint16_t* d_out,
+                       float d_aux, uint16_t* d_x, float* d_w_router, float* d_w_gate,
+                       float* d_w_up, float* d_w_down, float* d_s_gate, float* d_s_up,
+                       float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

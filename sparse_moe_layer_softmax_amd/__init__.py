@@ -27,7 +27,8 @@ EXPORTED = (
     "moe_permute", "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "moe_layer_forward",
     "moe_layer_forward_profiled", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
-    "moe_route_train_workspace_size", "moe_route_train",
+    "moe_route_train_workspace_size", "moe_route_train", "moe_layer_backward_workspace_size",
+    "moe_layer_backward_workspace_layout", "moe_layer_backward",
 )
 MOE_LAYER_PHASE_EVENTS = 7
 
@@ -48,6 +49,11 @@ class moe_shape(ctypes.Structure):
 class moe_layer_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("logits", "topk_w", "topk_idx", "counts", "offsets",
                                                "row_to_slot", "slot_to_row", "h", "y", "total")]
+
+
+class moe_bwd_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("dy", "dh", "dgu", "dx_rows", "dx_router",
+                                               "d_topk_w", "d_logits", "total")]
 
 
 @dataclass(frozen=True)
@@ -97,6 +103,10 @@ def _load():
         "moe_expert_ffn_fp8": ([sp, I32, I32] + [P] * 12 + [S, P], ctypes.c_int),
         "moe_route_train_workspace_size": ([sp], S),
         "moe_route_train": ([sp] + [P] * 12 + [ctypes.c_float, P, S, P], ctypes.c_int),
+        "moe_layer_backward_workspace_size": ([sp], S),
+        "moe_layer_backward_workspace_layout": ([sp, ctypes.POINTER(moe_bwd_ws_layout)], ctypes.c_int),
+        "moe_layer_backward": ([sp] + [P] * 9 + [S, P, ctypes.c_float] + [P] * 10 + [P, S, P],
+                               ctypes.c_int),
         "moe_layer_forward_fp8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
@@ -190,6 +200,29 @@ def moe_route_train(shape: Shape, x, w_router, bias, noise, logits, topk_w, topk
         _p(topk_idx), _p(prob_mean), _p(load_frac), _p(aux_loss), _p(ema_counts), _p(ema_tokens),
         float(ema_decay), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)),
         "moe_route_train")
+
+
+def moe_layer_backward_workspace_size(shape: Shape) -> int:
+    return library().moe_layer_backward_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_layer_backward_workspace_layout(shape: Shape) -> dict:
+    lay = moe_bwd_ws_layout()
+    _check(library().moe_layer_backward_workspace_layout(ctypes.byref(shape.c()), ctypes.byref(lay)),
+           "moe_layer_backward_workspace_layout")
+    return {n: getattr(lay, n) for n, _ in moe_bwd_ws_layout._fields_}
+
+
+def moe_layer_backward(shape: Shape, x, w_router, w_gate, w_up, w_down, s_gate, s_up, s_down,
+                       fwd_ws, d_out, d_aux, d_x, d_w_router, d_w_gate, d_w_up, d_w_down,
+                       d_s_gate, d_s_up, d_s_down, d_topk_w, d_logits, ws, stream=None):
+    """Backward of moe_layer_forward from its workspace fwd_ws (see include/moe.h)."""
+    _check(library().moe_layer_backward(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(w_gate), _p(w_up), _p(w_down),
+        _p(s_gate), _p(s_up), _p(s_down), _p(fwd_ws), fwd_ws.numel(), _p(d_out), float(d_aux),
+        _p(d_x), _p(d_w_router), _p(d_w_gate), _p(d_w_up), _p(d_w_down), _p(d_s_gate),
+        _p(d_s_up), _p(d_s_down), _p(d_topk_w), _p(d_logits), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer_backward")
 
 
 def moe_permute(shape: Shape, topk_idx, counts, offsets, row_to_slot, slot_to_row, ws,
@@ -286,6 +319,7 @@ class MoELayer:
         if out is None:
             out = torch.empty((self.shape.T, self.shape.H), dtype=torch.bfloat16, device=self.device)
         wr, b, wg, wu, wd, sg, su, sd = self.w
+        self._x = x
         if self.fp8:
             sc = self.scales
             moe_layer_forward_fp8(self.shape, x, wr, b, wg, sc["w_gate"], wu, sc["w_up"], wd,
@@ -297,6 +331,43 @@ class MoELayer:
         else:
             moe_layer_forward(self.shape, x, wr, b, wg, wu, wd, sg, su, sd, out, self.ws, stream)
         return out
+
+    def backward(self, d_out, d_aux=0.0, stream=None):
+        """moe_layer_backward after forward(): returns a dict of gradients (d_x bf16; d_w_router,
+        d_w_gate, d_w_up, d_w_down and the shared expert's d_s_* fp32; d_topk_w, d_logits fp32).
+        The backward workspace stays in self.bws (layout in self.blayout)."""
+        if self.fp8:
+            raise ValueError("the backward pass takes bf16 expert weights")
+        s, dev = self.shape, self.device
+        wr, _, wg, wu, wd, sg, su, sd = self.w
+        f32 = dict(dtype=torch.float32, device=dev)
+        g = dict(d_x=torch.empty((s.T, s.H), dtype=torch.bfloat16, device=dev),
+                 d_w_router=torch.empty((s.E, s.H), **f32),
+                 d_w_gate=torch.empty((s.E, s.I, s.H), **f32),
+                 d_w_up=torch.empty((s.E, s.I, s.H), **f32),
+                 d_w_down=torch.empty((s.E, s.H, s.I), **f32),
+                 d_topk_w=torch.empty((s.T, s.K), **f32),
+                 d_logits=torch.empty((s.T, s.E), **f32))
+        if sg is not None:
+            g.update(d_s_gate=torch.empty((s.I, s.H), **f32), d_s_up=torch.empty((s.I, s.H), **f32),
+                     d_s_down=torch.empty((s.H, s.I), **f32))
+        if getattr(self, "bws", None) is None:
+            self.bws = _ws(moe_layer_backward_workspace_size(s), dev)
+            self.blayout = moe_layer_backward_workspace_layout(s)
+        moe_layer_backward(s, self._x, wr, wg, wu, wd, sg, su, sd, self.ws, d_out, d_aux,
+                           g["d_x"], g["d_w_router"], g["d_w_gate"], g["d_w_up"], g["d_w_down"],
+                           g.get("d_s_gate"), g.get("d_s_up"), g.get("d_s_down"), g["d_topk_w"],
+                           g["d_logits"], self.bws, stream)
+        return g
+
+    def bwd_intermediate(self, name: str, dtype, shape):
+        """A view of a backward intermediate (dy, dh, dgu, dx_rows, dx_router)."""
+        off = self.blayout[name]
+        n = 1
+        for d in shape:
+            n *= d
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.bws[off:off + nbytes].view(dtype).view(*shape)
 
     def intermediate(self, name: str, dtype, shape):
         """A view of an intermediate inside the workspace (valid after the stream completes)."""

@@ -448,4 +448,121 @@ int moe_layer_forward_fp8(const moe_shape* s, const uint16_t* x, const uint16_t*
                     out, ws, ws_bytes, stream, ev);
 }
 
+namespace {
+struct BwdWs {
+  size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles, d_topk_w, d_logits, total;
+};
+BwdWs bwd_ws(const moe_shape& s) {
+  BwdWs w{};
+  const size_t rows = static_cast<size_t>(s.T) * s.K + (s.n_shared ? s.T : 0);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  w.dy = take(sizeof(uint16_t) * rows * s.H);
+  w.dh = take(sizeof(uint16_t) * rows * s.I);
+  w.dgu = take(sizeof(uint16_t) * rows * 2 * s.I);
+  w.dx_rows = take(sizeof(uint16_t) * rows * s.H);
+  w.dx_router = take(sizeof(float) * static_cast<size_t>(s.T) * s.H);
+  w.cnt = take(sizeof(int32_t) * s.E);
+  w.tiles = take(moe::tile_table_bytes(moe::max_tiles_for(static_cast<int>(rows), s.E + s.n_shared,
+                                                          moe::backward_tile_rows())));
+  w.d_topk_w = take(sizeof(float) * static_cast<size_t>(s.T) * s.K);
+  w.d_logits = take(sizeof(float) * static_cast<size_t>(s.T) * s.E);
+  w.total = o;
+  return w;
+}
+}  // namespace
+
+size_t moe_layer_backward_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return bwd_ws(*s).total;
+}
+
+int moe_layer_backward_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout) {
+  const int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  const BwdWs w = bwd_ws(*s);
+  layout->dy = w.dy;
+  layout->dh = w.dh;
+  layout->dgu = w.dgu;
+  layout->dx_rows = w.dx_rows;
+  layout->dx_router = w.dx_router;
+  layout->d_topk_w = w.d_topk_w;
+  layout->d_logits = w.d_logits;
+  layout->total = w.total;
+  return MOE_OK;
+}
+
+int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                       const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
+                       const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                       const void* fwd_ws, size_t fwd_ws_bytes, const uint16_t* d_out,
+                       float d_aux, uint16_t* d_x, float* d_w_router, float* d_w_gate,
+                       float* d_w_up, float* d_w_down, float* d_s_gate, float* d_s_up,
+                       float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  const bool shared = s->n_shared == 1;
+  if (!x || !w_router || !w_gate || !w_up || !w_down || !fwd_ws || !d_out || !d_x ||
+      !d_w_router || !d_w_gate || !d_w_up || !d_w_down || !ws)
+    return MOE_ERR_INVALID_ARG;
+  const bool sw = s_gate && s_up && s_down, sg = d_s_gate && d_s_up && d_s_down;
+  if (shared != sw || shared != sg) return MOE_ERR_INVALID_ARG;
+  if (!shared && (s_gate || s_up || s_down || d_s_gate || d_s_up || d_s_down))
+    return MOE_ERR_INVALID_ARG;
+  if (!std::isfinite(d_aux)) return MOE_ERR_INVALID_ARG;
+  if (s->H % 128 != 0 || s->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_x)) & 15u)
+    return MOE_ERR_INVALID_ARG;  // 16-byte vector accesses
+  const LayerWs fw = layer_ws(*s);
+  if (fwd_ws_bytes < fw.pub.total || !aligned(fwd_ws)) return MOE_ERR_WORKSPACE;
+  const BwdWs w = bwd_ws(*s);
+  if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  void* fws = const_cast<void*>(fwd_ws);
+  moe::BwdProblem b{};
+  b.s = *s;
+  b.shared = shared;
+  b.x = x;
+  b.w_router = w_router;
+  b.w_gate = w_gate;
+  b.w_up = w_up;
+  b.w_down = w_down;
+  b.s_gate = s_gate;
+  b.s_up = s_up;
+  b.s_down = s_down;
+  b.logits = reinterpret_cast<const float*>(at(fws, fw.pub.logits));
+  b.topk_w = reinterpret_cast<const float*>(at(fws, fw.pub.topk_w));
+  b.topk_idx = reinterpret_cast<const int32_t*>(at(fws, fw.pub.topk_idx));
+  b.row_to_slot = reinterpret_cast<const int32_t*>(at(fws, fw.pub.row_to_slot));
+  b.slot_to_row = reinterpret_cast<const int32_t*>(at(fws, fw.pub.slot_to_row));
+  b.grp_offsets = reinterpret_cast<const int32_t*>(at(fws, shared ? fw.ext_offsets : fw.pub.offsets));
+  b.h = reinterpret_cast<const uint16_t*>(at(fws, fw.pub.h));
+  b.y = reinterpret_cast<const uint16_t*>(at(fws, fw.pub.y));
+  b.dout = d_out;
+  b.d_aux = d_aux;
+  b.dy = reinterpret_cast<uint16_t*>(at(ws, w.dy));
+  b.dh = reinterpret_cast<uint16_t*>(at(ws, w.dh));
+  b.dgu = reinterpret_cast<uint16_t*>(at(ws, w.dgu));
+  b.dx_rows = reinterpret_cast<uint16_t*>(at(ws, w.dx_rows));
+  b.dx_router = reinterpret_cast<float*>(at(ws, w.dx_router));
+  b.cnt = reinterpret_cast<int32_t*>(at(ws, w.cnt));
+  b.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  b.d_topk_w = d_topk_w ? d_topk_w : reinterpret_cast<float*>(at(ws, w.d_topk_w));
+  b.d_logits = d_logits ? d_logits : reinterpret_cast<float*>(at(ws, w.d_logits));
+  b.d_x = d_x;
+  b.d_w_router = d_w_router;
+  b.d_w_gate = d_w_gate;
+  b.d_w_up = d_w_up;
+  b.d_w_down = d_w_down;
+  b.d_s_gate = d_s_gate;
+  b.d_s_up = d_s_up;
+  b.d_s_down = d_s_down;
+  return hip_status(moe::launch_layer_backward(b, stream));
+}
+
 }  // extern "C"

@@ -66,6 +66,13 @@ size_t tile_table_bytes(int max_tiles) { return sizeof(int32_t) * (1 + 4 * stati
 
 int max_tiles_for(int rows_max, int n_groups, int bm) { return (rows_max + bm - 1) / bm + n_groups; }
 
+hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int max_tiles,
+                              int32_t* tiles, hipStream_t stream) {
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, offsets, n_groups, bm,
+                     max_tiles, tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_single_group_offsets(int32_t* offsets, int rows, hipStream_t stream) {
   hipLaunchKernelGGL(single_group_offsets_kernel, dim3(1), dim3(1), 0, stream, offsets, rows);
   return hipGetLastError();

@@ -45,6 +45,9 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* topk_idx, int32_t* 
 // Tile table: tiles[0] = number of tiles, tiles[1 + i] = group, tiles[1 + max + i] = first row.
 size_t tile_table_bytes(int max_tiles);
 int max_tiles_for(int rows_max, int n_groups, int bm);
+// Tile table of bm-row tiles over the groups of offsets [n_groups + 1] (at most max_tiles).
+hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int max_tiles,
+                              int32_t* tiles, hipStream_t stream);
 // Writes {0, rows} into offsets[0..1] (a one-group offsets array on the device).
 hipError_t launch_single_group_offsets(int32_t* offsets, int rows, hipStream_t stream);
 
@@ -82,6 +85,30 @@ bool dense_gemm_f32_supported(int N, int Kd);
 int dense_gemm_splits(int rows, int Kd);
 hipError_t launch_dense_gemm_f32(const uint16_t* A, int rows, const uint16_t* W, int N, int Kd,
                                  int splits, float* out, hipStream_t stream);
+
+// ---- backward pass (backward.hip)
+// Rows per tile of the backward's grouped products (sizes its tile table).
+int backward_tile_rows();
+struct BwdProblem {
+  moe_shape s;
+  bool shared;
+  // inputs: layer weights and the forward's saved tensors (rows: shared rows first, then the
+  // routed rows grouped by expert; grp_offsets = {0, T, T + offsets} or offsets)
+  const uint16_t *x, *w_router, *w_gate, *w_up, *w_down, *s_gate, *s_up, *s_down;
+  const float *logits, *topk_w;
+  const int32_t *topk_idx, *row_to_slot, *slot_to_row, *grp_offsets;
+  const uint16_t *h, *y, *dout;
+  float d_aux;
+  // scratch
+  uint16_t *dy, *dh, *dgu, *dx_rows;  // [rows, H], [rows, I], [rows, 2I], [rows, H]
+  float* dx_router;                   // [T, H]
+  int32_t *cnt, *tiles;               // [E], tile table
+  // outputs
+  float *d_topk_w, *d_logits;         // [T, K], [T, E]
+  uint16_t* d_x;                      // [T, H]
+  float *d_w_router, *d_w_gate, *d_w_up, *d_w_down, *d_s_gate, *d_s_up, *d_s_down;
+};
+hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,

@@ -159,3 +159,14 @@ def test_route_train_errors(m):
     assert rt(sc, *ok, 1.5, 256, n, None) == m.MOE_ERR_INVALID_ARG
     assert rt(sc, *ok, float("nan"), 256, n, None) == m.MOE_ERR_INVALID_ARG
     assert rt(sc, *ok, 0.9, 256 + 8, n, None) == m.MOE_ERR_WORKSPACE  # misaligned
+
+
+def test_binding_argument_counts_match_the_header(m):
+    """Each ctypes signature has as many parameters as the header's declaration."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    lib = m.library()
+    for name in _declared_functions():
+        decl = re.search(r"\b%s\s*\(([^)]*)\)" % name, src).group(1)
+        n = 0 if decl.strip() in ("", "void") else decl.count(",") + 1
+        fn = getattr(lib, name)
+        assert fn.argtypes is not None and len(fn.argtypes) == n, (name, n, fn.argtypes)

@@ -1,0 +1,221 @@
+"""GPU parity of the layer backward (moe_layer_backward) against the oracle, through the C ABI.
+
+The forward runs first (moe_layer_forward); the backward reads its workspace. Comparisons are
+chained, as for the forward: every stage of the GPU backward is compared with the oracle's step
+applied to the same inputs the GPU stage consumed (its own dy, dh, dg/du, d logits):
+  * bf16 tensors (dy, dh, dg, du, per-row dx, dx): |gpu - oracle| <= 1e-2 |oracle| + 1e-3 rms.
+  * fp32 sums of n products (routing-weight gradients over H, weight gradients over an expert's
+    rows, dWr over T, dx_router over E): the accumulation bound n_steps * 2^-24 * sum|terms|,
+    n_steps = n/16 + 16 for the MFMA weight gradients (16-wide partial sums), n for the others.
+  * logit gradients: |gpu - oracle| <= 1e-5 * max|row| + 1e-6 |oracle| (fp32 softmax).
+Integers (routing) are the forward's, already checked bit-exactly by the forward tests. The
+oracle's own rounded backward from the same routing is compared end to end on the final
+gradients by relative norm (<= 2e-2): a consistency check, since single bf16 rounding flips
+propagate through the chain; the chained comparisons are the bar.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_moe_layer_softmax_amd as moe
+from sparse_moe_layer_softmax_amd.workloads import WORKLOADS, Workload, as_u16, generate
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+BASE = WORKLOADS["tiny_t128_h512_e32_k2"]
+CASES = {
+    "tiny_t128_h512_e32_k2": (BASE, 0.0),
+    "aux_ragged_t130_h256_e256_k8": (Workload("ragged_t130_h256_e256_k8", T=130, H=256, E=256, K=8,
+                                              I=256, scale=2.827, w_std=0.02, router_std=0.02,
+                                              seed=51), 0.7),
+    "no_shared_t128": (BASE.with_(name="no_shared_t128", n_shared=0, seed=52), 0.0),
+    "no_renorm_t128": (BASE.with_(name="no_renorm_t128", norm_topk=False, scale=2.827, seed=53), 0.2),
+    "capacity_drops_t200_e8_k2": (Workload("capacity_drops_t200_e8_k2", T=200, H=256, E=8, K=2,
+                                           I=256, capacity=30, zipf=0.3, seed=54), 0.5),
+    "clamp_forced_t128": (BASE.with_(name="clamp_forced_t128", x_std=30.0, seed=55), 0.0),
+    "multi_tile_t300_e16_k4": (Workload("multi_tile_t300_e16_k4", T=300, H=512, E=16, K=4, I=256,
+                                        scale=2.827, seed=56), 0.1),
+    "bands_t3000_e4_k2": (Workload("bands_t3000_e4_k2", T=3000, H=256, E=4, K=2, I=256,
+                                   scale=2.827, seed=57), 0.0),
+    "dense_e1_k1_t100": (Workload("dense_e1_k1_t100", T=100, H=512, E=1, K=1, I=256, n_shared=0,
+                                  seed=58), 0.0),
+}
+
+f64 = oracle.bf16_to_f64
+
+
+def _u16(v):
+    """float64 values that are bf16 values -> bf16 bit patterns."""
+    return (np.asarray(v, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _close_sum(got, ref, abs_sum, steps, what):
+    tol = steps * 2.0 ** -24 * abs_sum + 1e-30
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    bad = err > tol
+    assert not bad.any(), "%s: %d/%d out of tolerance; worst err %g tol %g" % (
+        what, bad.sum(), bad.size, err[bad].max(), tol[bad][np.argmax(err[bad])])
+
+
+def _run(wl, d_aux):
+    dev = generate(wl, DEV)
+    s = moe.Shape.of(wl)
+    layer = moe.MoELayer.from_inputs(s, dev)
+    layer.forward(dev["x"])
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1000 * wl.seed + 77)
+    dout = torch.randn(wl.T, wl.H, generator=gen, device=DEV).to(torch.bfloat16)
+    g = layer.backward(dout, d_aux)
+    torch.cuda.synchronize()
+    T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
+    n_id = T if wl.n_shared else 0
+    rows = n_id + T * K
+    fw = dict(
+        logits=layer.intermediate("logits", torch.float32, (T, E)).cpu().numpy(),
+        topk_w=layer.intermediate("topk_w", torch.float32, (T, K)).cpu().numpy(),
+        topk_idx=layer.intermediate("topk_idx", torch.int32, (T, K)).cpu().numpy(),
+        counts=layer.intermediate("counts", torch.int32, (E,)).cpu().numpy(),
+        offsets=layer.intermediate("offsets", torch.int32, (E + 1,)).cpu().numpy(),
+        row_to_slot=layer.intermediate("row_to_slot", torch.int32, (T * K,)).cpu().numpy(),
+        slot_to_row=layer.intermediate("slot_to_row", torch.int32, (T * K,)).cpu().numpy(),
+        h=as_u16(layer.intermediate("h", torch.bfloat16, (rows, I))),
+        y=as_u16(layer.intermediate("y", torch.bfloat16, (rows, H))),
+    )
+    bw = dict(
+        dy=as_u16(layer.bwd_intermediate("dy", torch.bfloat16, (rows, H))),
+        dh=as_u16(layer.bwd_intermediate("dh", torch.bfloat16, (rows, I))),
+        dgu=as_u16(layer.bwd_intermediate("dgu", torch.bfloat16, (rows, 2 * I))),
+        dx_rows=as_u16(layer.bwd_intermediate("dx_rows", torch.bfloat16, (rows, H))),
+        dx_router=layer.bwd_intermediate("dx_router", torch.float32, (T, H)).cpu().numpy(),
+    )
+    gg = {k: (as_u16(v) if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in g.items()}
+    return dev, P.host(dev), as_u16(dout), fw, bw, gg
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_backward_small(name):
+    assert torch.cuda.is_available()
+    wl, d_aux = CASES[name]
+    dev, hw, dout, fw, bw, gg = _run(wl, d_aux)
+    check_backward(wl, d_aux, hw, dout, fw, bw, gg)
+
+
+def check_backward(wl, d_aux, hw, dout, fw, bw, gg):
+    T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
+    n_id = T if wl.n_shared else 0
+    off = fw["offsets"]
+    R = int(off[-1])
+    x = hw["x"]
+    r2s = fw["row_to_slot"]
+
+    # combine backward: routed dy rows and routing-weight gradients
+    y_r = f64(fw["y"][n_id:n_id + R])
+    dy_o, dw_o = oracle.combine_bwd(fw["topk_w"], fw["slot_to_row"], y_r, dout)
+    P.assert_bf16_close(bw["dy"][n_id:n_id + R], _u16(dy_o), "dy (routed rows)")
+    if n_id:
+        np.testing.assert_array_equal(bw["dy"][:T], dout)
+    absw = np.zeros((T, K))
+    s2r = fw["slot_to_row"].reshape(T, K)
+    for j in range(K):
+        kept = s2r[:, j] >= 0
+        absw[kept, j] = np.sum(np.abs(f64(dout[kept])) * np.abs(y_r[s2r[kept, j]]), axis=1)
+    _close_sum(gg["d_topk_w"], dw_o, absw, H, "d_topk_w")
+
+    # per group: dh, dg/du, per-row dx, weight gradients
+    groups = [("shared", 0, n_id, hw["s_gate"], hw["s_up"], hw["s_down"], "d_s")] if n_id else []
+    for e in range(E):
+        groups.append(("expert %d" % e, n_id + off[e], n_id + off[e + 1], hw["w_gate"][e],
+                       hw["w_up"][e], hw["w_down"][e], e))
+    for label, a, b, wg, wu, wd, key in groups:
+        gwd = gg["d_s_down"] if key == "d_s" else gg["d_w_down"][key]
+        gwg = gg["d_s_gate"] if key == "d_s" else gg["d_w_gate"][key]
+        gwu = gg["d_s_up"] if key == "d_s" else gg["d_w_up"][key]
+        n = b - a
+        if n == 0:
+            assert not gwd.any() and not gwg.any() and not gwu.any(), label + ": no rows, zero grads"
+            continue
+        rows_x = x[np.arange(a, b)] if key == "d_s" else x[r2s[a - n_id:b - n_id] // K]
+        dy_g = f64(bw["dy"][a:b])
+        dh_o = oracle.down_bwd_rows(dy_g, wd)
+        P.assert_bf16_close(bw["dh"][a:b], _u16(dh_o), "dh " + label)
+        dh_g = f64(bw["dh"][a:b])
+        dg_o, du_o = oracle.swiglu_bwd_rows(rows_x, wg, wu, dh_g, wl.limit)
+        P.assert_bf16_close(bw["dgu"][a:b, :I], _u16(dg_o), "dg " + label)
+        P.assert_bf16_close(bw["dgu"][a:b, I:], _u16(du_o), "du " + label)
+        dg_g, du_g = f64(bw["dgu"][a:b, :I]), f64(bw["dgu"][a:b, I:])
+        dx_o = oracle.gateup_dgrad_rows(dg_g, du_g, wg, wu)
+        P.assert_bf16_close(bw["dx_rows"][a:b], _u16(dx_o), "dx rows " + label)
+        h_g, xf = f64(fw["h"][a:b]), f64(rows_x)
+        steps = n / 16 + 16
+        _close_sum(gwd, oracle.wgrad(dy_g, h_g), oracle.wgrad(np.abs(dy_g), np.abs(h_g)), steps,
+                   "dWd " + label)
+        _close_sum(gwg, oracle.wgrad(dg_g, xf), oracle.wgrad(np.abs(dg_g), np.abs(xf)), steps,
+                   "dWg " + label)
+        _close_sum(gwu, oracle.wgrad(du_g, xf), oracle.wgrad(np.abs(du_g), np.abs(xf)), steps,
+                   "dWu " + label)
+
+    # router: logit gradients from the GPU's routing-weight gradients, then dWr and dx_router
+    dl_o = oracle.router_bwd(fw["logits"], fw["topk_idx"], gg["d_topk_w"], wl.scale, wl.norm_topk,
+                             d_aux)
+    # fp32 rounding of dl_e = p_e (dp_e - sum_k p_k dp_k) is relative to the terms of dp, not to
+    # dl (they cancel when the selected weights' gradients are close): bound the terms by A
+    lg = fw["logits"].astype(np.float64)
+    pr = np.exp(lg - lg.max(axis=1, keepdims=True))
+    pr /= pr.sum(axis=1, keepdims=True)
+    dwg = gg["d_topk_w"].astype(np.float64)
+    if wl.norm_topk:
+        pk = np.take_along_axis(pr, fw["topk_idx"].astype(np.int64), axis=1)
+        Z = pk.sum(axis=1, keepdims=True)
+        A = wl.scale * (np.abs(dwg) / Z + np.abs((dwg * pk).sum(axis=1, keepdims=True)) / Z ** 2)
+    else:
+        A = wl.scale * np.abs(dwg)
+    A = A.max(axis=1, keepdims=True) + abs(d_aux) * E / T
+    tol = 1e-5 * pr * A + 1e-6 * np.abs(dl_o) + 1e-12
+    err = np.abs(gg["d_logits"] - dl_o)
+    assert np.all(err <= tol), ("d_logits", err.max(), int(np.sum(err > tol)))
+    dl_g = gg["d_logits"].astype(np.float64)
+    xf = f64(x)
+    _close_sum(gg["d_w_router"], oracle.wgrad(dl_g, xf), oracle.wgrad(np.abs(dl_g), np.abs(xf)),
+               T + 16, "dWr")
+    wr = f64(hw["w_router"])
+    _close_sum(bw["dx_router"], dl_g @ wr, np.abs(dl_g) @ np.abs(wr), E + 16, "dx_router")
+
+    # dx: the token's rows in slot order, the shared row, the router term
+    acc = np.zeros((T, H))
+    dxr = f64(bw["dx_rows"])
+    for j in range(K):
+        kept = s2r[:, j] >= 0
+        acc[kept] += dxr[n_id + s2r[kept, j]]
+    if n_id:
+        acc += dxr[:T]
+    acc += bw["dx_router"].astype(np.float64)
+    P.assert_bf16_close(gg["d_x"], oracle.bf16_round_array(acc), "dx")
+
+    # end to end: the oracle's own rounded backward from the same routing
+    fwd = {k: fw[k] for k in ("logits", "topk_idx", "topk_w", "counts", "offsets", "row_to_slot",
+                              "slot_to_row")}
+    r = oracle.layer_backward(x, hw["w_router"], hw["w_gate"], hw["w_up"], hw["w_down"], fwd, dout,
+                              sg=hw["s_gate"], su=hw["s_up"], sd=hw["s_down"], scale=wl.scale,
+                              limit=wl.limit, norm_topk=wl.norm_topk, d_aux=d_aux)
+    pairs = [("dx", f64(gg["d_x"]), r["dx"]), ("d_wr", gg["d_w_router"], r["d_wr"]),
+             ("d_wg", gg["d_w_gate"], r["d_wg"]), ("d_wu", gg["d_w_up"], r["d_wu"]),
+             ("d_wd", gg["d_w_down"], r["d_wd"])]
+    if n_id:
+        pairs += [("d_sg", gg["d_s_gate"], r["d_sg"]), ("d_su", gg["d_s_up"], r["d_su"]),
+                  ("d_sd", gg["d_s_down"], r["d_sd"])]
+    for k, a_, b_ in pairs:
+        rel = np.linalg.norm(np.asarray(a_, np.float64) - b_) / (np.linalg.norm(b_) + 1e-300)
+        assert rel <= 2e-2, (k, rel)
+
+
+def test_layer_backward_is_deterministic():
+    assert torch.cuda.is_available()
+    wl, d_aux = CASES["multi_tile_t300_e16_k4"]
+    outs = [_run(wl, d_aux)[5] for _ in range(2)]
+    for k in outs[0]:
+        np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
