@@ -32,6 +32,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--mode", choices=("forward", "train"), default="forward",
+                    help="train: one step = forward + backward (bf16 weights)")
     return ap.parse_args()
 
 
@@ -176,6 +178,8 @@ def main():
     dev = generate_inputs(wl)
     shape = moe.Shape.of(wl)
     layer = moe.MoELayer.from_inputs(shape, dev)
+    if args.mode == "train":
+        return train_step(args, wl, dev, layer)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -251,6 +255,154 @@ def main():
     if not args.no_cpu_baseline:
         n_tok = args.cpu_tokens or min(wl.T, 64)
         res["cpu_baseline"] = cpu_baseline(wl, dev, n_tok)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+def train_flops(wl, counts):
+    """Algorithmic FLOPs of one training step from the run's routing: the forward, and a backward
+    of dh, dx rows, dWd, dWg/dWu (2+4+2+4 H I per row), the recomputed gate/up (4 H I per row) and
+    the router's two products (2 T E H each)."""
+    T, H, E, I, S = wl.T, wl.H, wl.E, wl.I, wl.n_shared
+    rows = int(counts.sum()) + S * T
+    fwd = 2 * T * H * E + 6 * H * I * rows
+    bwd = 16 * H * I * rows + 4 * T * E * H
+    return fwd, bwd
+
+
+def cpu_baseline_train(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
+    """The oracle's forward and backward steps over a sample of the workload's tokens, taken as a
+    layer of their own (their routing, their experts' rows): router, routing, dispatch, expert
+    FFNs and combine, then the combine, down, SwiGLU, gate/up and weight-gradient backward of the
+    touched experts and the shared expert, the router backward and dx. Repeated until at least
+    min_seconds have passed."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_moe_layer_softmax_amd.workloads import as_u16
+
+    rng = np.random.default_rng(99)
+    toks = np.sort(rng.choice(wl.T, min(n_tok, wl.T), replace=False))
+    sel = torch.from_numpy(toks).to(dev["x"].device)
+    x = as_u16(dev["x"][sel])
+    wr = as_u16(dev["w_router"])
+    bias = None if dev["router_bias"] is None else dev["router_bias"].cpu().numpy()
+    g = torch.Generator()
+    g.manual_seed(7)
+    dout = as_u16(torch.randn(len(toks), wl.H, generator=g).to(torch.bfloat16))
+    lg = oracle.router_logits(x, wr, bias)
+    idx, _ = oracle.route_from_logits(lg, wl.K, wl.scale, wl.norm_topk)
+    experts = sorted(set(int(e) for e in idx.ravel()))
+    W = {e: tuple(as_u16(dev[n][e]) for n in ("w_gate", "w_up", "w_down")) for e in experts}
+    SW = tuple(as_u16(dev[n]) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
+    f64 = oracle.bf16_to_f64
+    Ts, K, H = len(toks), wl.K, wl.H
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        lg = oracle.router_logits(x, wr, bias)
+        idx, w = oracle.route_from_logits(lg, K, wl.scale, wl.norm_topk)
+        counts, offsets, r2s, s2r = oracle.dispatch(idx, wl.E, 0)
+        R = int(offsets[-1])
+        y = np.zeros((max(R, 1), H), np.uint16)
+        hh = {}
+        for e in experts:
+            a, b = offsets[e], offsets[e + 1]
+            hh[e], y[a:b] = oracle.expert_ffn_rows(x[r2s[a:b] // K], *W[e], wl.limit)
+        hs, ys = oracle.expert_ffn_rows(x, *SW, wl.limit) if SW else (None, None)
+        oracle.combine(w, s2r, y, ys)
+        dy, dw = oracle.combine_bwd(w, s2r, f64(y), dout)
+        dx = np.zeros((Ts, H))
+        for e in experts:
+            a, b = offsets[e], offsets[e + 1]
+            xr = x[r2s[a:b] // K]
+            dh = oracle.down_bwd_rows(dy[a:b], W[e][2])
+            dg, du = oracle.swiglu_bwd_rows(xr, W[e][0], W[e][1], dh, wl.limit)
+            dxr = oracle.gateup_dgrad_rows(dg, du, W[e][0], W[e][1])
+            oracle.wgrad(dy[a:b], f64(hh[e]))
+            oracle.wgrad(dg, f64(xr))
+            oracle.wgrad(du, f64(xr))
+            np.add.at(dx, r2s[a:b] // K, dxr)
+        if SW:
+            dys = f64(dout)
+            dh = oracle.down_bwd_rows(dys, SW[2])
+            dg, du = oracle.swiglu_bwd_rows(x, SW[0], SW[1], dh, wl.limit)
+            dx += oracle.gateup_dgrad_rows(dg, du, SW[0], SW[1])
+            oracle.wgrad(dys, f64(hs))
+            oracle.wgrad(dg, f64(x))
+            oracle.wgrad(du, f64(x))
+        dl = oracle.router_bwd(lg, idx, dw, wl.scale, wl.norm_topk, 0.0)
+        oracle.wgrad(dl, f64(x))
+        dx += dl @ f64(wr)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or reps >= max_reps:
+            break
+    return {"value": round(reps * Ts / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": "%d of the workload's %d tokens as a layer of their own, %d pass(es): forward "
+                      "and backward steps (%d distinct routed experts + shared), fp64 C++ oracle"
+                      % (Ts, wl.T, reps, len(experts))}
+
+
+def train_step(args, wl, dev, layer):
+    """One step = moe_layer_forward + moe_layer_backward (d_aux 0.01), HIP events around each."""
+    import torch
+
+    if wl.fp8:
+        print("train mode takes bf16 expert weights", file=sys.stderr)
+        sys.exit(2)
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    dout = torch.randn(wl.T, wl.H, generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.warmup):
+        layer.forward(dev["x"], out)
+        layer.backward(dout, 0.01)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        layer.forward(dev["x"], out)
+        ev[i][1].record(stream)
+        layer.backward(dout, 0.01)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    import numpy as np
+    f_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    b_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms = f_ms + b_ms
+    counts = layer.intermediate("counts", torch.int32, (wl.E,)).cpu().numpy()
+    fwd_f, bwd_f = train_flops(wl, counts)
+    a = bwd_f / (b_ms / 1e3) / 1e12
+    res = {
+        "metric": "MoE-layer training step (forward + backward) tokens/s at Hy4 shape",
+        "value": round(wl.T / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I,
+                   "n_shared": wl.n_shared, "mode": "train", "d_aux": 0.01,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(a, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(a / PEAK_MFMA_TFLOPS, 4), "traffic": None,
+                     "kernel": "moe_layer_backward (all its kernels)", "algorithmic_flops": bwd_f,
+                     "avg_launch_ms": round(b_ms, 4)},
+        "phases_ms": {"forward": round(f_ms, 4), "backward": round(b_ms, 4)},
+        "forward_mfma_frac": round(fwd_f / (f_ms / 1e3) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_train(wl, dev, args.cpu_tokens or min(wl.T, 16))
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

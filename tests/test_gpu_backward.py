@@ -219,3 +219,117 @@ def test_layer_backward_is_deterministic():
     outs = [_run(wl, d_aux)[5] for _ in range(2)]
     for k in outs[0]:
         np.testing.assert_array_equal(outs[0][k], outs[1][k], err_msg=k)
+
+
+# ----------------------------------------------------------------------------- full sizes, sampled
+FULL = ["hy4_decode_t64", "hy4_prefill_t8192"]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", FULL)
+def test_layer_backward_full_size_sampled(name):
+    """Full workload shapes: chained checks on sampled tokens (their routing-weight gradients,
+    every row stage and dx), sampled weight-gradient blocks of sampled experts, and every logit
+    gradient."""
+    assert torch.cuda.is_available()
+    wl = WORKLOADS[name]
+    d_aux = 0.01
+    print("\n[backward full-size] %s T=%d" % (name, wl.T), flush=True)
+    dev = generate(wl, DEV)
+    s = moe.Shape.of(wl)
+    layer = moe.MoELayer.from_inputs(s, dev)
+    layer.forward(dev["x"])
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4242)
+    dout_d = torch.randn(wl.T, wl.H, generator=gen, device=DEV).to(torch.bfloat16)
+    g = layer.backward(dout_d, d_aux)
+    torch.cuda.synchronize()
+    T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
+    n_id = T
+    rows = n_id + T * K
+    inter = lambda nm, dt, shp: layer.intermediate(nm, dt, shp)
+    binter = lambda nm, dt, shp: layer.bwd_intermediate(nm, dt, shp)
+    logits = inter("logits", torch.float32, (T, E)).cpu().numpy()
+    topk_w = inter("topk_w", torch.float32, (T, K)).cpu().numpy()
+    topk_idx = inter("topk_idx", torch.int32, (T, K)).cpu().numpy()
+    off = inter("offsets", torch.int32, (E + 1,)).cpu().numpy()
+    r2s = inter("row_to_slot", torch.int32, (T * K,)).cpu().numpy()
+    s2r = inter("slot_to_row", torch.int32, (T * K,)).cpu().numpy().reshape(T, K)
+    h_all, y_all = inter("h", torch.bfloat16, (rows, I)), inter("y", torch.bfloat16, (rows, H))
+    dy_all, dh_all = binter("dy", torch.bfloat16, (rows, H)), binter("dh", torch.bfloat16, (rows, I))
+    dgu_all, dxr_all = binter("dgu", torch.bfloat16, (rows, 2 * I)), binter("dx_rows", torch.bfloat16, (rows, H))
+    dx_router = binter("dx_router", torch.float32, (T, H))
+    take = lambda t_, idx: as_u16(t_[torch.from_numpy(np.asarray(idx, np.int64)).to(DEV)])
+    wgt = lambda nm, e=None: as_u16(dev[nm] if e is None else dev[nm][e])
+
+    rng = np.random.default_rng(9)
+    toks = np.sort(rng.choice(T, 4, replace=False))
+    dout = take(dout_d, toks)
+    x_s = take(dev["x"], toks)
+    for i, t in enumerate(toks):
+        kept = [j for j in range(K) if s2r[t, j] >= 0]
+        lrows = n_id + s2r[t, kept]
+        y_rows = f64(take(y_all, lrows))
+        s2r_local = np.full((1, K), -1, np.int32)
+        s2r_local[0, kept] = np.arange(len(kept))
+        dy_o, dw_o = oracle.combine_bwd(topk_w[t:t + 1], s2r_local, y_rows, dout[i:i + 1])
+        dy_g = take(dy_all, lrows)
+        P.assert_bf16_close(dy_g, _u16(dy_o), "dy token %d" % t)
+        absw = np.array([np.sum(np.abs(f64(dout[i])) * np.abs(y_rows[n])) for n in range(len(kept))])
+        _close_sum(g["d_topk_w"][t, kept].cpu().numpy(), dw_o[0, kept], absw, H, "d_topk_w token %d" % t)
+        # each routed row and the shared row: dh, dg/du, dx rows
+        row_list = [(lr, int(topk_idx[t, j]), "routed") for lr, j in zip(lrows, kept)] + [(t, -1, "shared")]
+        for lr, e, kind in row_list:
+            wg, wu, wd = ((wgt("s_gate"), wgt("s_up"), wgt("s_down")) if e < 0 else
+                          (wgt("w_gate", e), wgt("w_up", e), wgt("w_down", e)))
+            dy1 = f64(take(dy_all, [lr]))
+            P.assert_bf16_close(take(dh_all, [lr]), _u16(oracle.down_bwd_rows(dy1, wd)), "dh %s %d" % (kind, t))
+            dh1 = f64(take(dh_all, [lr]))
+            dg_o, du_o = oracle.swiglu_bwd_rows(x_s[i:i + 1], wg, wu, dh1, wl.limit)
+            dgu1 = take(dgu_all, [lr])
+            P.assert_bf16_close(dgu1[:, :I], _u16(dg_o), "dg %s %d" % (kind, t))
+            P.assert_bf16_close(dgu1[:, I:], _u16(du_o), "du %s %d" % (kind, t))
+            dx_o = oracle.gateup_dgrad_rows(f64(dgu1[:, :I]), f64(dgu1[:, I:]), wg, wu)
+            P.assert_bf16_close(take(dxr_all, [lr]), _u16(dx_o), "dx rows %s %d" % (kind, t))
+        # dx of the token
+        acc = f64(take(dxr_all, lrows)).sum(axis=0) + f64(take(dxr_all, [t]))[0]
+        dr = dx_router[int(t)].cpu().numpy().astype(np.float64)
+        P.assert_bf16_close(take(g["d_x"], [t]), oracle.bf16_round_array((acc + dr)[None]), "dx token %d" % t)
+    # every logit gradient, from the GPU's routing-weight gradients
+    dl_o = oracle.router_bwd(logits, topk_idx, g["d_topk_w"].cpu().numpy(), wl.scale, wl.norm_topk, d_aux)
+    dl_g = g["d_logits"].cpu().numpy()
+    lg = logits.astype(np.float64)
+    pr = np.exp(lg - lg.max(axis=1, keepdims=True))
+    pr /= pr.sum(axis=1, keepdims=True)
+    dwg = g["d_topk_w"].cpu().numpy().astype(np.float64)
+    pk = np.take_along_axis(pr, topk_idx.astype(np.int64), axis=1)
+    Z = pk.sum(axis=1, keepdims=True)
+    A = (wl.scale * (np.abs(dwg) / Z + np.abs((dwg * pk).sum(axis=1, keepdims=True)) / Z ** 2)).max(axis=1, keepdims=True)
+    tol = 1e-5 * pr * (A + d_aux * E / T) + 1e-6 * np.abs(dl_o) + 1e-12
+    assert np.all(np.abs(dl_g - dl_o) <= tol), "d_logits"
+    # weight-gradient blocks: 8 x 8 entries of the busiest and one other expert, the shared expert
+    cs, is_ = np.sort(rng.choice(H, 8, replace=False)), np.sort(rng.choice(I, 8, replace=False))
+    busiest = int(np.argmax(np.diff(off)))
+    for e in (busiest, int(rng.integers(E)), -1):
+        a, b = (0, T) if e < 0 else (n_id + off[e], n_id + off[e + 1])
+        if b == a:
+            continue
+        rws = np.arange(a, b)
+        dyb = f64(take(dy_all, rws))[:, cs]
+        hb = f64(take(h_all, rws))[:, is_]
+        dgb = f64(take(dgu_all, rws))[:, is_]
+        xrows = rws if e < 0 else r2s[rws - n_id] // K
+        xb = f64(take(dev["x"], xrows))[:, cs]
+        n = b - a
+        gd = (g["d_s_down"] if e < 0 else g["d_w_down"][e]).cpu().numpy()[np.ix_(cs, is_)]
+        gg_ = (g["d_s_gate"] if e < 0 else g["d_w_gate"][e]).cpu().numpy()[np.ix_(is_, cs)]
+        _close_sum(gd, oracle.wgrad(dyb, hb), oracle.wgrad(np.abs(dyb), np.abs(hb)), n / 16 + 16, "dWd block %d" % e)
+        _close_sum(gg_, oracle.wgrad(dgb, xb), oracle.wgrad(np.abs(dgb), np.abs(xb)), n / 16 + 16, "dWg block %d" % e)
+    # router weight gradient columns and the router term of sampled tokens
+    xc = f64(as_u16(dev["x"]))[:, cs]
+    _close_sum(g["d_w_router"].cpu().numpy()[:, cs], oracle.wgrad(dl_g.astype(np.float64), xc),
+               oracle.wgrad(np.abs(dl_g.astype(np.float64)), np.abs(xc)), T + 16, "dWr columns")
+    wr = f64(wgt("w_router"))
+    dls = dl_g[toks].astype(np.float64)
+    _close_sum(dx_router[torch.from_numpy(toks).to(DEV)].cpu().numpy(), dls @ wr, np.abs(dls) @ np.abs(wr), E + 16,
+               "dx_router tokens")
