@@ -6,6 +6,7 @@
 #include <climits>
 
 #include "moe.h"
+#include "ffn_kernels.h"
 #include "moe_internal.h"
 
 using moe::align_up;
@@ -450,7 +451,8 @@ int moe_layer_forward_fp8(const moe_shape* s, const uint16_t* x, const uint16_t*
 
 namespace {
 struct BwdWs {
-  size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles, d_topk_w, d_logits, total;
+  size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles_tiled, d_topk_w, d_logits, wdT, wguT;
+  size_t total;
 };
 BwdWs bwd_ws(const moe_shape& s) {
   BwdWs w{};
@@ -467,10 +469,13 @@ BwdWs bwd_ws(const moe_shape& s) {
   w.dx_rows = take(sizeof(uint16_t) * rows * s.H);
   w.dx_router = take(sizeof(float) * static_cast<size_t>(s.T) * s.H);
   w.cnt = take(sizeof(int32_t) * s.E);
-  w.tiles = take(moe::tile_table_bytes(moe::max_tiles_for(static_cast<int>(rows), s.E + s.n_shared,
-                                                          moe::backward_tile_rows())));
+  w.tiles_tiled = take(moe::tile_table_bytes(
+      moe::max_tiles_for(static_cast<int>(rows), s.E + s.n_shared, moe::kTiledRows)));
   w.d_topk_w = take(sizeof(float) * static_cast<size_t>(s.T) * s.K);
   w.d_logits = take(sizeof(float) * static_cast<size_t>(s.T) * s.E);
+  const size_t nmat = static_cast<size_t>(s.E + s.n_shared) * s.I * s.H;
+  w.wdT = take(sizeof(uint16_t) * nmat);
+  w.wguT = take(sizeof(uint16_t) * 2 * nmat);
   w.total = o;
   return w;
 }
@@ -551,7 +556,9 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
   b.dx_rows = reinterpret_cast<uint16_t*>(at(ws, w.dx_rows));
   b.dx_router = reinterpret_cast<float*>(at(ws, w.dx_router));
   b.cnt = reinterpret_cast<int32_t*>(at(ws, w.cnt));
-  b.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  b.tiles_tiled = reinterpret_cast<int32_t*>(at(ws, w.tiles_tiled));
+  b.wdT = reinterpret_cast<uint16_t*>(at(ws, w.wdT));
+  b.wguT = reinterpret_cast<uint16_t*>(at(ws, w.wguT));
   b.d_topk_w = d_topk_w ? d_topk_w : reinterpret_cast<float*>(at(ws, w.d_topk_w));
   b.d_logits = d_logits ? d_logits : reinterpret_cast<float*>(at(ws, w.d_logits));
   b.d_x = d_x;

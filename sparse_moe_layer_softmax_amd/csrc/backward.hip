@@ -4,26 +4,27 @@
 // load-balancing loss; Hy4 deep-dive `MoERouter` scores noise) but no backward is printed, so
 // this differentiates the forward in reverse:
 //   combine   dy_row = w_j * dout[t] (bf16); d w_j = <dout[t], y_row>          combine_bwd
-//   down      dh = dy Wd (bf16)                                                 gemm kDh
+//   down      dh = dy Wd (bf16)                                  tiled kernel, Wd transposed
 //   SwiGLU    g, u recomputed (x Wg^T, x Wu^T); dg = dh clamp(u) silu'(clamp g) [|g| <= L],
-//             du = dh silu(clamp g) [|u| <= L] (bf16)                           gemm kGu
-//   gate/up   dx_row = dg Wg + du Wu (bf16)                                     gemm kDx
-//   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x (fp32, per expert)     gemm kWd, kWgu
+//             du = dh silu(clamp g) [|u| <= L] (bf16)           tiled kernel, backward epilogue
+//   gate/up   dx_row = dg Wg + du Wu (bf16)                      tiled kernel, [Wg;Wu] transposed
+//   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x (fp32, per expert)      wgrad kernel
 //   routing   d logits through renormalisation, scaling and softmax, plus the load-balancing
 //             loss term (its f held fixed); dWr = dl^T x, dx_router = dl Wr    router_bwd, f32 gemm
 //   dx        the token's routed rows in slot order, the shared row, the router term  dx_sum
-// The shared expert is group 0 of the grouped GEMMs (identity rows), as in the forward.
+// The shared expert is group 0 of the grouped products (identity rows), as in the forward.
 //
-// One MFMA kernel serves the five grouped products. Tiles of 128x128 outputs, K staged 32 at
-// a time through a double-buffered LDS pair [128][40] (operand rows with K contiguous, padded
-// so that the 16-byte fragment reads of 16 lanes hit distinct bank groups); 4 wavefronts of
-// 64x64 (2x2 MFMA 32x32x16). Operands whose source is K-contiguous are copied row-wise with
-// 16-byte loads; operands whose source is contiguous along M or N (the data-gradient weights
-// and both operands of the weight gradients, which reduce over rows) are transposed on their
-// way into LDS. The next K tile's global loads are in flight while the current one computes.
+// The three data-gradient products run on the forward's LDS-tiled MFMA kernel (ffn_tiled.hip):
+// their weight operands are transposed once per call so that they, too, are read along the
+// reduction dimension. The weight gradients reduce over the rows of each expert; their kernel
+// stages 128x128 output tiles, K (rows) 32 at a time through a double-buffered LDS pair
+// [128][40] (both operands transposed on their way into LDS, padded rows so that the 16-byte
+// fragment reads of 16 lanes hit distinct bank groups), 4 wavefronts of 64x64 (2x2 MFMA
+// 32x32x16), the next K tile's global loads in flight during the current one's MFMAs.
 // Everything runs in a fixed order: no floating-point atomics.
 #include <cfloat>
 
+#include "ffn_kernels.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -31,24 +32,18 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 32, kLd = kBK + 8;  // LDS row stride in bf16
-enum Mode { kDh = 0, kGu = 1, kDx = 2, kWd = 3, kWgu = 4 };
+enum Mode { kWd = 0, kWgu = 1 };
 
 struct GemmP {
   const int32_t* offsets;  // [G+1] group row offsets (shared group first when present)
   int g_split;             // groups below it use the *_a (shared expert) operands
-  const int32_t* tiles;
-  int max_tiles;
   const int32_t* gather;   // row_to_slot
   int n_ident, topk, rows_max, H, I;
   const uint16_t* x;       // [T, H]
   const uint16_t* dy;      // [rows, H]
   const uint16_t* h;       // [rows, I] forward
-  const uint16_t* dh;      // [rows, I]
   const uint16_t* dgu;     // [rows, 2I] = [dg | du]
-  uint16_t* out16;         // kDh: dh, kGu: dgu, kDx: dx_rows
-  const uint16_t *wg_a, *wg_b, *wu_a, *wu_b, *wd_a, *wd_b;
   float *gwg_a, *gwg_b, *gwu_a, *gwu_b, *gwd_a, *gwd_b;
-  float limit;
 };
 
 __device__ __forceinline__ int x_row(const GemmP& p, int r) {
@@ -64,99 +59,53 @@ __device__ __forceinline__ void lds_column8(uint16_t* l, int outer0, int k, u32x
   }
 }
 
+// Weight gradients, one output matrix per group: C_g[m][n] = sum over the group's rows r of
+// A[r][m] B[r][n] (kWd: A = dy, B = h; kWgu: A = [dg | du], B = x of the row's token). Both
+// operands run along M / N in memory, so they are transposed into the K-contiguous LDS tiles.
 template <int MODE>
-__global__ __launch_bounds__(256) void bwd_gemm_kernel(GemmP p) {
+__global__ __launch_bounds__(256) void wgrad_kernel(GemmP p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kBM + kBN) * kLd];
-  constexpr bool GK = MODE == kWd || MODE == kWgu;  // grouped over K: weight gradients
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  int g, m0, m_end, k_lo, k_hi;
   const int n0 = blockIdx.y * kBN;
-  if (!GK) {
-    const int tile = blockIdx.x;
-    if (tile >= p.tiles[0]) return;
-    g = p.tiles[1 + tile];
-    m0 = p.tiles[1 + p.max_tiles + tile];
-    m_end = min(p.offsets[g + 1], p.rows_max);
-    if (m0 < 0 || m0 >= m_end) return;
-    k_lo = 0;
-    k_hi = MODE == kDx ? 2 * p.I : p.H;
-  } else {
-    g = blockIdx.z;
-    m0 = blockIdx.x * kBM;
-    m_end = MODE == kWd ? p.H : 2 * p.I;
-    k_lo = p.offsets[g];
-    k_hi = min(p.offsets[g + 1], p.rows_max);
-  }
+  const int g = blockIdx.z;
+  const int m0 = blockIdx.x * kBM;
+  const int k_lo = p.offsets[g];
+  const int k_hi = min(p.offsets[g + 1], p.rows_max);
   const bool sh = g < p.g_split;
   const size_t IH = static_cast<size_t>(p.I) * p.H;
   const size_t eo = sh ? 0 : static_cast<size_t>(g - p.g_split) * IH;
-  const uint16_t* Wg = (sh ? p.wg_a : p.wg_b) + eo;
-  const uint16_t* Wu = (sh ? p.wu_a : p.wu_b) + eo;
-  const uint16_t* Wd = (sh ? p.wd_a : p.wd_b) + eo;
   const int I2 = 2 * p.I;
 
-  // ---- global loads of one K tile (two 16-byte chunks of A and two of B per thread)
+  // ---- global loads of one K tile: two 16-byte chunks of each operand per thread (k row idx/16,
+  // 8 outer elements at 8 * (idx % 16))
   u32x4_t ra[2], rb[2];
   auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 256 * i;
+      const int kr = idx >> 4, c8 = 8 * (idx & 15), r = k0 + kr;
       const u32x4_t z = {0u, 0u, 0u, 0u};
-      if (!GK) {
-        // A rows (K contiguous): row idx/4, chunk idx%4
-        const int row = idx >> 2, ch = idx & 3, m = m0 + row, k = k0 + 8 * ch;
-        if (m < m_end) {
-          if (MODE == kDh) ra[i] = ld16(p.dy + static_cast<size_t>(m) * p.H + k);
-          if (MODE == kGu) ra[i] = ld16(p.x + static_cast<size_t>(x_row(p, m)) * p.H + k);
-          if (MODE == kDx) ra[i] = ld16(p.dgu + static_cast<size_t>(m) * I2 + k);
+      if (r < k_hi) {
+        if (MODE == kWd) {
+          ra[i] = ld16(p.dy + static_cast<size_t>(r) * p.H + m0 + c8);
+          rb[i] = ld16(p.h + static_cast<size_t>(r) * p.I + n0 + c8);
         } else {
-          ra[i] = z;
-        }
-        if (MODE == kGu) {  // B rows (K contiguous): 64 gate rows then the same 64 up rows
-          const int n = idx >> 2, c = n0 / 2 + (n & 63);
-          rb[i] = ld16((n < 64 ? Wg : Wu) + static_cast<size_t>(c) * p.H + k0 + 8 * ch);
-        } else {  // B contiguous along N: k row idx/16, 8 columns at 8*(idx%16)
-          const int kr = idx >> 4, nc = n0 + 8 * (idx & 15), k = k0 + kr;
-          if (MODE == kDh) rb[i] = ld16(Wd + static_cast<size_t>(k) * p.I + nc);
-          if (MODE == kDx)
-            rb[i] = k < p.I ? ld16(Wg + static_cast<size_t>(k) * p.H + nc)
-                            : ld16(Wu + static_cast<size_t>(k - p.I) * p.H + nc);
+          ra[i] = ld16(p.dgu + static_cast<size_t>(r) * I2 + m0 + c8);
+          rb[i] = ld16(p.x + static_cast<size_t>(x_row(p, r)) * p.H + n0 + c8);
         }
       } else {
-        // both operands contiguous along M / N, K = layer rows of the group
-        const int kr = idx >> 4, c8 = 8 * (idx & 15), r = k0 + kr;
-        if (r < k_hi) {
-          if (MODE == kWd) {
-            ra[i] = ld16(p.dy + static_cast<size_t>(r) * p.H + m0 + c8);
-            rb[i] = ld16(p.h + static_cast<size_t>(r) * p.I + n0 + c8);
-          } else {
-            ra[i] = ld16(p.dgu + static_cast<size_t>(r) * I2 + m0 + c8);
-            rb[i] = ld16(p.x + static_cast<size_t>(x_row(p, r)) * p.H + n0 + c8);
-          }
-        } else {
-          ra[i] = z;
-          rb[i] = z;
-        }
+        ra[i] = z;
+        rb[i] = z;
       }
     }
   };
   auto store = [&](uint16_t* l) {
-    uint16_t* la = l;
-    uint16_t* lb = l + kBM * kLd;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int idx = tid + 256 * i;
-      if (!GK) {
-        *reinterpret_cast<u32x4_t*>(la + (idx >> 2) * kLd + 8 * (idx & 3)) = ra[i];
-        if (MODE == kGu)
-          *reinterpret_cast<u32x4_t*>(lb + (idx >> 2) * kLd + 8 * (idx & 3)) = rb[i];
-        else
-          lds_column8(lb, 8 * (idx & 15), idx >> 4, rb[i]);
-      } else {
-        lds_column8(la, 8 * (idx & 15), idx >> 4, ra[i]);
-        lds_column8(lb, 8 * (idx & 15), idx >> 4, rb[i]);
-      }
+      lds_column8(l, 8 * (idx & 15), idx >> 4, ra[i]);
+      lds_column8(l + kBM * kLd, 8 * (idx & 15), idx >> 4, rb[i]);
     }
   };
 
@@ -195,51 +144,7 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(GemmP p) {
     }
   }
 
-  // ---- epilogue. Lane l of fragment (i, j) holds rows 8(v/4) + 4(l/32) + v%4, column l%32.
-  if (MODE == kGu) {
-    // gate (wn = 0) and up (wn = 1) of the same columns meet through LDS
-    float* ex = reinterpret_cast<float*>(&lds[0][0]);  // [2 wm][64][64] fp32 = 32 KB
-    __syncthreads();
-    if (wn == 1) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            ex[(wm * 64 + row) * 64 + j * 32 + (lane & 31)] = acc[i][j][v];
-          }
-    }
-    __syncthreads();
-    if (wn == 0) {
-      const float L = p.limit;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int row = i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const int m = m0 + wm * 64 + row;
-            if (m >= m_end) continue;
-            const int c = n0 / 2 + j * 32 + (lane & 31);  // intermediate column
-            const float gv = acc[i][j][v];
-            const float uv = ex[(wm * 64 + row) * 64 + j * 32 + (lane & 31)];
-            const float gc = L > 0.f ? fminf(fmaxf(gv, -L), L) : gv;
-            const float uc = L > 0.f ? fminf(fmaxf(uv, -L), L) : uv;
-            const float sg = 1.f / (1.f + expf(-gc));
-            const float dhv = bf16_to_f32(p.dh[static_cast<size_t>(m) * p.I + c]);
-            const bool pg = !(L > 0.f) || (gv >= -L && gv <= L);
-            const bool pu = !(L > 0.f) || (uv >= -L && uv <= L);
-            const float dg = pg ? dhv * uc * (sg * (1.f + gc * (1.f - sg))) : 0.f;
-            const float du = pu ? dhv * (gc * sg) : 0.f;
-            p.out16[static_cast<size_t>(m) * I2 + c] = f32_to_bf16(dg);
-            p.out16[static_cast<size_t>(m) * I2 + p.I + c] = f32_to_bf16(du);
-          }
-    }
-    return;
-  }
+  // ---- fp32 stores. Lane l of fragment (i, j) holds rows 8(v/4) + 4(l/32) + v%4, column l%32.
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -248,16 +153,13 @@ __global__ __launch_bounds__(256) void bwd_gemm_kernel(GemmP p) {
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (m >= m_end) continue;
         const float a = acc[i][j][v];
-        if (MODE == kDh) p.out16[static_cast<size_t>(m) * p.I + n] = f32_to_bf16(a);
-        if (MODE == kDx) p.out16[static_cast<size_t>(m) * p.H + n] = f32_to_bf16(a);
-        if (MODE == kWd) ((sh ? p.gwd_a : p.gwd_b) + eo)[static_cast<size_t>(m) * p.I + n] = a;
-        if (MODE == kWgu) {
-          if (m < p.I)
-            ((sh ? p.gwg_a : p.gwg_b) + eo)[static_cast<size_t>(m) * p.H + n] = a;
-          else
-            ((sh ? p.gwu_a : p.gwu_b) + eo)[static_cast<size_t>(m - p.I) * p.H + n] = a;
+        if (MODE == kWd) {
+          ((sh ? p.gwd_a : p.gwd_b) + eo)[static_cast<size_t>(m) * p.I + n] = a;
+        } else if (m < p.I) {
+          ((sh ? p.gwg_a : p.gwg_b) + eo)[static_cast<size_t>(m) * p.H + n] = a;
+        } else {
+          ((sh ? p.gwu_a : p.gwu_b) + eo)[static_cast<size_t>(m - p.I) * p.H + n] = a;
         }
       }
 }
@@ -303,6 +205,23 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) d_topk_w[s] = acc;
   }
+}
+
+// dst[b][c][col0 + r] = src[b][r][c] for r < R, c < C (bf16; R and C multiples of 64): the
+// weights in the layout that lets the tiled kernel read the data-gradient products' weight
+// operand along its reduction dimension.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
+                                                        size_t src_bstride, int R, int C,
+                                                        uint16_t* __restrict__ dst,
+                                                        size_t dst_bstride, int dst_ld, int col0) {
+  __shared__ uint16_t tile[64][66];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const uint16_t* s = src + blockIdx.z * src_bstride;
+  uint16_t* d = dst + blockIdx.z * dst_bstride;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) tile[i][tx] = s[static_cast<size_t>(r0 + i) * C + c0 + tx];
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) d[static_cast<size_t>(c0 + i) * dst_ld + col0 + r0 + tx] = tile[tx][i];
 }
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
@@ -463,14 +382,12 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(const uint16_t* __restrict_
 }
 
 template <int MODE>
-hipError_t gemm(const GemmP& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE>), grid, dim3(256), 0, stream, p);
+hipError_t wgrad(const GemmP& p, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((wgrad_kernel<MODE>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
-
-int backward_tile_rows() { return kBM; }
 
 hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   const moe_shape& s = b.s;
@@ -478,19 +395,14 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   const int n_ident = b.shared ? T : 0;
   const int G = E + (b.shared ? 1 : 0);
   const int rows_max = n_ident + T * K;
-  if (H % kBN || I % 64 || (2 * I) % kBM || H % kBM || G > 1024) return hipErrorInvalidValue;
+  if (H % kBN || I % kBN || H % 64 || I % 64 || G > 1024) return hipErrorInvalidValue;
   hipError_t e;
   // 1. combine backward
   hipLaunchKernelGGL(combine_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, b.dout,
                      b.topk_w, b.slot_to_row, b.y, n_ident, T, K, H, b.dy, b.d_topk_w);
-  // 2. tile table of 128-row tiles over the groups
-  const int max_tiles = max_tiles_for(rows_max, G, kBM);
-  if ((e = launch_build_tiles(b.grp_offsets, G, kBM, max_tiles, b.tiles, stream)) != hipSuccess) return e;
   GemmP p{};
   p.offsets = b.grp_offsets;
   p.g_split = b.shared ? 1 : 0;
-  p.tiles = b.tiles;
-  p.max_tiles = max_tiles;
   p.gather = b.row_to_slot;
   p.n_ident = n_ident;
   p.topk = K;
@@ -500,31 +412,97 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   p.x = b.x;
   p.dy = b.dy;
   p.h = b.h;
-  p.dh = b.dh;
   p.dgu = b.dgu;
-  p.wg_a = b.s_gate;
-  p.wu_a = b.s_up;
-  p.wd_a = b.s_down;
-  p.wg_b = b.w_gate;
-  p.wu_b = b.w_up;
-  p.wd_b = b.w_down;
   p.gwg_a = b.d_s_gate;
   p.gwu_a = b.d_s_up;
   p.gwd_a = b.d_s_down;
   p.gwg_b = b.d_w_gate;
   p.gwu_b = b.d_w_up;
   p.gwd_b = b.d_w_down;
-  p.limit = s.swiglu_limit;
-  // 3. dh = dy Wd;  4. dg, du with g, u recomputed;  5. dx rows = dg Wg + du Wu
-  p.out16 = b.dh;
-  if ((e = gemm<kDh>(p, dim3(max_tiles, I / kBN), stream)) != hipSuccess) return e;
-  p.out16 = b.dgu;
-  if ((e = gemm<kGu>(p, dim3(max_tiles, 2 * I / kBN), stream)) != hipSuccess) return e;
-  p.out16 = b.dx_rows;
-  if ((e = gemm<kDx>(p, dim3(max_tiles, H / kBN), stream)) != hipSuccess) return e;
+  // 2. weights transposed for the tiled kernel: WdT [I][H] and [Wg;Wu]T [H][2I] per expert
+  const size_t IH = static_cast<size_t>(I) * H;
+  auto transpose = [&](const uint16_t* src, int nb, int R, int C, uint16_t* dst, int ld, int col0) {
+    hipLaunchKernelGGL(transpose_kernel, dim3(C / 64, R / 64, nb), dim3(256), 0, stream, src, IH, R,
+                       C, dst, static_cast<size_t>(ld) * C, ld, col0);
+  };
+  uint16_t* wdT_s = b.wdT;
+  uint16_t* wdT_r = b.wdT + (b.shared ? IH : 0);
+  uint16_t* wguT_s = b.wguT;
+  uint16_t* wguT_r = b.wguT + (b.shared ? 2 * IH : 0);
+  if (b.shared) {
+    transpose(b.s_down, 1, H, I, wdT_s, H, 0);
+    transpose(b.s_gate, 1, I, H, wguT_s, 2 * I, 0);
+    transpose(b.s_up, 1, I, H, wguT_s, 2 * I, I);
+  }
+  transpose(b.w_down, E, H, I, wdT_r, H, 0);
+  transpose(b.w_gate, E, I, H, wguT_r, 2 * I, 0);
+  transpose(b.w_up, E, I, H, wguT_r, 2 * I, I);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // 3. dh = dy Wd, 4. dg, du with g, u recomputed, 5. dx rows = dg Wg + du Wu: the tiled kernel
+  const int mt = max_tiles_for(rows_max, G, kTiledRows);
+  if ((e = launch_build_tiles(b.grp_offsets, G, kTiledRows, mt, b.tiles_tiled, stream)) != hipSuccess)
+    return e;
+  {
+    GroupedParams q{};
+    q.A = b.dy;
+    q.a_rows = rows_max;
+    q.n_ident = 0x7fffffff;  // rows are already in layer order
+    q.rows_max = rows_max;
+    q.offsets = b.grp_offsets;
+    q.tiles = b.tiles_tiled;
+    q.max_tiles = mt;
+    q.W0a = wdT_s;
+    q.W0b = wdT_r;
+    q.g_split = b.shared ? 1 : 0;
+    q.out = b.dh;
+    q.N = I;
+    q.Kd = H;
+    if ((e = launch_tiled(kEpiBf16, q, mt, stream)) != hipSuccess) return e;
+  }
+  {
+    // g and u recomputed by the tiled forward kernel, whose epilogue forms dg and du
+    GroupedParams q{};
+    q.A = b.x;
+    q.a_rows = T;
+    q.gather = b.row_to_slot;
+    q.n_ident = n_ident;
+    q.topk = K;
+    q.rows_max = rows_max;
+    q.offsets = b.grp_offsets;
+    q.tiles = b.tiles_tiled;
+    q.max_tiles = mt;
+    q.W0a = b.s_gate;
+    q.W0b = b.w_gate;
+    q.W1a = b.s_up;
+    q.W1b = b.w_up;
+    q.g_split = b.shared ? 1 : 0;
+    q.out = b.dgu;
+    q.N = I;
+    q.Kd = H;
+    q.limit = s.swiglu_limit;
+    q.dh = b.dh;
+    if ((e = launch_tiled(kEpiSwigluBwd, q, mt, stream)) != hipSuccess) return e;
+  }
+  {
+    GroupedParams q{};
+    q.A = b.dgu;
+    q.a_rows = rows_max;
+    q.n_ident = 0x7fffffff;
+    q.rows_max = rows_max;
+    q.offsets = b.grp_offsets;
+    q.tiles = b.tiles_tiled;
+    q.max_tiles = mt;
+    q.W0a = wguT_s;
+    q.W0b = wguT_r;
+    q.g_split = b.shared ? 1 : 0;
+    q.out = b.dx_rows;
+    q.N = H;
+    q.Kd = 2 * I;
+    if ((e = launch_tiled(kEpiBf16, q, mt, stream)) != hipSuccess) return e;
+  }
   // 6. weight gradients, one output per group (zero for a group without rows)
-  if ((e = gemm<kWd>(p, dim3(H / kBM, I / kBN, G), stream)) != hipSuccess) return e;
-  if ((e = gemm<kWgu>(p, dim3(2 * I / kBM, H / kBN, G), stream)) != hipSuccess) return e;
+  if ((e = wgrad<kWd>(p, dim3(H / kBM, I / kBN, G), stream)) != hipSuccess) return e;
+  if ((e = wgrad<kWgu>(p, dim3(2 * I / kBM, H / kBN, G), stream)) != hipSuccess) return e;
   // 7. router: selections per expert, logit gradients, dWr = dl^T x, dx_router = dl Wr
   hipLaunchKernelGGL(zero_i32_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, b.cnt, E);
   hipLaunchKernelGGL(count_kernel, dim3((T * K + 255) / 256), dim3(256), 0, stream, b.topk_idx,

@@ -38,6 +38,7 @@ struct GroupedParams {
   int32_t N;                // output columns (I for gate/up, H for down)
   int32_t Kd;               // reduction length (H for gate/up, I for down)
   float limit;
+  const uint16_t* dh;       // kEpiSwigluBwd: [rows, N] bf16 gradient of h
 };
 
 
@@ -49,7 +50,9 @@ hipError_t launch_skinny(bool gated, bool w8, const GroupedParams& p, int max_ti
 
 // LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
 constexpr int kTiledRows = 320;
-enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2 };
+// kEpiSwigluBwd: gate/up recomputed for the backward pass; with dh it writes dg and du
+// (the clamped SwiGLU's derivative) into out [rows, 2N] as [dg | du].
+enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 }  // namespace moe

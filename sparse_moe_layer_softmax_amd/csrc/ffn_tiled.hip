@@ -108,7 +108,7 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
 template <int EPI, int MIV>
 __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1,
                                            int kb, int nk, int split) {
-  constexpr bool GATED = EPI == kEpiSwiglu;
+  constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sA = smem;                      // [2][320][64]
@@ -254,6 +254,30 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       }
     return;
   }
+  if (EPI == kEpiSwigluBwd) {
+    // g = acc[i][0], u = acc[i][1] at intermediate column c; the clamp passes the gradient on
+    // [-L, L]. Lanes store 32 consecutive columns of a row (64-byte segments).
+    const int c = nb * 128 + quarter * 32 + fr;
+    const float L = p.limit;
+    const size_t ld = 2 * static_cast<size_t>(p.N);
+#pragma unroll
+    for (int i = 0; i < MIV; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = rbase + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (r >= r1) continue;
+        const float gv = acc[i][0][v], uv = acc[i][1][v];
+        const float gc = L > 0.f ? fminf(fmaxf(gv, -L), L) : gv;
+        const float uc = L > 0.f ? fminf(fmaxf(uv, -L), L) : uv;
+        const float sg = 1.f / (1.f + expf(-gc));
+        const float dhv = bf16_to_f32(p.dh[static_cast<size_t>(r) * p.N + c]);
+        const bool pg = !(L > 0.f) || (gv >= -L && gv <= L);
+        const bool pu = !(L > 0.f) || (uv >= -L && uv <= L);
+        p.out[r * ld + c] = f32_to_bf16(pg ? dhv * uc * (sg * (1.f + gc * (1.f - sg))) : 0.f);
+        p.out[r * ld + p.N + c] = f32_to_bf16(pu ? dhv * (gc * sg) : 0.f);
+      }
+    return;
+  }
   // bf16 outputs go through LDS so that global stores are whole 16-byte row segments. Each
   // wavefront owns two [32][C] bf16 buffers of the (now idle) stage ring, used by alternate
   // fragment rows; their 16-byte chunks are XOR-swizzled by row so the column-wise fragment
@@ -370,6 +394,7 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
   static_assert(kBM == kTiledRows, "row tile of the tiled kernel");
   switch (epi) {
     case kEpiSwiglu: return tiled_launch<kEpiSwiglu>(p, p.N / 128, max_tiles, stream);
+    case kEpiSwigluBwd: return tiled_launch<kEpiSwigluBwd>(p, p.N / 128, max_tiles, stream);
     case kEpiBf16: return tiled_launch<kEpiBf16>(p, p.N / kTN, max_tiles, stream);
     default: return tiled_launch<kEpiF32>(p, p.N / kTN, max_tiles, stream);
   }

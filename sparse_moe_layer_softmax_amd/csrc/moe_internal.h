@@ -87,8 +87,6 @@ hipError_t launch_dense_gemm_f32(const uint16_t* A, int rows, const uint16_t* W,
                                  int splits, float* out, hipStream_t stream);
 
 // ---- backward pass (backward.hip)
-// Rows per tile of the backward's grouped products (sizes its tile table).
-int backward_tile_rows();
 struct BwdProblem {
   moe_shape s;
   bool shared;
@@ -102,7 +100,9 @@ struct BwdProblem {
   // scratch
   uint16_t *dy, *dh, *dgu, *dx_rows;  // [rows, H], [rows, I], [rows, 2I], [rows, H]
   float* dx_router;                   // [T, H]
-  int32_t *cnt, *tiles;               // [E], tile table
+  int32_t* cnt;                       // [E]
+  int32_t* tiles_tiled;               // tile table of the tiled forward kernel's row tile
+  uint16_t *wdT, *wguT;               // transposed weights: [G][I][H], [G][H][2I] (shared first)
   // outputs
   float *d_topk_w, *d_logits;         // [T, K], [T, E]
   uint16_t* d_x;                      // [T, H]
