@@ -452,6 +452,7 @@ int moe_layer_forward_fp8(const moe_shape* s, const uint16_t* x, const uint16_t*
 namespace {
 struct BwdWs {
   size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles_tiled, d_topk_w, d_logits, wdT, wguT;
+  size_t dyT, hT, dguT, xgT, ktiles, kt;
   size_t total;
 };
 BwdWs bwd_ws(const moe_shape& s) {
@@ -476,6 +477,14 @@ BwdWs bwd_ws(const moe_shape& s) {
   const size_t nmat = static_cast<size_t>(s.E + s.n_shared) * s.I * s.H;
   w.wdT = take(sizeof(uint16_t) * nmat);
   w.wguT = take(sizeof(uint16_t) * 2 * nmat);
+  const int mtk = moe::backward_ktiles(static_cast<int>(rows), s.E + s.n_shared);
+  const size_t ldk = static_cast<size_t>(mtk) * 64;
+  w.dyT = take(sizeof(uint16_t) * s.H * ldk);
+  w.hT = take(sizeof(uint16_t) * s.I * ldk);
+  w.dguT = take(sizeof(uint16_t) * 2 * s.I * ldk);
+  w.xgT = take(sizeof(uint16_t) * s.H * ldk);
+  w.ktiles = take(moe::tile_table_bytes(mtk));
+  w.kt = take(sizeof(int32_t) * 2 * (s.E + s.n_shared));
   w.total = o;
   return w;
 }
@@ -559,6 +568,12 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
   b.tiles_tiled = reinterpret_cast<int32_t*>(at(ws, w.tiles_tiled));
   b.wdT = reinterpret_cast<uint16_t*>(at(ws, w.wdT));
   b.wguT = reinterpret_cast<uint16_t*>(at(ws, w.wguT));
+  b.dyT = reinterpret_cast<uint16_t*>(at(ws, w.dyT));
+  b.hT = reinterpret_cast<uint16_t*>(at(ws, w.hT));
+  b.dguT = reinterpret_cast<uint16_t*>(at(ws, w.dguT));
+  b.xgT = reinterpret_cast<uint16_t*>(at(ws, w.xgT));
+  b.ktiles = reinterpret_cast<int32_t*>(at(ws, w.ktiles));
+  b.kt = reinterpret_cast<int32_t*>(at(ws, w.kt));
   b.d_topk_w = d_topk_w ? d_topk_w : reinterpret_cast<float*>(at(ws, w.d_topk_w));
   b.d_logits = d_logits ? d_logits : reinterpret_cast<float*>(at(ws, w.d_logits));
   b.d_x = d_x;

@@ -8,19 +8,19 @@
 //   SwiGLU    g, u recomputed (x Wg^T, x Wu^T); dg = dh clamp(u) silu'(clamp g) [|g| <= L],
 //             du = dh silu(clamp g) [|u| <= L] (bf16)           tiled kernel, backward epilogue
 //   gate/up   dx_row = dg Wg + du Wu (bf16)                      tiled kernel, [Wg;Wu] transposed
-//   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x (fp32, per expert)      wgrad kernel
+//   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x (fp32, per expert)
+//                                   tiled kernel over row-contiguous (transposed) operands
 //   routing   d logits through renormalisation, scaling and softmax, plus the load-balancing
 //             loss term (its f held fixed); dWr = dl^T x, dx_router = dl Wr    router_bwd, f32 gemm
 //   dx        the token's routed rows in slot order, the shared row, the router term  dx_sum
 // The shared expert is group 0 of the grouped products (identity rows), as in the forward.
 //
-// The three data-gradient products run on the forward's LDS-tiled MFMA kernel (ffn_tiled.hip):
-// their weight operands are transposed once per call so that they, too, are read along the
-// reduction dimension. The weight gradients reduce over the rows of each expert; their kernel
-// stages 128x128 output tiles, K (rows) 32 at a time through a double-buffered LDS pair
-// [128][40] (both operands transposed on their way into LDS, padded rows so that the 16-byte
-// fragment reads of 16 lanes hit distinct bank groups), 4 wavefronts of 64x64 (2x2 MFMA
-// 32x32x16), the next K tile's global loads in flight during the current one's MFMAs.
+// Every MFMA product runs on the forward's LDS-tiled kernel (ffn_tiled.hip), which reads both
+// operands along the reduction dimension. For the data gradients the weights are transposed once
+// per call. The weight gradients reduce over the rows of each expert: their operands (dy, h,
+// [dg | du], the gathered x) are transposed so that each expert's rows form one contiguous,
+// 64-aligned K range, and the tiled kernel runs in dense mode with one K range and one fp32
+// output matrix per expert (an expert without rows gets zeros).
 // Everything runs in a fixed order: no floating-point atomics.
 #include <cfloat>
 
@@ -31,137 +31,47 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 128, kBN = 128, kBK = 32, kLd = kBK + 8;  // LDS row stride in bf16
-enum Mode { kWd = 0, kWgu = 1 };
+constexpr int kKT = 64;  // rows per K-tile of the weight gradients (the tiled kernel's K step)
 
-struct GemmP {
-  const int32_t* offsets;  // [G+1] group row offsets (shared group first when present)
-  int g_split;             // groups below it use the *_a (shared expert) operands
-  const int32_t* gather;   // row_to_slot
-  int n_ident, topk, rows_max, H, I;
-  const uint16_t* x;       // [T, H]
-  const uint16_t* dy;      // [rows, H]
-  const uint16_t* h;       // [rows, I] forward
-  const uint16_t* dgu;     // [rows, 2I] = [dg | du]
-  float *gwg_a, *gwg_b, *gwu_a, *gwu_b, *gwd_a, *gwd_b;
-};
-
-__device__ __forceinline__ int x_row(const GemmP& p, int r) {
-  return r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
+// Weight-gradient operands with the layer rows (their reduction dimension) contiguous:
+// dst[c][t * 64 + j] = src[row(r0_t + j)][c] for the rows of K-tile t of the tile table (rows
+// past the group's end read as 0), so each group's rows start at a multiple of 64.
+// row(r) = r, or with gather the token of layer row r (identity rows first).
+__global__ __launch_bounds__(256) void ktile_transpose_kernel(
+    const uint16_t* __restrict__ src, int C, const int32_t* __restrict__ tiles, int max_tiles,
+    const int32_t* __restrict__ offsets, int rows_max, const int32_t* __restrict__ gather,
+    int n_ident, int topk, int ld_dst, uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[64][66];
+  const int t = blockIdx.y;
+  if (t >= tiles[0]) return;
+  const int g = tiles[1 + t], r0 = tiles[1 + max_tiles + t];
+  const int r_end = min(offsets[g + 1], rows_max);
+  const int c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i;
+    uint16_t v = 0;
+    if (r < r_end) {
+      const int sr = gather ? (r < n_ident ? r : gather[r - n_ident] / topk) : r;
+      v = src[static_cast<size_t>(sr) * C + c0 + tx];
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4)
+    dst[static_cast<size_t>(c0 + i) * ld_dst + static_cast<size_t>(t) * kKT + tx] = tile[tx][i];
 }
 
-// 8 bf16 values of a 16-byte chunk written down a column of the [rows][kLd] LDS tile.
-__device__ __forceinline__ void lds_column8(uint16_t* l, int outer0, int k, u32x4_t v) {
-#pragma unroll
-  for (int d = 0; d < 4; ++d) {
-    l[(outer0 + 2 * d) * kLd + k] = static_cast<uint16_t>(v[d] & 0xffffu);
-    l[(outer0 + 2 * d + 1) * kLd + k] = static_cast<uint16_t>(v[d] >> 16);
+// kt[2g], kt[2g+1]: first K-tile and K-tile count of group g (the tile table's order).
+__global__ void group_ktiles_kernel(const int32_t* __restrict__ offsets, int G,
+                                    int32_t* __restrict__ kt) {
+  int acc = 0;
+  for (int g = 0; g < G; ++g) {
+    const int c = (offsets[g + 1] - offsets[g] + kKT - 1) / kKT;
+    kt[2 * g] = acc;
+    kt[2 * g + 1] = c;
+    acc += c;
   }
-}
-
-// Weight gradients, one output matrix per group: C_g[m][n] = sum over the group's rows r of
-// A[r][m] B[r][n] (kWd: A = dy, B = h; kWgu: A = [dg | du], B = x of the row's token). Both
-// operands run along M / N in memory, so they are transposed into the K-contiguous LDS tiles.
-template <int MODE>
-__global__ __launch_bounds__(256) void wgrad_kernel(GemmP p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(kBM + kBN) * kLd];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int n0 = blockIdx.y * kBN;
-  const int g = blockIdx.z;
-  const int m0 = blockIdx.x * kBM;
-  const int k_lo = p.offsets[g];
-  const int k_hi = min(p.offsets[g + 1], p.rows_max);
-  const bool sh = g < p.g_split;
-  const size_t IH = static_cast<size_t>(p.I) * p.H;
-  const size_t eo = sh ? 0 : static_cast<size_t>(g - p.g_split) * IH;
-  const int I2 = 2 * p.I;
-
-  // ---- global loads of one K tile: two 16-byte chunks of each operand per thread (k row idx/16,
-  // 8 outer elements at 8 * (idx % 16))
-  u32x4_t ra[2], rb[2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      const int kr = idx >> 4, c8 = 8 * (idx & 15), r = k0 + kr;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      if (r < k_hi) {
-        if (MODE == kWd) {
-          ra[i] = ld16(p.dy + static_cast<size_t>(r) * p.H + m0 + c8);
-          rb[i] = ld16(p.h + static_cast<size_t>(r) * p.I + n0 + c8);
-        } else {
-          ra[i] = ld16(p.dgu + static_cast<size_t>(r) * I2 + m0 + c8);
-          rb[i] = ld16(p.x + static_cast<size_t>(x_row(p, r)) * p.H + n0 + c8);
-        }
-      } else {
-        ra[i] = z;
-        rb[i] = z;
-      }
-    }
-  };
-  auto store = [&](uint16_t* l) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i;
-      lds_column8(l, 8 * (idx & 15), idx >> 4, ra[i]);
-      lds_column8(l + kBM * kLd, 8 * (idx & 15), idx >> 4, rb[i]);
-    }
-  };
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-  const int nk = (k_hi - k_lo + kBK - 1) / kBK;
-  if (nk > 0) {
-    load(k_lo);
-    store(lds[0]);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-      if (t + 1 < nk) load(k_lo + (t + 1) * kBK);
-      const uint16_t* la = lds[t & 1];
-      const uint16_t* lb = la + kBM * kLd;
-#pragma unroll
-      for (int kk = 0; kk < kBK; kk += 16) {
-        u32x4_t af[2], bf[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          af[i] = *reinterpret_cast<const u32x4_t*>(la + (wm * 64 + i * 32 + (lane & 31)) * kLd + kk + 8 * (lane >> 5));
-          bf[i] = *reinterpret_cast<const u32x4_t*>(lb + (wn * 64 + i * 32 + (lane & 31)) * kLd + kk + 8 * (lane >> 5));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[i], bf[j], acc[i][j]);
-      }
-      if (t + 1 < nk) store(lds[(t + 1) & 1]);
-      __syncthreads();
-    }
-  }
-
-  // ---- fp32 stores. Lane l of fragment (i, j) holds rows 8(v/4) + 4(l/32) + v%4, column l%32.
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-        const float a = acc[i][j][v];
-        if (MODE == kWd) {
-          ((sh ? p.gwd_a : p.gwd_b) + eo)[static_cast<size_t>(m) * p.I + n] = a;
-        } else if (m < p.I) {
-          ((sh ? p.gwg_a : p.gwg_b) + eo)[static_cast<size_t>(m) * p.H + n] = a;
-        } else {
-          ((sh ? p.gwu_a : p.gwu_b) + eo)[static_cast<size_t>(m - p.I) * p.H + n] = a;
-        }
-      }
 }
 
 // Routed-row gradients dy = w * dout (bf16), the shared rows' dy = dout, and the routing-weight
@@ -381,12 +291,6 @@ __global__ __launch_bounds__(256) void dx_sum_kernel(const uint16_t* __restrict_
   *reinterpret_cast<u32x4_t*>(dx + static_cast<size_t>(t) * H + c) = o;
 }
 
-template <int MODE>
-hipError_t wgrad(const GemmP& p, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((wgrad_kernel<MODE>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
@@ -395,30 +299,11 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   const int n_ident = b.shared ? T : 0;
   const int G = E + (b.shared ? 1 : 0);
   const int rows_max = n_ident + T * K;
-  if (H % kBN || I % kBN || H % 64 || I % 64 || G > 1024) return hipErrorInvalidValue;
+  if (H % 256 || I % 256 || G > 1024) return hipErrorInvalidValue;
   hipError_t e;
   // 1. combine backward
   hipLaunchKernelGGL(combine_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, b.dout,
                      b.topk_w, b.slot_to_row, b.y, n_ident, T, K, H, b.dy, b.d_topk_w);
-  GemmP p{};
-  p.offsets = b.grp_offsets;
-  p.g_split = b.shared ? 1 : 0;
-  p.gather = b.row_to_slot;
-  p.n_ident = n_ident;
-  p.topk = K;
-  p.rows_max = rows_max;
-  p.H = H;
-  p.I = I;
-  p.x = b.x;
-  p.dy = b.dy;
-  p.h = b.h;
-  p.dgu = b.dgu;
-  p.gwg_a = b.d_s_gate;
-  p.gwu_a = b.d_s_up;
-  p.gwd_a = b.d_s_down;
-  p.gwg_b = b.d_w_gate;
-  p.gwu_b = b.d_w_up;
-  p.gwd_b = b.d_w_down;
   // 2. weights transposed for the tiled kernel: WdT [I][H] and [Wg;Wu]T [H][2I] per expert
   const size_t IH = static_cast<size_t>(I) * H;
   auto transpose = [&](const uint16_t* src, int nb, int R, int C, uint16_t* dst, int ld, int col0) {
@@ -500,9 +385,46 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     q.Kd = 2 * I;
     if ((e = launch_tiled(kEpiBf16, q, mt, stream)) != hipSuccess) return e;
   }
-  // 6. weight gradients, one output per group (zero for a group without rows)
-  if ((e = wgrad<kWd>(p, dim3(H / kBM, I / kBN, G), stream)) != hipSuccess) return e;
-  if ((e = wgrad<kWgu>(p, dim3(2 * I / kBM, H / kBN, G), stream)) != hipSuccess) return e;
+  // 6. weight gradients, one output matrix per group (zero for a group without rows): the
+  // operands transposed so that each group's rows are a contiguous, 64-aligned K range, then the
+  // tiled kernel in dense mode with one K range and one output plane per group
+  {
+    const int mtk = max_tiles_for(rows_max, G, kKT);
+    const int ldk = mtk * kKT;
+    if ((e = launch_build_tiles(b.grp_offsets, G, kKT, mtk, b.ktiles, stream)) != hipSuccess) return e;
+    hipLaunchKernelGGL(group_ktiles_kernel, dim3(1), dim3(1), 0, stream, b.grp_offsets, G, b.kt);
+    auto ktr = [&](const uint16_t* src, int C, const int32_t* gather, uint16_t* dst) {
+      hipLaunchKernelGGL(ktile_transpose_kernel, dim3(C / 64, mtk), dim3(256), 0, stream, src, C,
+                         b.ktiles, mtk, b.grp_offsets, rows_max, gather, n_ident, K, ldk, dst);
+    };
+    ktr(b.dy, H, nullptr, b.dyT);
+    ktr(b.h, I, nullptr, b.hT);
+    ktr(b.dgu, 2 * I, nullptr, b.dguT);
+    ktr(b.x, H, b.row_to_slot, b.xgT);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    auto wgrad = [&](const uint16_t* A, int M, const uint16_t* B, int N, float* out_shared,
+                     float* out_routed) {
+      GroupedParams q{};
+      q.A = A;
+      q.a_rows = M;
+      q.n_ident = 0x7fffffff;
+      q.rows_max = M;
+      q.tiles = nullptr;  // dense mode
+      q.W0a = q.W0b = B;
+      q.g_split = b.shared ? 1 : 0;
+      q.out_f32 = out_shared;
+      q.out_f32_b = out_routed;
+      q.N = N;
+      q.Kd = ldk;
+      q.k_splits = G;
+      q.k_tiles = b.kt;
+      return launch_tiled(kEpiF32, q, (M + kTiledRows - 1) / kTiledRows, stream);
+    };
+    if ((e = wgrad(b.dyT, H, b.hT, I, b.d_s_down, b.d_w_down)) != hipSuccess) return e;
+    if ((e = wgrad(b.dguT, I, b.xgT, H, b.d_s_gate, b.d_w_gate)) != hipSuccess) return e;
+    if ((e = wgrad(b.dguT + static_cast<size_t>(I) * ldk, I, b.xgT, H, b.d_s_up, b.d_w_up)) != hipSuccess)
+      return e;
+  }
   // 7. router: selections per expert, logit gradients, dWr = dl^T x, dx_router = dl Wr
   hipLaunchKernelGGL(zero_i32_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, b.cnt, E);
   hipLaunchKernelGGL(count_kernel, dim3((T * K + 255) / 256), dim3(256), 0, stream, b.topk_idx,

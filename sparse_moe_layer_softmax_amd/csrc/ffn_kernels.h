@@ -39,6 +39,11 @@ struct GroupedParams {
   int32_t Kd;               // reduction length (H for gate/up, I for down)
   float limit;
   const uint16_t* dh;       // kEpiSwigluBwd: [rows, N] bf16 gradient of h
+  // dense mode with per-split K ranges (weight gradients): split s reduces K-tiles
+  // [k_tiles[2s], k_tiles[2s] + k_tiles[2s+1]) into its own fp32 output plane; planes of
+  // splits >= g_split go to out_f32_b (at split - g_split)
+  const int32_t* k_tiles;
+  float* out_f32_b;
 };
 
 

@@ -209,35 +209,38 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // 0's first M of it: each wavefront waits for all of its DMA there (half 0 at the end of the
   // last C of K-tile kt, half 1 at the end of its last M). Past the end of K the DMA reloads the
   // last K-tile into the free stage (never read). Every wavefront passes 2 + 4*nk barriers.
-  dma_tile(0, 0);
-  wait_vmcnt<0>();
-  barrier_no_fence();
-  if (half == 1) barrier_no_fence();
-  for (int kt = 0; kt < nk; ++kt) {
+  // nk == 0 (an empty K range, uniform over the workgroup): no DMA, no barrier, zero result
+  if (nk > 0) {
+    dma_tile(0, 0);
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    if (half == 1) barrier_no_fence();
+    for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // ---- memory phase
-      if (MIV > 0) fetch(kt & 1, h);
-      if (h == 0) dma_tile(min(kt + 1, nk - 1), (kt + 1) & 1);
-      if (half == 1 && h == 1) wait_vmcnt<0>();
-      wait_lgkmcnt0();
-      barrier_no_fence();
-      // ---- compute phase
-      if (MIV > 0) {
-        __builtin_amdgcn_s_setprio(1);
+      for (int h = 0; h < 2; ++h) {
+        // ---- memory phase
+        if (MIV > 0) fetch(kt & 1, h);
+        if (h == 0) dma_tile(min(kt + 1, nk - 1), (kt + 1) & 1);
+        if (half == 1 && h == 1) wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier_no_fence();
+        // ---- compute phase
+        if (MIV > 0) {
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+          for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-          for (int i = 0; i < MIV; ++i)
+            for (int i = 0; i < MIV; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
-        __builtin_amdgcn_s_setprio(0);
+              for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        if (half == 0 && h == 1) wait_vmcnt<0>();
+        barrier_no_fence();
       }
-      if (half == 0 && h == 1) wait_vmcnt<0>();
-      barrier_no_fence();
     }
+    if (half == 0) barrier_no_fence();
   }
-  if (half == 0) barrier_no_fence();
 
   // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
   const int rbase = r0 + half * 160;
@@ -248,7 +251,10 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       for (int v = 0; v < 16; ++v) {
         const int r = rbase + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= r1) continue;
-        float* o = p.out_f32 + (static_cast<size_t>(split) * p.rows_max + r) * p.N + nb * kTN + quarter * 64 + fr;
+        const size_t plane = static_cast<size_t>(p.rows_max) * p.N;
+        float* ob = p.out_f32 + split * plane;
+        if (p.k_tiles && split >= p.g_split) ob = p.out_f32_b + (split - p.g_split) * plane;
+        float* o = ob + static_cast<size_t>(r) * p.N + nb * kTN + quarter * 64 + fr;
 #pragma unroll
         for (int j = 0; j < 2; ++j) o[j * 32] = acc[i][j][v];
       }
@@ -328,10 +334,18 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   if (slot >= per_xcd) return;
   const int ws = (blockIdx.x % kXcds) * per_xcd + slot;
   if (ws >= total) return;
-  // dense mode: the K splits of one output tile are adjacent items
-  const int split = ws % splits;
-  const int w = ws / splits;
-  const int nk = p.Kd / kBK / splits;  // K-tiles of this item
+  // dense mode: the K splits of one output tile are adjacent items. With per-split K-tile ranges
+  // (k_tiles: one output matrix per split, over its own rows of K) the splits are outermost.
+  int split, w;
+  if (p.k_tiles) {
+    split = ws / (n_tiles * nblk);
+    w = ws - split * (n_tiles * nblk);
+  } else {
+    split = ws % splits;
+    w = ws / splits;
+  }
+  const int nk = p.k_tiles ? p.k_tiles[2 * split + 1] : p.Kd / kBK / splits;  // K-tiles of this item
+  const int kb = p.k_tiles ? p.k_tiles[2 * split] : split * nk;                // its first K-tile
   // the group's items occupy nblk x its tile range of the work list
   const int ts = w / nblk;
   const int g = dense ? 0 : p.tiles[1 + ts];
@@ -356,12 +370,12 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   // specialisation passes the same barriers.
   const int miv = min(kMI, max(0, (r1 - (r0 + half * 160) + 31) / 32));
   switch (miv) {
-    case 0: tiled_main<EPI, 0>(p, g, nb, r0, r1, split * nk, nk, split); break;
-    case 1: tiled_main<EPI, 1>(p, g, nb, r0, r1, split * nk, nk, split); break;
-    case 2: tiled_main<EPI, 2>(p, g, nb, r0, r1, split * nk, nk, split); break;
-    case 3: tiled_main<EPI, 3>(p, g, nb, r0, r1, split * nk, nk, split); break;
-    case 4: tiled_main<EPI, 4>(p, g, nb, r0, r1, split * nk, nk, split); break;
-    default: tiled_main<EPI, 5>(p, g, nb, r0, r1, split * nk, nk, split); break;
+    case 0: tiled_main<EPI, 0>(p, g, nb, r0, r1, kb, nk, split); break;
+    case 1: tiled_main<EPI, 1>(p, g, nb, r0, r1, kb, nk, split); break;
+    case 2: tiled_main<EPI, 2>(p, g, nb, r0, r1, kb, nk, split); break;
+    case 3: tiled_main<EPI, 3>(p, g, nb, r0, r1, kb, nk, split); break;
+    case 4: tiled_main<EPI, 4>(p, g, nb, r0, r1, kb, nk, split); break;
+    default: tiled_main<EPI, 5>(p, g, nb, r0, r1, kb, nk, split); break;
   }
 }
 

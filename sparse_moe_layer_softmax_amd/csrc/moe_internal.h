@@ -103,12 +103,17 @@ struct BwdProblem {
   int32_t* cnt;                       // [E]
   int32_t* tiles_tiled;               // tile table of the tiled forward kernel's row tile
   uint16_t *wdT, *wguT;               // transposed weights: [G][I][H], [G][H][2I] (shared first)
+  // weight-gradient operands with the rows contiguous (ld = backward_ktile_ld(rows, G)):
+  uint16_t *dyT, *hT, *dguT, *xgT;    // [H][ld], [I][ld], [2I][ld], [H][ld]
+  int32_t *ktiles, *kt;               // K-tile table of 64-row tiles, [2G] per-group ranges
   // outputs
   float *d_topk_w, *d_logits;         // [T, K], [T, E]
   uint16_t* d_x;                      // [T, H]
   float *d_w_router, *d_w_gate, *d_w_up, *d_w_down, *d_s_gate, *d_s_up, *d_s_down;
 };
 hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream);
+// Row stride of the transposed weight-gradient operands, and the K-tile table's tile bound.
+inline int backward_ktiles(int rows_max, int n_groups) { return max_tiles_for(rows_max, n_groups, 64); }
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,
