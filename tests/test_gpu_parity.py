@@ -48,6 +48,12 @@ SMALL = {
     # several 8-tile bands in one group (about 1500 rows per expert), ragged last tiles
     "bands_t3000_e4_k2": Workload("bands_t3000_e4_k2", T=3000, H=256, E=4, K=2, I=256, scale=2.827,
                                   seed=22),
+    # a few hundred rows per expert on the tiled kernel: one and two row tiles per expert (skewed
+    # router), partly filled tiles
+    "midsize_t1000_h512_e16_k4": Workload("midsize_t1000_h512_e16_k4", T=1000, H=512, E=16, K=4, I=256,
+                                         scale=2.827, zipf=0.4, seed=26),
+    "midsize_t640_h256_e32_k8": Workload("midsize_t640_h256_e32_k8", T=640, H=256, E=32, K=8, I=512,
+                                        scale=2.827, seed=27),
     # a dense SwiGLU FFN (E = 1, k = 1, no shared expert) with a wide intermediate on the tiled path
     "dense_ffn_t700_h512_i2304": Workload("dense_ffn_t700_h512_i2304", T=700, H=512, E=1, K=1,
                                           I=2304, n_shared=0, seed=25),
@@ -232,6 +238,7 @@ def _dev_weights(dev, names, lead=False):
 
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "ragged_t130_h256_e256_k8",
                                   "clamp_forced_t128", "multi_tile_t300_e16_k4", "bands_t3000_e4_k2",
+                                  "midsize_t1000_h512_e16_k4", "midsize_t640_h256_e32_k8",
                                   "fp8_tiny_t128_h512_e32_k2", "fp8_ragged_t130_h256_e256_k8",
                                   "fp8_clamp_forced_t128", "fp8_multi_tile_t300_e16_k4",
                                   "fp8_bands_t3000_e4_k2"])
