@@ -82,9 +82,9 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
-  // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA. FP8
-  // weights always take the weight-streaming kernel (its W8 form), which handles any row count.
-  const bool tiled = !q.w8 && q.rows_max >= 64 * q.n_groups;
+  // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA. Both
+  // kernels have an FP8-weight form.
+  const bool tiled = q.rows_max >= 64 * q.n_groups;
   const int bm = tiled ? kTiledRows : kSkinnyRows;
   const int max_tiles = max_tiles_for(q.rows_max, q.n_groups, bm);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, q.offsets, q.n_groups, bm,
@@ -120,7 +120,7 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.out = q.h;
   p.N = q.I;
   p.Kd = q.H;
-  hipError_t e = tiled ? launch_tiled(kEpiSwiglu, p, max_tiles, stream)
+  hipError_t e = tiled ? launch_tiled(q.w8 ? kEpiSwiglu8 : kEpiSwiglu, p, max_tiles, stream)
                        : launch_skinny(true, q.w8, p, max_tiles, stream);
   if (e != hipSuccess) return e;
   mark(1);
@@ -142,7 +142,7 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.out = q.y;
   p.N = q.H;
   p.Kd = q.I;
-  e = tiled ? launch_tiled(kEpiBf16, p, max_tiles, stream)
+  e = tiled ? launch_tiled(q.w8 ? kEpiBf16_8 : kEpiBf16, p, max_tiles, stream)
             : launch_skinny(false, q.w8, p, max_tiles, stream);
   if (e != hipSuccess) return e;
   mark(2);

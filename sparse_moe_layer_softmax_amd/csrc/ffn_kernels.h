@@ -57,7 +57,10 @@ hipError_t launch_skinny(bool gated, bool w8, const GroupedParams& p, int max_ti
 constexpr int kTiledRows = 320;
 // kEpiSwigluBwd: gate/up recomputed for the backward pass; with dh it writes dg and du
 // (the clamped SwiGLU's derivative) into out [rows, 2N] as [dg | du].
-enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3 };
+// kEpiSwiglu8 / kEpiBf16_8: kEpiSwiglu / kEpiBf16 with FP8 weights (the Q* codes and S* row
+// scales of GroupedParams).
+enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3, kEpiSwiglu8 = 4,
+                kEpiBf16_8 = 5 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 }  // namespace moe

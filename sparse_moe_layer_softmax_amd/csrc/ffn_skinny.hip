@@ -25,16 +25,6 @@
 namespace moe {
 namespace {
 
-// Eight E4M3 codes (two dwords, code 0 in the low byte) -> the eight bf16 of one MFMA operand.
-__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
-  u32x4_t r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
-  return r;
-}
-
 // Weight loads bypass cache retention: each weight line is read once per launch.
 constexpr bool kWeightNT = true;
 

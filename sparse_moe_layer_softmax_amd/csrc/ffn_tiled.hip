@@ -56,6 +56,7 @@ constexpr int kStages = 2;
 constexpr int kXcds = 8;
 constexpr int kBand = 8;
 constexpr int kStageA = kBM * kBK, kStageB = kTN * kBK;  // bf16 elements per stage
+constexpr int kStageB8 = kTN * kBK;                      // bytes per FP8 weight stage
 constexpr size_t kSmem = sizeof(uint16_t) * kStages * (kStageA + kStageB);
 constexpr int kDmaB = kTN / 8 / 8;  // weight-tile DMA instructions per wavefront per K-tile
 
@@ -108,11 +109,13 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
 template <int EPI, int MIV>
 __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1,
                                            int kb, int nk, int split) {
-  constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd;
+  constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;  // FP8 weights
+  constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sA = smem;                      // [2][320][64]
-  uint16_t* sB = smem + kStages * kStageA;  // [2][256][64]
+  uint16_t* sB = smem + kStages * kStageA;  // [2][256][64] bf16, or [2][256][64] bytes (W8)
+  uint8_t* sB8 = reinterpret_cast<uint8_t*>(sB);
   const int Kd = p.Kd;
   const int tid = threadIdx.x;
   // wavefront index as a scalar: the LDS destinations of the DMA (M0) are then pure SALU math
@@ -142,30 +145,49 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   const uint16_t* W0 = g < p.g_split ? p.W0a + g * wst : p.W0b + (g - p.g_split) * wst;
   const uint16_t* W1 = W0;
   if (GATED) W1 = g < p.g_split ? p.W1a + g * wst : p.W1b + (g - p.g_split) * wst;
+  // weight-tile row b (0..255) -> weight matrix row; gated: the wavefront with quarter q holds
+  // h columns nb*128 + q*32 + [0,32), its fragment 0 the gate rows, fragment 1 the up rows
+  auto wrow = [&](int b) { return GATED ? nb * 128 + (b >> 6) * 32 + (b & 31) : nb * kTN + b; };
   const uint16_t* bsrc[kDmaB];
+  if (!W8) {
 #pragma unroll
-  for (int i = 0; i < kDmaB; ++i) {
-    const int b = (wave + 8 * i) * 8 + lrow;  // weight-tile row 0..255
-    int row;
-    const uint16_t* Wm = W0;
-    if (GATED) {
-      // the wavefront with quarter q holds h columns nb*128 + q*32 + [0,32): its fragment 0 is
-      // the gate rows, fragment 1 the matching up rows
-      row = nb * 128 + (b >> 6) * 32 + (b & 31);
-      Wm = (b >> 5) & 1 ? W1 : W0;
-    } else {
-      row = nb * kTN + b;
+    for (int i = 0; i < kDmaB; ++i) {
+      const int b = (wave + 8 * i) * 8 + lrow;
+      const uint16_t* Wm = GATED && ((b >> 5) & 1) ? W1 : W0;
+      bsrc[i] = Wm + static_cast<size_t>(wrow(b)) * Kd + kb * kBK + lchunk * 8;
     }
-    bsrc[i] = Wm + static_cast<size_t>(row) * Kd + kb * kBK + lchunk * 8;
+  }
+  // W8: a B stage is [256 rows][64 codes]; a 1 KB DMA block holds 16 rows. Lane i fills row
+  // i/4 of the block, physical 16-byte chunk i%4, which holds logical chunk
+  // (i%4) ^ ((row / 4) % 4); wavefront w fills blocks w + 8i, i < 2.
+  const uint8_t* bsrc8[2];
+  if (W8) {
+    const uint8_t* Q0 = g < p.g_split ? p.Q0a + g * wst : p.Q0b + (g - p.g_split) * wst;
+    const uint8_t* Q1 = Q0;
+    if (GATED) Q1 = g < p.g_split ? p.Q1a + g * wst : p.Q1b + (g - p.g_split) * wst;
+    const int lc8 = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int b = (wave + 8 * i) * 16 + (lane >> 2);
+      const uint8_t* Qm = GATED && ((b >> 5) & 1) ? Q1 : Q0;
+      bsrc8[i] = Qm + static_cast<size_t>(wrow(b)) * Kd + kb * kBK + lc8 * 16;
+    }
   }
   auto dma_tile = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
       lds_dma16(p.A + aoff[i] + kt * kBK,
                 sA + stage * kStageA + (20 * half + quarter + 4 * i) * 512);
+    if (W8) {
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i)
-      lds_dma16<true>(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
+      for (int i = 0; i < 2; ++i)
+        lds_dma16<true>(reinterpret_cast<const uint16_t*>(bsrc8[i] + kt * kBK),
+                        reinterpret_cast<uint16_t*>(sB8 + stage * kStageB8 + (wave + 8 * i) * 1024));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kDmaB; ++i)
+        lds_dma16<true>(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
+    }
   };
 
   f32x16_t acc[MV][2];
@@ -180,9 +202,15 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // LDS offset of this lane's fragment row fr at 16-wide K-step ks inside a 32-row-aligned
   // block: the swizzle term depends only on fr (row bases are multiples of 32), so one offset
   // per K-step serves every fragment and stage.
+  // W8 takes a different one-to-one assignment of K elements to lanes, the same for A and B:
+  // K-step ks of slice h reads elements 32h + 16q + 8ks + [0, 8) (q = lane / 32), so that one
+  // 16-byte LDS read returns a lane's codes for both K-steps of the slice.
   int lds_off[kBK / 16];
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) lds_off[ks] = swz(fr, ks * 16 + fk);
+  for (int ks = 0; ks < kBK / 16; ++ks)
+    lds_off[ks] = W8 ? swz(fr, 32 * (ks >> 1) + 2 * fk + 8 * (ks & 1)) : swz(fr, ks * 16 + fk);
+  // W8 B read: row quarter*64 + 32j + fr, logical chunk 2h + q of the 64-byte row
+  const int boff8 = ((fr >> 2) & 3);
   u32x4_t af[2][MV], bf[2][2];
   // fragments of the 32-wide K slice h of a stage
   auto fetch = [&](int stage, int h) {
@@ -193,10 +221,21 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       af[0][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h]]);
       af[1][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h + 1]]);
     }
+    if (W8) {
+      const uint8_t* b8 = sB8 + stage * kStageB8 + quarter * 64 * 64;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      bf[0][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h]]);
-      bf[1][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h + 1]]);
+      for (int j = 0; j < 2; ++j) {
+        const u32x4_t c = *reinterpret_cast<const u32x4_t*>(
+            b8 + (j * 32 + fr) * 64 + (((2 * h + (lane >> 5)) ^ boff8) << 4));
+        bf[0][j] = e4m3x8_to_bf16(c[0], c[1]);
+        bf[1][j] = e4m3x8_to_bf16(c[2], c[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf[0][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h]]);
+        bf[1][j] = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h + 1]]);
+      }
     }
   };
 
@@ -244,6 +283,25 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
 
   // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
   const int rbase = r0 + half * 160;
+  if (W8) {  // per-row weight scales of this lane's two columns multiply the fp32 sums
+    const size_t so = static_cast<size_t>(g < p.g_split ? g : g - p.g_split) * p.N;
+    const float* S0 = (g < p.g_split ? p.S0a : p.S0b) + so;
+    const float* S1 = GATED ? (g < p.g_split ? p.S1a : p.S1b) + so : S0;
+    float sc[2];
+    if (GATED) {
+      sc[0] = S0[nb * 128 + quarter * 32 + fr];
+      sc[1] = S1[nb * 128 + quarter * 32 + fr];
+    } else {
+      sc[0] = S0[nb * kTN + quarter * 64 + fr];
+      sc[1] = S0[nb * kTN + quarter * 64 + 32 + fr];
+    }
+#pragma unroll
+    for (int i = 0; i < MIV; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] *= sc[j];
+  }
   if (EPI == kEpiF32) {
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
@@ -409,6 +467,8 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
   switch (epi) {
     case kEpiSwiglu: return tiled_launch<kEpiSwiglu>(p, p.N / 128, max_tiles, stream);
     case kEpiSwigluBwd: return tiled_launch<kEpiSwigluBwd>(p, p.N / 128, max_tiles, stream);
+    case kEpiSwiglu8: return tiled_launch<kEpiSwiglu8>(p, p.N / 128, max_tiles, stream);
+    case kEpiBf16_8: return tiled_launch<kEpiBf16_8>(p, p.N / kTN, max_tiles, stream);
     case kEpiBf16: return tiled_launch<kEpiBf16>(p, p.N / kTN, max_tiles, stream);
     default: return tiled_launch<kEpiF32>(p, p.N / kTN, max_tiles, stream);
   }

@@ -44,6 +44,17 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Eight OCP E4M3 codes (two dwords, code 0 in the low byte) -> the eight bf16 of one MFMA
+// operand. Exact: every E4M3 value is a bf16 value (the gfx950 scaled convert, scale 1).
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return r;
+}
+
 // silu(clamp(g)) * clamp(u): the SwiGLU activation with swiglu_limit applied to both
 // pre-activations (limit <= 0 disables the clamp).
 __device__ __forceinline__ float clamped_swiglu(float g, float u, float limit) {

@@ -85,10 +85,14 @@ WORKLOADS = {
     "dense_ffn_t8192_h6144_i18432": Workload(
         "dense_ffn_t8192_h6144_i18432", T=8192, H=6144, E=1, K=1, I=18432, n_shared=0, scale=1.0,
         limit=10.0, w_std=0.006, router_std=0.006, seed=6),
-    # the decode batch with FP8 expert weights (the pages' deployment checkpoint is FP8)
+    # the decode and prefill batches with FP8 expert weights (the pages' deployment checkpoint is
+    # FP8)
     "hy4_decode_t64_fp8": Workload(
         "hy4_decode_t64_fp8", T=64, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
         w_std=0.006, router_std=0.006, seed=5, fp8=True),
+    "hy4_prefill_t8192_fp8": Workload(
+        "hy4_prefill_t8192_fp8", T=8192, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, seed=7, fp8=True),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

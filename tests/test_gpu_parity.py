@@ -312,7 +312,7 @@ def test_moe_combine(name):
 
 # ----------------------------------------------------------------------------- full sizes, sampled
 FULL = ["hy4_decode_t64", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2", "hy4_skew_t65536",
-        "hy4_decode_t64_fp8", "dense_ffn_t8192_h6144_i18432"]
+        "hy4_decode_t64_fp8", "dense_ffn_t8192_h6144_i18432", "hy4_prefill_t8192_fp8"]
 
 
 @pytest.mark.timeout(600)
