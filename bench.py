@@ -213,11 +213,13 @@ def main():
     gu_s = phase_ms["gate_up_gemm"] / 1e3
     dn_s = phase_ms["down_gemm"] / 1e3
     rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s)
-    # the tiled MFMA kernel takes bf16 weights with at least 64 rows per group on average; FP8
-    # weights always stream through the skinny kernel
-    tiled = not wl.fp8 and wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
-    kname = ("ffn_tiled_kernel<kEpiSwiglu>" if tiled else
-             "ffn_skinny_kernel<true, %s>" % ("true" if wl.fp8 else "false"))
+    # the tiled MFMA kernel runs when the groups hold at least 64 rows each on average (bf16 or
+    # FP8 weights alike); below that the weights stream through the skinny kernel
+    tiled = wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
+    if tiled:
+        kname = "ffn_tiled_kernel<%s>" % ("kEpiSwiglu8" if wl.fp8 else "kEpiSwiglu")
+    else:
+        kname = "ffn_skinny_kernel<true, %s>" % ("true" if wl.fp8 else "false")
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
