@@ -23,19 +23,36 @@ __global__ __launch_bounds__(256) void build_tiles_kernel(const int32_t* __restr
                                                           int G, int bm, int max_tiles,
                                                           int32_t* __restrict__ tiles) {
   __shared__ int base[1025];
-  // G <= 1024 groups; ntiles per group then an exclusive scan (one thread, fixed order)
-  for (int g = threadIdx.x; g < G; g += blockDim.x) {
-    const int n = offsets[g + 1] - offsets[g];
-    base[g] = n > 0 ? (n + bm - 1) / bm : 0;
+  __shared__ int wsum[4];
+  // G <= 1024 groups, four consecutive ones per thread: tiles per group, then an exclusive
+  // integer scan (lanes by shuffles, wavefronts through LDS)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int n4[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    const int n = g < G ? offsets[g + 1] - offsets[g] : 0;
+    n4[i] = n > 0 ? (n + bm - 1) / bm : 0;
+    sum += n4[i];
   }
+  int inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[w] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int g = 0; g < G; ++g) {
-      const int c = base[g];
-      base[g] = acc;
-      acc += c;
-    }
+  int b = inc - sum;
+  for (int j = 0; j < w; ++j) b += wsum[j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    if (g < G) base[g] = b;
+    b += n4[i];
+  }
+  if (tid == 0) {
+    const int acc = wsum[0] + wsum[1] + wsum[2] + wsum[3];
     base[G] = acc;
     tiles[0] = acc < max_tiles ? acc : max_tiles;
   }

@@ -57,6 +57,7 @@ constexpr int kXcds = 8;
 constexpr int kBand = 8;
 constexpr int kStageA = kBM * kBK, kStageB = kTN * kBK;  // bf16 elements per stage
 constexpr int kStageB8 = kTN * kBK;                      // bytes per FP8 weight stage
+constexpr int kStagesB8 = 3;  // FP8 weight stages: K-tile kt+2 is fetched during K-tile kt
 constexpr size_t kSmem = sizeof(uint16_t) * kStages * (kStageA + kStageB);
 constexpr int kDmaB = kTN / 8 / 8;  // weight-tile DMA instructions per wavefront per K-tile
 
@@ -112,6 +113,9 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;  // FP8 weights
   constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
+  // DMA instructions of this wavefront that may still be in flight when a K-tile's operands
+  // must have landed: FP8 weight tiles run one K-tile further ahead (the next-but-one tile's)
+  constexpr int kLead = W8 ? 2 : 0;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   uint16_t* sA = smem;                      // [2][320][64]
   uint16_t* sB = smem + kStages * kStageA;  // [2][256][64] bf16, or [2][256][64] bytes (W8)
@@ -173,11 +177,13 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       bsrc8[i] = Qm + static_cast<size_t>(wrow(b)) * Kd + kb * kBK + lc8 * 16;
     }
   }
-  auto dma_tile = [&](int kt, int stage) {
+  auto dma_a = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
       lds_dma16(p.A + aoff[i] + kt * kBK,
                 sA + stage * kStageA + (20 * half + quarter + 4 * i) * 512);
+  };
+  auto dma_b = [&](int kt, int stage) {
     if (W8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -213,7 +219,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   const int boff8 = ((fr >> 2) & 3);
   u32x4_t af[2][MV], bf[2][2];
   // fragments of the 32-wide K slice h of a stage
-  auto fetch = [&](int stage, int h) {
+  auto fetch = [&](int stage, int bstage, int h) {
     const uint16_t* a = sA + stage * kStageA + half * 160 * kBK;
     const uint16_t* b = sB + stage * kStageB + quarter * 64 * kBK;
 #pragma unroll
@@ -222,7 +228,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       af[1][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h + 1]]);
     }
     if (W8) {
-      const uint8_t* b8 = sB8 + stage * kStageB8 + quarter * 64 * 64;
+      const uint8_t* b8 = sB8 + bstage * kStageB8 + quarter * 64 * 64;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4_t c = *reinterpret_cast<const u32x4_t*>(
@@ -250,17 +256,23 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // last K-tile into the free stage (never read). Every wavefront passes 2 + 4*nk barriers.
   // nk == 0 (an empty K range, uniform over the workgroup): no DMA, no barrier, zero result
   if (nk > 0) {
-    dma_tile(0, 0);
-    wait_vmcnt<0>();
+    dma_a(0, 0);
+    dma_b(0, 0);
+    if (W8) dma_b(min(1, nk - 1), 1);
+    wait_vmcnt<kLead>();
     barrier_no_fence();
     if (half == 1) barrier_no_fence();
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         // ---- memory phase
-        if (MIV > 0) fetch(kt & 1, h);
-        if (h == 0) dma_tile(min(kt + 1, nk - 1), (kt + 1) & 1);
-        if (half == 1 && h == 1) wait_vmcnt<0>();
+        if (MIV > 0) fetch(kt & 1, W8 ? kt % kStagesB8 : kt & 1, h);
+        if (h == 0) {
+          dma_a(min(kt + 1, nk - 1), (kt + 1) & 1);
+          if (W8) dma_b(min(kt + 2, nk - 1), (kt + 2) % kStagesB8);
+          else dma_b(min(kt + 1, nk - 1), (kt + 1) & 1);
+        }
+        if (half == 1 && h == 1) wait_vmcnt<kLead>();
         wait_lgkmcnt0();
         barrier_no_fence();
         // ---- compute phase
@@ -274,7 +286,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
               for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
           __builtin_amdgcn_s_setprio(0);
         }
-        if (half == 0 && h == 1) wait_vmcnt<0>();
+        if (half == 0 && h == 1) wait_vmcnt<kLead>();
         barrier_no_fence();
       }
     }

@@ -84,28 +84,55 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const size_t plane = static_cast<size_t>(T) * E;
+  // each lane sums the S partials of its experts e = lane + 64q in split order; the loads of a
+  // batch of 16 splits for all four experts are issued together so their latencies overlap
+  // (lanes past E read expert 0's column and discard it)
+  // (-0 + p == p for every p, so starting from -0 keeps the split-order sum exact)
+  const float* src[4];
   float v[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = lane + 64 * q;
-    v[q] = -FLT_MAX;
+    src[q] = part + static_cast<size_t>(t) * E + (e < E ? e : 0);
+    v[q] = -0.f;
+  }
+  int z = 0;
+  for (; z + 16 <= S; z += 16) {
+    float pz[4][16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 16; ++u) pz[q][u] = src[q][(z + u) * plane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[q] += pz[q][u];
+  }
+  for (; z + 4 <= S; z += 4) {
+    float pz[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) pz[q][u] = src[q][(z + u) * plane];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[q] += pz[q][u];
+  }
+  for (; z < S; ++z)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += src[q][z * plane];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
     if (e < E) {
-      const float* src = part + static_cast<size_t>(t) * E + e;
-      // partials in split order; loads batched 8 at a time so their latencies overlap
-      float s = src[0];
-      int z = 1;
-      for (; z + 8 <= S; z += 8) {
-        float pz[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pz[u] = src[(z + u) * plane];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) s += pz[u];
-      }
-      for (; z < S; ++z) s += src[z * plane];
+      float s = v[q];
       if (bias) s += bias[e];
       if (noise) s += noise[static_cast<size_t>(t) * E + e];
       v[q] = s;
       if (logits) logits[static_cast<size_t>(t) * E + e] = s;
+    } else {
+      v[q] = -FLT_MAX;
     }
   }
   // k rounds of wavefront arg-max. Lane j keeps the j-th selection.

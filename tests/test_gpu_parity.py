@@ -188,8 +188,11 @@ def test_moe_route(name):
     assert torch.equal(idx2, idx) and torch.equal(w2, w)
 
 
+# up to 1024 slots one single-wavefront launch does the dispatch, above it three launches; the
+# cases cover both forms, their boundary (1024 and 1040 slots) and capacity drops in each
 @pytest.mark.parametrize("T,K,E,C", [(128, 2, 32, 0), (130, 8, 256, 0), (1, 8, 256, 0),
-                                     (200, 2, 8, 30), (4096, 2, 32, 320), (65536, 8, 256, 0),
+                                     (200, 2, 8, 30), (64, 8, 256, 0), (128, 8, 256, 3),
+                                     (512, 2, 16, 40), (4096, 2, 32, 320), (65536, 8, 256, 0),
                                      (40000, 8, 256, 1200)])
 def test_moe_permute(T, K, E, C):
     _require_gpu()
