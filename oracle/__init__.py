@@ -14,7 +14,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "moe_oracle.cpp"), os.path.join(_HERE, "moe_oracle_bwd.cpp")]
+_SRCS = [os.path.join(_HERE, "moe_oracle.cpp"), os.path.join(_HERE, "moe_oracle_bwd.cpp"),
+         os.path.join(_HERE, "moe_oracle_w8a8.cpp")]
 _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 _lib = None
 
@@ -75,6 +76,12 @@ def _declare(L):
     L.oracle_router_bwd.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _D, _P]
     L.oracle_layer_backward.argtypes = [_I] * 6 + [_D, _D, _I] + [_P] * 16 + [_D] + [_P] * 15
     L.oracle_num_threads.restype = _I
+    L.oracle_e4m3_from_float_array.argtypes = [ctypes.c_long, _P, _P]
+    L.oracle_quant_rows_e4m3.argtypes = [_I, _I, _P, _P, _P]
+    L.oracle_gateup_rows_w8a8.argtypes = [_I, _I, _I, _D] + [_P] * 7
+    L.oracle_down_rows_w8a8.argtypes = [_I, _I, _I] + [_P] * 5
+    L.oracle_layer_forward_w8a8.argtypes = ([_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 15 + [_I]
+                                            + [_P] * 14)
 
 
 def _ptr(a):
@@ -334,6 +341,87 @@ def layer_dense_fp8(x, wg: Fp8, wu: Fp8, wd: Fp8, topk_idx, topk_w, slot_to_row,
     lib().oracle_layer_dense_fp8(T, H, E, K, I, float(limit), _ptr(x), *_fp8_ptrs(wg, wu, wd, sg, su, sd),
                                  _ptr(topk_idx), _ptr(topk_w), _ptr(slot_to_row), _ptr(out))
     return out
+
+
+# ------------------------------------------------------- FP8 weights and FP8 activations (W8A8)
+def e4m3_from_float(q):
+    """Nearest-even OCP E4M3 codes (uint8) of float32 values, saturating at +-448."""
+    q = np.ascontiguousarray(np.asarray(q, dtype=np.float32))
+    out = np.zeros(q.shape, dtype=np.uint8)
+    if q.size:
+        lib().oracle_e4m3_from_float_array(q.size, _ptr(q), _ptr(out))
+    return out
+
+
+def quant_rows_e4m3(v):
+    """Per-row dynamic E4M3 quantisation of bf16 rows [rows, cols] -> (codes uint8 [rows, cols],
+    scales float32 [rows]); value ~= scale * e4m3(code)."""
+    v = _u16(v)
+    rows, cols = v.shape
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros(rows, dtype=np.float32)
+    if rows:
+        lib().oracle_quant_rows_e4m3(rows, cols, _ptr(v), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def gateup_rows_w8a8(xq, sx, wg: Fp8, wu: Fp8, limit):
+    xq = np.ascontiguousarray(np.asarray(xq, dtype=np.uint8))
+    sx = _f32(sx)
+    n, H = xq.shape
+    I = wg.q.shape[0]
+    h = np.zeros((n, I), dtype=np.uint16)
+    if n:
+        lib().oracle_gateup_rows_w8a8(n, H, I, float(limit), _ptr(xq), _ptr(sx), _ptr(wg.q),
+                                      _ptr(wg.scale), _ptr(wu.q), _ptr(wu.scale), _ptr(h))
+    return h
+
+
+def down_rows_w8a8(hq, sh, wd: Fp8):
+    hq = np.ascontiguousarray(np.asarray(hq, dtype=np.uint8))
+    sh = _f32(sh)
+    n, I = hq.shape
+    H = wd.q.shape[0]
+    y = np.zeros((n, H), dtype=np.uint16)
+    if n:
+        lib().oracle_down_rows_w8a8(n, H, I, _ptr(hq), _ptr(sh), _ptr(wd.q), _ptr(wd.scale), _ptr(y))
+    return y
+
+
+def layer_forward_w8a8(x, wr, wg: Fp8, wu: Fp8, wd: Fp8, K, *, bias=None, sg=None, su=None,
+                       sd=None, scale=1.0, limit=10.0, capacity=0, norm_topk=True, logits=None):
+    """layer_forward_fp8 with the activations of each expert projection quantised per row to
+    E4M3; returns the same dict plus the quantised input (xq, x_scale)."""
+    x, wr = _u16(x), _u16(wr)
+    T, H = x.shape
+    E, I = wg.q.shape[0], wg.q.shape[1]
+    use_logits = logits is not None
+    lg = _f32(logits).copy() if use_logits else np.zeros((T, E), dtype=np.float32)
+    r = dict(
+        logits=lg,
+        topk_idx=np.zeros((T, K), dtype=np.int32),
+        topk_w=np.zeros((T, K), dtype=np.float32),
+        counts=np.zeros(E, dtype=np.int32),
+        offsets=np.zeros(E + 1, dtype=np.int32),
+        row_to_slot=np.zeros(T * K, dtype=np.int32),
+        slot_to_row=np.zeros(T * K, dtype=np.int32),
+        xq=np.zeros((T, H), dtype=np.uint8),
+        x_scale=np.zeros(T, dtype=np.float32),
+        h_routed=np.zeros((T * K, I), dtype=np.uint16),
+        y_routed=np.zeros((T * K, H), dtype=np.uint16),
+        out=np.zeros((T, H), dtype=np.uint16),
+    )
+    if sg is not None:
+        r["h_shared"] = np.zeros((T, I), dtype=np.uint16)
+        r["y_shared"] = np.zeros((T, H), dtype=np.uint16)
+    lib().oracle_layer_forward_w8a8(
+        T, H, E, K, I, int(bool(norm_topk)), float(scale), float(limit), int(capacity),
+        _ptr(x), _ptr(wr), _ptr(_f32(bias)), *_fp8_ptrs(wg, wu, wd, sg, su, sd), int(use_logits),
+        _ptr(lg), _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+        _ptr(r["row_to_slot"]), _ptr(r["slot_to_row"]), _ptr(r["xq"]), _ptr(r["x_scale"]),
+        _ptr(r["h_routed"]), _ptr(r["y_routed"]), _ptr(r.get("h_shared")), _ptr(r.get("y_shared")),
+        _ptr(r["out"]))
+    return r
 
 
 # ---------------------------------------------------------------------------- training side

@@ -147,6 +147,29 @@ void oracle_layer_dense_fp8(int T, int H, int E, int K, int I, double limit, con
                             const int32_t* topk_idx, const float* topk_w,
                             const int32_t* slot_to_row, uint16_t* out);
 
+// ---- FP8 weights and FP8 activations (W8A8), moe_oracle_w8a8.cpp. Per-row dynamic E4M3
+// quantisation of the activations entering each expert projection; see that file's header.
+uint8_t oracle_e4m3_from_float(float q);
+void oracle_e4m3_from_float_array(long n, const float* q, uint8_t* codes);
+void oracle_quant_rows_e4m3(int rows, int cols, const uint16_t* v, uint8_t* codes, float* scales);
+void oracle_gateup_rows_w8a8(int n, int H, int I, double limit, const uint8_t* xq,
+                             const float* sx, const uint8_t* qg, const float* cg,
+                             const uint8_t* qu, const float* cu, uint16_t* h);
+void oracle_down_rows_w8a8(int n, int H, int I, const uint8_t* hq, const float* sh,
+                           const uint8_t* qd, const float* cd, uint16_t* y);
+void oracle_layer_forward_w8a8(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                               double limit, int capacity, const uint16_t* x,
+                               const uint16_t* wr, const float* bias, const uint8_t* qg,
+                               const float* cg, const uint8_t* qu, const float* cu,
+                               const uint8_t* qd, const float* cd, const uint8_t* sqg,
+                               const float* scg, const uint8_t* squ, const float* scu,
+                               const uint8_t* sqd, const float* scd, int use_logits,
+                               float* logits, int32_t* topk_idx, float* topk_w,
+                               int32_t* counts, int32_t* offsets, int32_t* row_to_slot,
+                               int32_t* slot_to_row, uint8_t* xq, float* sx,
+                               uint16_t* h_routed, uint16_t* y_routed, uint16_t* h_shared,
+                               uint16_t* y_shared, uint16_t* out);
+
 /* Training-side router statistics (Hy3 deep-dive, SparseMoERouter training branch and its
  * load-balancing loss): from fp32 logits [T,E] (bias and noise already added) and the top-k
  * indices [T,K]:
