@@ -21,6 +21,7 @@ import time
 METRIC = "MoE-layer tokens/s at Hy4 shape; % of bf16 MFMA or HBM roofline"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_MFMA_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s (the W8A8 expert products)
 
 
 def parse():
@@ -53,21 +54,23 @@ def algorithmic(wl, counts):
     layer_bytes = (touched + S) * (w_gu + w_dn) + 2 * E * H + 2 * 2 * T * H + 4 * T * E + 8 * T * K
     # gate/up grouped GEMM launch: its weights, x in, h out
     gu_flops = 4 * H * I * (R + S * T)
-    gu_bytes = (touched + S) * w_gu + 2 * T * H + 2 * (R + S * T) * I
+    # activations read by the projections: bf16, or E4M3 codes plus one fp32 scale per row
+    a_x, a_h = (T * (H + 4), (R + S * T) * (I + 4)) if wl.act_fp8 else (2 * T * H, 2 * (R + S * T) * I)
+    gu_bytes = (touched + S) * w_gu + a_x + 2 * (R + S * T) * I
     # down grouped GEMM launch: its weights, h in, y out
     dn_flops = 2 * H * I * (R + S * T)
-    dn_bytes = (touched + S) * w_dn + 2 * (R + S * T) * I + 2 * (R + S * T) * H
+    dn_bytes = (touched + S) * w_dn + a_h + 2 * (R + S * T) * H
     return dict(R=R, touched=touched, layer_flops=layer_flops, layer_bytes=layer_bytes,
                 gu_flops=gu_flops, gu_bytes=gu_bytes, dn_flops=dn_flops, dn_bytes=dn_bytes)
 
 
-def roofline(flops, nbytes, seconds):
+def roofline(flops, nbytes, seconds, peak_mfma=PEAK_MFMA_TFLOPS):
     ai = flops / nbytes
-    ridge = PEAK_MFMA_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ridge = peak_mfma * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ai >= ridge:
         a = flops / seconds / 1e12
-        return dict(bound="mfma", achieved=round(a, 2), peak=PEAK_MFMA_TFLOPS, unit="TFLOP/s",
-                    frac=round(a / PEAK_MFMA_TFLOPS, 4))
+        return dict(bound="mfma", achieved=round(a, 2), peak=peak_mfma, unit="TFLOP/s",
+                    frac=round(a / peak_mfma, 4))
     a = nbytes / seconds / 1e9
     return dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                 frac=round(a / PEAK_HBM_GBS, 4))
@@ -119,7 +122,14 @@ def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
             return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
         return as_u16(t)
 
-    ffn = oracle.expert_ffn_rows_fp8 if wl.fp8 else oracle.expert_ffn_rows
+    def ffn_w8a8(x_rows, wg, wu, wd, limit):
+        xq, sx = oracle.quant_rows_e4m3(x_rows)
+        h = oracle.gateup_rows_w8a8(xq, sx, wg, wu, limit)
+        hq, sh = oracle.quant_rows_e4m3(h)
+        return h, oracle.down_rows_w8a8(hq, sh, wd)
+
+    ffn = (ffn_w8a8 if wl.act_fp8 else
+           oracle.expert_ffn_rows_fp8 if wl.fp8 else oracle.expert_ffn_rows)
     W = {e: tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down")) for e in experts}
     SW = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
     reps = 0
@@ -218,12 +228,16 @@ def main():
     alg = algorithmic(wl, counts)
     gu_s = phase_ms["gate_up_gemm"] / 1e3
     dn_s = phase_ms["down_gemm"] / 1e3
-    rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s)
+    peak_mfma = PEAK_MFMA_FP8_TFLOPS if wl.act_fp8 else PEAK_MFMA_TFLOPS
+    rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s, peak_mfma)
     # the tiled MFMA kernel runs when the groups hold at least 64 rows each on average (bf16 or
     # FP8 weights alike); below that the weights stream through the skinny kernel
     tiled = wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
     if tiled:
-        kname = "ffn_tiled_kernel<%s>" % ("kEpiSwiglu8" if wl.fp8 else "kEpiSwiglu")
+        kname = "ffn_tiled_kernel<%s>" % ("kEpiSwiglu88" if wl.act_fp8 else
+                                          "kEpiSwiglu8" if wl.fp8 else "kEpiSwiglu")
+    elif wl.act_fp8:
+        kname = "ffn_skinny_kernel<true, true, true>"
     else:
         kname = "ffn_skinny_kernel<true, %s>" % ("true" if wl.fp8 else "false")
     rf["traffic"] = recorded_traffic(wl.name, kname)
@@ -243,21 +257,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8_e4m3" if wl.act_fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I,
                    "n_shared": wl.n_shared, "routed_scaling": wl.scale, "swiglu_limit": wl.limit,
                    "capacity": wl.capacity, "parallelism": "none (1 GPU)",
-                   "expert_weights": "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16"},
+                   "expert_weights": "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16",
+                   "expert_activations": ("fp8_e4m3 + fp32 row scale (dynamic)" if wl.act_fp8
+                                          else "bf16")},
         "roofline": rf,
         "layer": {"algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"],
                   "hbm_GBs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
                   "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS, 4),
                   "mfma_TFLOPs": round(alg["layer_flops"] / layer_s / 1e12, 2),
-                  "mfma_frac": round(alg["layer_flops"] / layer_s / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                  "mfma_frac": round(alg["layer_flops"] / layer_s / 1e12 / peak_mfma, 4),
                   "routed_rows": alg["R"], "touched_experts": alg["touched"],
                   "max_rows_per_expert": int(counts.max())},
-        "down_gemm": roofline(alg["dn_flops"], alg["dn_bytes"], dn_s),
+        "down_gemm": roofline(alg["dn_flops"], alg["dn_bytes"], dn_s, peak_mfma),
         "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
     }
     if not args.no_cpu_baseline:

@@ -246,6 +246,49 @@ int moe_layer_forward_fp8(const moe_shape* shape, const uint16_t* x, const uint1
                           const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
                           hipStream_t stream, hipEvent_t const* phase_events);
 
+/* ---------------------------------------------------------------- FP8 activations too (W8A8)
+ * The same FP8 deployment (the pages name an FP8 checkpoint and no format), with the FP8
+ * matrix cores doing the products: the activations entering each expert projection are also
+ * OCP E4M3, quantised per row on the fly (dynamic, one fp32 scale per row):
+ *   amax = max_c |v[c]|,  scale = amax / 448,  code[c] = E4M3_RNE(clamp(v[c] * (448 / amax), +-448))
+ * with both divisions correctly rounded fp32 and the product one fp32 multiply; an all-zero row
+ * gets scale 1 and zero codes. A projection is then
+ *   (sum_k e4m3(a_code[k]) * e4m3(w_code[k])) * w_scale[col] * a_scale[row]
+ * with the code products summed in fp32, rounded where the bf16 path rounds (h, y, out).
+ *
+ * moe_quantize_rows_e4m3: that quantisation on its own.
+ *   x [rows, cols] bf16 (16-byte aligned),  codes [rows, cols] uint8 (8-byte aligned),
+ *   scales [rows] fp32;  rows >= 1, cols a positive multiple of 8.
+ * Returns MOE_ERR_INVALID_ARG for a NULL pointer, bad sizes or bad alignment.              */
+int moe_quantize_rows_e4m3(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes,
+                           float* scales, hipStream_t stream);
+
+/* moe_layer_forward_w8a8: moe_layer_forward_fp8 (same arguments, same outputs) in the W8A8 form:
+ * x is quantised once per token (the shared expert reads the same codes) before the gate/up
+ * projections, and the h rows once each before the down projections. The router and the
+ * combine stay as in the bf16 layer.
+ * ws: moe_layer_w8a8_workspace_size(shape) bytes, 256-byte aligned. Its first part has the
+ * layout moe_layer_workspace_layout gives; the quantised activations follow at the offsets
+ * moe_layer_w8a8_workspace_layout gives, readable after the stream completes.              */
+typedef struct moe_layer_a8_ws_layout {
+  size_t xq;      /* [T,H] E4M3 codes of x                                        */
+  size_t x_scale; /* [T] fp32                                                     */
+  size_t hq;      /* [T + T*K, I] E4M3 codes of h, rows as in h (valid rows only) */
+  size_t h_scale; /* [T + T*K] fp32                                               */
+  size_t total;   /* bytes of the whole workspace                                 */
+} moe_layer_a8_ws_layout;
+
+size_t moe_layer_w8a8_workspace_size(const moe_shape* shape);
+int moe_layer_w8a8_workspace_layout(const moe_shape* shape, moe_layer_a8_ws_layout* layout);
+int moe_layer_forward_w8a8(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                           const float* bias, const uint8_t* w_gate, const float* w_gate_scale,
+                           const uint8_t* w_up, const float* w_up_scale, const uint8_t* w_down,
+                           const float* w_down_scale, const uint8_t* s_gate,
+                           const float* s_gate_scale, const uint8_t* s_up,
+                           const float* s_up_scale, const uint8_t* s_down,
+                           const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t const* phase_events);
+
 /* ================================================================ backward pass (training)
  * The routers on the pages are trained (Hy3 deep-dive `SparseMoERouter`: training branch with a
  * load-balancing loss and count EMAs; Hy4 deep-dive `MoERouter`: noise on the scores in

@@ -28,7 +28,8 @@ EXPORTED = (
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "moe_layer_forward",
     "moe_layer_forward_profiled", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
     "moe_route_train_workspace_size", "moe_route_train", "moe_layer_backward_workspace_size",
-    "moe_layer_backward_workspace_layout", "moe_layer_backward",
+    "moe_layer_backward_workspace_layout", "moe_layer_backward", "moe_quantize_rows_e4m3",
+    "moe_layer_w8a8_workspace_size", "moe_layer_w8a8_workspace_layout", "moe_layer_forward_w8a8",
 )
 MOE_LAYER_PHASE_EVENTS = 7
 
@@ -49,6 +50,10 @@ class moe_shape(ctypes.Structure):
 class moe_layer_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("logits", "topk_w", "topk_idx", "counts", "offsets",
                                                "row_to_slot", "slot_to_row", "h", "y", "total")]
+
+
+class moe_layer_a8_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("xq", "x_scale", "hq", "h_scale", "total")]
 
 
 class moe_bwd_ws_layout(ctypes.Structure):
@@ -108,6 +113,10 @@ def _load():
         "moe_layer_backward": ([sp] + [P] * 9 + [S, P, ctypes.c_float] + [P] * 10 + [P, S, P],
                                ctypes.c_int),
         "moe_layer_forward_fp8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
+        "moe_quantize_rows_e4m3": ([P, I32, I32, P, P, P], ctypes.c_int),
+        "moe_layer_w8a8_workspace_size": ([sp], S),
+        "moe_layer_w8a8_workspace_layout": ([sp, ctypes.POINTER(moe_layer_a8_ws_layout)], ctypes.c_int),
+        "moe_layer_forward_w8a8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -285,6 +294,36 @@ def moe_layer_forward_fp8(shape: Shape, x, w_router, bias, w_gate, w_gate_scale,
         "moe_layer_forward_fp8")
 
 
+def moe_quantize_rows_e4m3(x, codes, scales, stream=None):
+    """Per-row dynamic E4M3 quantisation: x [rows, cols] bf16 -> codes uint8, scales fp32 [rows]."""
+    rows, cols = x.shape
+    _check(library().moe_quantize_rows_e4m3(_p(x), rows, cols, _p(codes), _p(scales),
+                                            _stream(stream)), "moe_quantize_rows_e4m3")
+
+
+def moe_layer_w8a8_workspace_size(shape: Shape) -> int:
+    return library().moe_layer_w8a8_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_layer_w8a8_workspace_layout(shape: Shape) -> dict:
+    lay = moe_layer_a8_ws_layout()
+    _check(library().moe_layer_w8a8_workspace_layout(ctypes.byref(shape.c()), ctypes.byref(lay)),
+           "moe_layer_w8a8_workspace_layout")
+    return {n: getattr(lay, n) for n, _ in moe_layer_a8_ws_layout._fields_}
+
+
+def moe_layer_forward_w8a8(shape: Shape, x, w_router, bias, w_gate, w_gate_scale, w_up, w_up_scale,
+                           w_down, w_down_scale, s_gate, s_gate_scale, s_up, s_up_scale, s_down,
+                           s_down_scale, out, ws, phase_events=None, stream=None):
+    """moe_layer_forward_fp8 with the expert activations quantised per row to E4M3 (W8A8)."""
+    _check(library().moe_layer_forward_w8a8(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_gate_scale),
+        _p(w_up), _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(s_gate), _p(s_gate_scale),
+        _p(s_up), _p(s_up_scale), _p(s_down), _p(s_down_scale), _p(out), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream), phase_events),
+        "moe_layer_forward_w8a8")
+
+
 # ----------------------------------------------------------------------------- conveniences
 _WEIGHTS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 
@@ -292,10 +331,11 @@ _WEIGHTS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 class MoELayer:
     """Holds device weights and a workspace; ``forward(x)`` runs moe_layer_forward (bf16 expert
     weights) or moe_layer_forward_fp8 (uint8 E4M3 expert weights; ``scales`` then maps each weight
-    name of _WEIGHTS to its fp32 per-row scale tensor)."""
+    name of _WEIGHTS to its fp32 per-row scale tensor); with ``act_fp8`` (FP8 weights only)
+    moe_layer_forward_w8a8, which quantises the expert activations per row as well."""
 
     def __init__(self, shape: Shape, w_router, w_gate, w_up, w_down, s_gate=None, s_up=None,
-                 s_down=None, router_bias=None, scales=None):
+                 s_down=None, router_bias=None, scales=None, act_fp8=False):
         self.shape = shape
         self.w = (w_router, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
         self.fp8 = w_gate.dtype == torch.uint8
@@ -304,16 +344,24 @@ class MoELayer:
             for n, t in zip(_WEIGHTS, (w_gate, w_up, w_down, s_gate, s_up, s_down)):
                 if t is not None and self.scales.get(n) is None:
                     raise ValueError("FP8 weight %s needs a scale tensor" % n)
+        if act_fp8 and not self.fp8:
+            raise ValueError("FP8 activations come with FP8 expert weights")
+        self.act_fp8 = act_fp8
         self.device = w_router.device
-        self.ws = _ws(moe_layer_workspace_size(shape), self.device)
         self.layout = moe_layer_workspace_layout(shape)
+        if act_fp8:
+            self.layout.update({k: v for k, v in moe_layer_w8a8_workspace_layout(shape).items()
+                                if k != "total"})
+            self.ws = _ws(moe_layer_w8a8_workspace_size(shape), self.device)
+        else:
+            self.ws = _ws(moe_layer_workspace_size(shape), self.device)
 
     @classmethod
     def from_inputs(cls, shape: Shape, d: dict):
         """Build from a ``workloads.generate`` dict (bf16 or FP8 expert weights)."""
         scales = {n: d.get(n + "_scale") for n in _WEIGHTS}
         return cls(shape, d["w_router"], d["w_gate"], d["w_up"], d["w_down"], d["s_gate"], d["s_up"],
-                   d["s_down"], d["router_bias"], scales=scales)
+                   d["s_down"], d["router_bias"], scales=scales, act_fp8=bool(d.get("act_fp8")))
 
     def forward(self, x, out=None, stream=None, phase_events=None):
         if out is None:
@@ -322,9 +370,10 @@ class MoELayer:
         self._x = x
         if self.fp8:
             sc = self.scales
-            moe_layer_forward_fp8(self.shape, x, wr, b, wg, sc["w_gate"], wu, sc["w_up"], wd,
-                                  sc["w_down"], sg, sc.get("s_gate"), su, sc.get("s_up"), sd,
-                                  sc.get("s_down"), out, self.ws, phase_events, stream)
+            fwd = moe_layer_forward_w8a8 if self.act_fp8 else moe_layer_forward_fp8
+            fwd(self.shape, x, wr, b, wg, sc["w_gate"], wu, sc["w_up"], wd, sc["w_down"], sg,
+                sc.get("s_gate"), su, sc.get("s_up"), sd, sc.get("s_down"), out, self.ws,
+                phase_events, stream)
         elif phase_events is not None:
             moe_layer_forward_profiled(self.shape, x, wr, b, wg, wu, wd, sg, su, sd, out, self.ws,
                                        phase_events, stream)

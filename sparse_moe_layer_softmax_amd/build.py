@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 SOURCES = ["route.hip", "router_train.hip", "permute.hip", "ffn.hip", "ffn_skinny.hip", "ffn_tiled.hip",
-           "backward.hip",
+           "backward.hip", "quant.hip",
            "combine.hip", "api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

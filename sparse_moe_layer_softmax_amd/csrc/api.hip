@@ -188,9 +188,30 @@ int expert_ffn_impl(const moe_shape* s, int32_t n_groups, int32_t rows_max, cons
   return hip_status(moe::launch_ffn(p, stream));
 }
 
+// The W8A8 workspace: the layer's own layout, then the quantised activations.
+struct A8Ws {
+  moe_layer_a8_ws_layout pub;
+};
+A8Ws a8_ws(const moe_shape& s) {
+  A8Ws w{};
+  const size_t rows = static_cast<size_t>(s.T) * s.K + (s.n_shared ? s.T : 0);
+  size_t o = layer_ws(s).pub.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  w.pub.xq = take(static_cast<size_t>(s.T) * s.H);
+  w.pub.x_scale = take(sizeof(float) * s.T);
+  w.pub.hq = take(rows * s.I);
+  w.pub.h_scale = take(sizeof(float) * rows);
+  w.pub.total = o;
+  return w;
+}
+
 int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, const float* bias,
                const Weights& routed, const Weights& shared_w, uint16_t* out, void* ws,
-               size_t ws_bytes, hipStream_t stream, hipEvent_t const* ev) {
+               size_t ws_bytes, hipStream_t stream, hipEvent_t const* ev, bool a8 = false) {
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
@@ -202,7 +223,8 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
   if (!shared && !shared_w.empty()) return MOE_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(out) & 15u) return MOE_ERR_INVALID_ARG;
   const LayerWs w = layer_ws(*s);
-  if (ws_bytes < w.pub.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  const A8Ws wa = a8_ws(*s);
+  if (ws_bytes < (a8 ? wa.pub.total : w.pub.total) || !aligned(ws)) return MOE_ERR_WORKSPACE;
 
   float* logits = reinterpret_cast<float*>(at(ws, w.pub.logits));
   float* topk_w = reinterpret_cast<float*>(at(ws, w.pub.topk_w));
@@ -253,6 +275,13 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
   p.h = h;
   p.y = y;
   p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  if (a8) {
+    p.a8 = true;
+    p.xq = reinterpret_cast<uint8_t*>(at(ws, wa.pub.xq));
+    p.sx = reinterpret_cast<float*>(at(ws, wa.pub.x_scale));
+    p.hq = reinterpret_cast<uint8_t*>(at(ws, wa.pub.hq));
+    p.sh = reinterpret_cast<float*>(at(ws, wa.pub.h_scale));
+  }
   rc = hip_status(moe::launch_ffn(p, stream, ev ? ev + 3 : nullptr));
   if (rc != MOE_OK) return rc;
 
@@ -447,6 +476,41 @@ int moe_layer_forward_fp8(const moe_shape* s, const uint16_t* x, const uint16_t*
                     Weights::fp8(w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale),
                     Weights::fp8(s_gate, s_gate_scale, s_up, s_up_scale, s_down, s_down_scale),
                     out, ws, ws_bytes, stream, ev);
+}
+
+int moe_quantize_rows_e4m3(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes,
+                           float* scales, hipStream_t stream) {
+  if (!x || !codes || !scales || rows < 1 || cols < 8 || cols % 8) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(codes) & 7u))
+    return MOE_ERR_INVALID_ARG;  // 16-byte loads, 8-byte stores
+  return hip_status(moe::launch_quant_rows(x, rows, cols, nullptr, codes, scales, stream));
+}
+
+size_t moe_layer_w8a8_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return a8_ws(*s).pub.total;
+}
+
+int moe_layer_w8a8_workspace_layout(const moe_shape* s, moe_layer_a8_ws_layout* layout) {
+  int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  *layout = a8_ws(*s).pub;
+  return MOE_OK;
+}
+
+int moe_layer_forward_w8a8(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                           const float* bias, const uint8_t* w_gate, const float* w_gate_scale,
+                           const uint8_t* w_up, const float* w_up_scale, const uint8_t* w_down,
+                           const float* w_down_scale, const uint8_t* s_gate,
+                           const float* s_gate_scale, const uint8_t* s_up,
+                           const float* s_up_scale, const uint8_t* s_down,
+                           const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream, hipEvent_t const* ev) {
+  return layer_impl(s, x, w_router, bias,
+                    Weights::fp8(w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale),
+                    Weights::fp8(s_gate, s_gate_scale, s_up, s_up_scale, s_down, s_down_scale),
+                    out, ws, ws_bytes, stream, ev, true);
 }
 
 namespace {

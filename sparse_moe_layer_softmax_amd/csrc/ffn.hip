@@ -119,8 +119,15 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.g_split = q.g_split;
   p.limit = q.limit;
 
-  // gate/up + clamped SwiGLU -> h
-  p.A = q.x;
+  // gate/up + clamped SwiGLU -> h. W8A8: x quantised per row first; the tiled kernel then
+  // moves the codes as pairs (Kd = H / 2), the skinny kernel reads them as bytes.
+  hipError_t e = hipSuccess;
+  if (q.a8) {
+    e = launch_quant_rows(q.x, q.T, q.H, nullptr, q.xq, q.sx, stream);
+    if (e != hipSuccess) return e;
+  }
+  p.A = q.a8 ? reinterpret_cast<const uint16_t*>(q.xq) : q.x;
+  p.a_scale = q.sx;
   p.a_rows = q.T;
   p.W0a = q.gate_a;
   p.W0b = q.gate_b;
@@ -134,16 +141,30 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.S0b = q.sgate_b;
   p.S1a = q.sup_a;
   p.S1b = q.sup_b;
+  if (q.a8) {  // the codes take the bf16 weights' places
+    p.W0a = reinterpret_cast<const uint16_t*>(q.qgate_a);
+    p.W0b = reinterpret_cast<const uint16_t*>(q.qgate_b);
+    p.W1a = reinterpret_cast<const uint16_t*>(q.qup_a);
+    p.W1b = reinterpret_cast<const uint16_t*>(q.qup_b);
+  }
   p.out = q.h;
   p.N = q.I;
-  p.Kd = q.H;
-  hipError_t e = tiled ? launch_tiled(q.w8 ? kEpiSwiglu8 : kEpiSwiglu, p, max_tiles, stream)
-                       : launch_skinny(true, q.w8, p, max_tiles, stream);
+  p.Kd = q.a8 && tiled ? q.H / 2 : q.H;
+  if (tiled)
+    e = launch_tiled(q.a8 ? kEpiSwiglu88 : (q.w8 ? kEpiSwiglu8 : kEpiSwiglu), p, max_tiles, stream);
+  else
+    e = launch_skinny(true, q.w8, q.a8, p, max_tiles, stream);
   if (e != hipSuccess) return e;
   mark(1);
 
-  // down -> y (h rows are already in row order: identity gather)
-  p.A = q.h;
+  // down -> y (h rows are already in row order: identity gather); W8A8: the valid h rows
+  // (offsets[G] of them) quantised per row first
+  if (q.a8) {
+    e = launch_quant_rows(q.h, q.rows_max, q.I, q.offsets + q.n_groups, q.hq, q.sh, stream);
+    if (e != hipSuccess) return e;
+  }
+  p.A = q.a8 ? reinterpret_cast<const uint16_t*>(q.hq) : q.h;
+  p.a_scale = q.sh;
   p.a_rows = q.rows_max;
   p.n_ident = 0x7fffffff;
   p.gather = nullptr;
@@ -156,11 +177,17 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.S0a = q.sdown_a;
   p.S0b = q.sdown_b;
   p.S1a = p.S1b = nullptr;
+  if (q.a8) {
+    p.W0a = reinterpret_cast<const uint16_t*>(q.qdown_a);
+    p.W0b = reinterpret_cast<const uint16_t*>(q.qdown_b);
+  }
   p.out = q.y;
   p.N = q.H;
-  p.Kd = q.I;
-  e = tiled ? launch_tiled(q.w8 ? kEpiBf16_8 : kEpiBf16, p, max_tiles, stream)
-            : launch_skinny(false, q.w8, p, max_tiles, stream);
+  p.Kd = q.a8 && tiled ? q.I / 2 : q.I;
+  if (tiled)
+    e = launch_tiled(q.a8 ? kEpiBf16_88 : (q.w8 ? kEpiBf16_8 : kEpiBf16), p, max_tiles, stream);
+  else
+    e = launch_skinny(false, q.w8, q.a8, p, max_tiles, stream);
   if (e != hipSuccess) return e;
   mark(2);
   return hipGetLastError();

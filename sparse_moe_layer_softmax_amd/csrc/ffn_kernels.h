@@ -44,14 +44,18 @@ struct GroupedParams {
   // splits >= g_split go to out_f32_b (at split - g_split)
   const int32_t* k_tiles;
   float* out_f32_b;
+  // FP8 activations (W8A8): A holds E4M3 codes, one fp32 scale per A row (indexed like A's rows)
+  const float* a_scale;
 };
 
 
 // Weight-streaming kernel for few rows per group (ffn_skinny.hip): row tiles of kSkinnyRows.
 constexpr int kSkinnyRows = 64;
 // gated: gate/up + SwiGLU over N = I columns (64 per workgroup); else down (128 per workgroup).
-// w8: the weights are the FP8 Q*/S* operands.
-hipError_t launch_skinny(bool gated, bool w8, const GroupedParams& p, int max_tiles, hipStream_t stream);
+// w8: the weights are the FP8 Q*/S* operands. a8 (with w8): A holds E4M3 codes [rows, Kd] with
+// one fp32 scale per row in a_scale.
+hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
+                         hipStream_t stream);
 
 // LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
 constexpr int kTiledRows = 320;
@@ -59,8 +63,12 @@ constexpr int kTiledRows = 320;
 // (the clamped SwiGLU's derivative) into out [rows, 2N] as [dg | du].
 // kEpiSwiglu8 / kEpiBf16_8: kEpiSwiglu / kEpiBf16 with FP8 weights (the Q* codes and S* row
 // scales of GroupedParams).
+// kEpiSwiglu88 / kEpiBf16_88: FP8 weights and FP8 activations (W8A8): A and W0*/W1* hold E4M3
+// codes, Kd counts pairs of codes (K / 2, so the byte tiles move exactly as bf16 tiles do), the
+// products run on the FP8 MFMA, and the S* weight-row scales times a_scale of the row multiply
+// the fp32 sums.
 enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3, kEpiSwiglu8 = 4,
-                kEpiBf16_8 = 5 };
+                kEpiBf16_8 = 5, kEpiSwiglu88 = 6, kEpiBf16_88 = 7 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 }  // namespace moe

@@ -59,9 +59,10 @@ __device__ __forceinline__ void exchange_line(const LineRaw& w, u32x4_t& f0, u32
   }
 }
 
-template <bool GATED, int NS, bool W8>
+template <bool GATED, int NS, bool W8, bool A8>
 __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r0, int r1,
                                             int col0) {
+  static_assert(!A8 || W8, "FP8 activations come with FP8 weights");
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
   const int lk = W8 ? (lane >> 4) * 16 : (lane >> 4) * 8;  // this lane's first K element
@@ -76,6 +77,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
   // already reads) and mask it to zero, rather than a fixed row that every workgroup would hit
   const int src0 = max(source(r0), 0);
   const uint16_t* ap[NS];
+  const uint8_t* ap8[NS];  // A8: this lane's codes of each row (lk is then a byte offset too)
   bool av[NS];
   u32x4_t am[NS];  // all ones for rows of the tile, zero past it
 #pragma unroll
@@ -91,6 +93,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
       }
     }
     ap[s] = p.A + static_cast<size_t>(src) * Kd + lk;
+    ap8[s] = reinterpret_cast<const uint8_t*>(p.A) + static_cast<size_t>(src) * Kd + lk;
     const uint32_t m = av[s] ? ~0u : 0u;
     am[s] = u32x4_t{m, m, m, m};
   }
@@ -157,14 +160,25 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
     // activations at the same K elements as the weight operands of MFMA u; rows past the tile
     // read a valid row and are masked to zero, so the loads need no branch
     u32x4_t aa[NS][U];
+    if (A8) {  // 16 codes per load: elements 16g + 64c + [0, 16) feed MFMAs 2c and 2c + 1
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+      for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ko = W8 ? 64 * (u >> 1) + 8 * (u & 1) : 32 * u;
-        const u32x4_t t = ld16(ap[s] + k + ko);
-        aa[s][u] = t & am[s];
-      }
+        for (int c = 0; c < 2; ++c) {
+          const u32x4_t t = *reinterpret_cast<const u32x4_t*>(ap8[s] + k + 64 * c);
+          aa[s][2 * c] = e4m3x8_to_bf16(t[0], t[1]) & am[s];
+          aa[s][2 * c + 1] = e4m3x8_to_bf16(t[2], t[3]) & am[s];
+        }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int ko = W8 ? 64 * (u >> 1) + 8 * (u & 1) : 32 * u;
+          const u32x4_t t = ld16(ap[s] + k + ko);
+          aa[s][u] = t & am[s];
+        }
+    }
     u32x4_t f0[2 * LN], f1[2 * LN];  // [2 * line + half]: chunk G (half 0) or G + 4 (half 1)
 #pragma unroll
     for (int ln = 0; ln < LN; ++ln) {
@@ -212,8 +226,14 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
       const int r = r0 + 16 * s + 4 * (lane >> 4) + v;
       if (r < r1) {
         uint16_t* o = p.out + static_cast<size_t>(r) * p.N;
-        const float a0 = W8 ? acc0[s][v] * sc0 : acc0[s][v];
-        const float a1 = W8 ? acc1[s][v] * sc1 : acc1[s][v];
+        float a0 = W8 ? acc0[s][v] * sc0 : acc0[s][v];
+        float a1 = W8 ? acc1[s][v] * sc1 : acc1[s][v];
+        if (A8) {  // the activation row's scale (rows of the tile hold their own source row)
+          const int sr = source(r);
+          const float sa = sr >= 0 ? p.a_scale[sr] : 0.f;
+          a0 *= sa;
+          a1 *= sa;
+        }
         if (GATED) {
           o[col0 + lr] = f32_to_bf16(clamped_swiglu(a0, a1, p.limit));
         } else {
@@ -224,7 +244,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
     }
 }
 
-template <bool GATED, bool W8>
+template <bool GATED, bool W8, bool A8 = false>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
   const int tile = blockIdx.x;
   if (tile >= p.tiles[0]) return;
@@ -235,10 +255,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
   const int wave = threadIdx.x >> 6;
   const int col0 = GATED ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
   switch ((r1 - r0 + 15) >> 4) {
-    case 1: skinny_tile<GATED, 1, W8>(p, g, r0, r1, col0); break;
-    case 2: skinny_tile<GATED, 2, W8>(p, g, r0, r1, col0); break;
-    case 3: skinny_tile<GATED, 3, W8>(p, g, r0, r1, col0); break;
-    case 4: skinny_tile<GATED, 4, W8>(p, g, r0, r1, col0); break;
+    case 1: skinny_tile<GATED, 1, W8, A8>(p, g, r0, r1, col0); break;
+    case 2: skinny_tile<GATED, 2, W8, A8>(p, g, r0, r1, col0); break;
+    case 3: skinny_tile<GATED, 3, W8, A8>(p, g, r0, r1, col0); break;
+    case 4: skinny_tile<GATED, 4, W8, A8>(p, g, r0, r1, col0); break;
     default: break;
   }
 }
@@ -246,9 +266,14 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
 
 }  // namespace
 
-hipError_t launch_skinny(bool gated, bool w8, const GroupedParams& p, int max_tiles, hipStream_t stream) {
+hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
+                         hipStream_t stream) {
   const dim3 grid(max_tiles, gated ? p.N / 64 : p.N / 128);
-  if (gated && w8)
+  if (a8 && gated)
+    hipLaunchKernelGGL((ffn_skinny_kernel<true, true, true>), grid, dim3(256), 0, stream, p);
+  else if (a8)
+    hipLaunchKernelGGL((ffn_skinny_kernel<false, true, true>), grid, dim3(256), 0, stream, p);
+  else if (gated && w8)
     hipLaunchKernelGGL((ffn_skinny_kernel<true, true>), grid, dim3(256), 0, stream, p);
   else if (gated)
     hipLaunchKernelGGL((ffn_skinny_kernel<true, false>), grid, dim3(256), 0, stream, p);

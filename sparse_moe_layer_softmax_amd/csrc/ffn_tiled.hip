@@ -58,7 +58,8 @@ constexpr int kBand = 8;
 constexpr int kStageA = kBM * kBK, kStageB = kTN * kBK;  // bf16 elements per stage
 constexpr int kStageB8 = kTN * kBK;                      // bytes per FP8 weight stage
 constexpr int kStagesB8 = 3;  // FP8 weight stages: K-tile kt+2 is fetched during K-tile kt
-constexpr size_t kSmem = sizeof(uint16_t) * kStages * (kStageA + kStageB);
+constexpr size_t kSmemRing = sizeof(uint16_t) * kStages * (kStageA + kStageB);
+constexpr size_t kSmem = kSmemRing + sizeof(float) * kBM;  // + W8A8 row scales of the tile
 constexpr int kDmaB = kTN / 8 / 8;  // weight-tile DMA instructions per wavefront per K-tile
 
 // LDS element offset of (row, k) in a [rows][64] bf16 stage. The eight 16-byte chunks of a row
@@ -110,8 +111,10 @@ __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
 template <int EPI, int MIV>
 __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1,
                                            int kb, int nk, int split) {
-  constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;  // FP8 weights
-  constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8;
+  constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;     // FP8 weights, bf16 activations
+  constexpr bool A8 = EPI == kEpiSwiglu88 || EPI == kEpiBf16_88;  // FP8 weights and activations
+  constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8 ||
+                         EPI == kEpiSwiglu88;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   // DMA instructions of this wavefront that may still be in flight when a K-tile's operands
   // must have landed: FP8 weight tiles run one K-tile further ahead (the next-but-one tile's)
@@ -126,6 +129,20 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = wave >> 2;    // rows 160*half .. +160 of the tile; also the ping-pong group
   const int quarter = wave & 3;  // weight rows 64*quarter .. +64 of the tile
+  if constexpr (A8) {  // the activation-row scale of every tile row (0 past the group's end)
+    float* srow = reinterpret_cast<float*>(smem + kSmemRing / sizeof(uint16_t));
+    if (tid < kBM) {
+      const int r = r0 + tid;
+      float sa = 0.f;
+      if (r < r1) {
+        int src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
+        if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) src = 0;
+        sa = p.a_scale[src];
+      }
+      srow[tid] = sa;
+    }
+    __syncthreads();
+  }
 
   // ---- DMA assignment. A 1 KB block holds 8 rows of 64 elements; lane i fills its 16-byte slot
   // i: row i/8 of the block, physical chunk i%8, which holds the logical chunk that swz() places
@@ -152,13 +169,16 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // weight-tile row b (0..255) -> weight matrix row; gated: the wavefront with quarter q holds
   // h columns nb*128 + q*32 + [0,32), its fragment 0 the gate rows, fragment 1 the up rows
   auto wrow = [&](int b) { return GATED ? nb * 128 + (b >> 6) * 32 + (b & 31) : nb * kTN + b; };
-  const uint16_t* bsrc[kDmaB];
+  // the weight rows a wavefront moves all come from one matrix: block w + 8i holds tile rows
+  // 8(w + 8i) .. +8, whose 32-row fragment index is (w >> 2) + 2i, so for gate/up the half of
+  // the wavefront picks gate (0) or up (1). A uniform base and 32-bit offsets then address them.
+  const uint16_t* Wb = GATED && half ? W1 : W0;
+  uint32_t boff[kDmaB];
   if (!W8) {
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
       const int b = (wave + 8 * i) * 8 + lrow;
-      const uint16_t* Wm = GATED && ((b >> 5) & 1) ? W1 : W0;
-      bsrc[i] = Wm + static_cast<size_t>(wrow(b)) * Kd + kb * kBK + lchunk * 8;
+      boff[i] = static_cast<uint32_t>(wrow(b)) * Kd + kb * kBK + lchunk * 8;
     }
   }
   // W8: a B stage is [256 rows][64 codes]; a 1 KB DMA block holds 16 rows. Lane i fills row
@@ -192,7 +212,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     } else {
 #pragma unroll
       for (int i = 0; i < kDmaB; ++i)
-        lds_dma16<true>(bsrc[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
+        lds_dma16<true>(Wb + boff[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
     }
   };
 
@@ -218,10 +238,24 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // W8 B read: row quarter*64 + 32j + fr, logical chunk 2h + q of the 64-byte row
   const int boff8 = ((fr >> 2) & 3);
   u32x4_t af[2][MV], bf[2][2];
+  u32x8_t af8[MV], bf8[2];  // W8A8: one 32-code operand per fragment, its two 16-byte halves
   // fragments of the 32-wide K slice h of a stage
   auto fetch = [&](int stage, int bstage, int h) {
     const uint16_t* a = sA + stage * kStageA + half * 160 * kBK;
     const uint16_t* b = sB + stage * kStageB + quarter * 64 * kBK;
+    if constexpr (A8) {
+#pragma unroll
+      for (int i = 0; i < MIV; ++i) {
+        af8[i].lo = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h]]);
+        af8[i].hi = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h + 1]]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf8[j].lo = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h]]);
+        bf8[j].hi = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h + 1]]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < MIV; ++i) {
       af[0][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h]]);
@@ -262,32 +296,47 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     wait_vmcnt<kLead>();
     barrier_no_fence();
     if (half == 1) barrier_no_fence();
-    for (int kt = 0; kt < nk; ++kt) {
+    // one memory phase and one compute phase of 32-wide K slice h of K-tile kt
+    auto phase = [&](int kt, int h) {
+      // ---- memory phase
+      if (MIV > 0) fetch(kt & 1, W8 ? kt % kStagesB8 : kt & 1, h);
+      if (h == 0) {
+        dma_a(min(kt + 1, nk - 1), (kt + 1) & 1);
+        if (W8) dma_b(min(kt + 2, nk - 1), (kt + 2) % kStagesB8);
+        else dma_b(min(kt + 1, nk - 1), (kt + 1) & 1);
+      }
+      if (half == 1 && h == 1) wait_vmcnt<kLead>();
+      wait_lgkmcnt0();
+      barrier_no_fence();
+      // ---- compute phase
+      if (MIV > 0) {
+        __builtin_amdgcn_s_setprio(1);
+        if constexpr (A8) {  // one FP8 MFMA covers the slice's 64 codes
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // ---- memory phase
-        if (MIV > 0) fetch(kt & 1, W8 ? kt % kStagesB8 : kt & 1, h);
-        if (h == 0) {
-          dma_a(min(kt + 1, nk - 1), (kt + 1) & 1);
-          if (W8) dma_b(min(kt + 2, nk - 1), (kt + 2) % kStagesB8);
-          else dma_b(min(kt + 1, nk - 1), (kt + 1) & 1);
-        }
-        if (half == 1 && h == 1) wait_vmcnt<kLead>();
-        wait_lgkmcnt0();
-        barrier_no_fence();
-        // ---- compute phase
-        if (MIV > 0) {
-          __builtin_amdgcn_s_setprio(1);
+          for (int i = 0; i < MIV; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x64_fp8(af8[i], bf8[j], acc[i][j]);
+        } else {
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < MIV; ++i)
 #pragma unroll
-              for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
-          __builtin_amdgcn_s_setprio(0);
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = mfma32x32x16(af[ks][i], bf[ks][j], acc[i][j]);
         }
-        if (half == 0 && h == 1) wait_vmcnt<kLead>();
-        barrier_no_fence();
+        __builtin_amdgcn_s_setprio(0);
+      }
+      if (half == 0 && h == 1) wait_vmcnt<kLead>();
+      barrier_no_fence();
+    };
+    for (int kt = 0; kt < nk; ++kt) {
+      if constexpr (A8) {  // not unrolled: keeps the FP8 operands within the registers
+#pragma clang loop unroll(disable)
+        for (int h = 0; h < 2; ++h) phase(kt, h);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) phase(kt, h);
       }
     }
     if (half == 0) barrier_no_fence();
@@ -295,7 +344,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
 
   // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
   const int rbase = r0 + half * 160;
-  if (W8) {  // per-row weight scales of this lane's two columns multiply the fp32 sums
+  if (W8 || A8) {  // per-row weight scales of this lane's two columns multiply the fp32 sums
     const size_t so = static_cast<size_t>(g < p.g_split ? g : g - p.g_split) * p.N;
     const float* S0 = (g < p.g_split ? p.S0a : p.S0b) + so;
     const float* S1 = GATED ? (g < p.g_split ? p.S1a : p.S1b) + so : S0;
@@ -366,6 +415,18 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   auto eoff = [&](int row, int col) { return row * C + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7); };
 #pragma unroll
   for (int i = 0; i < MIV; ++i) {
+    if constexpr (A8) {  // the scale of each output row's activation row (staged in LDS)
+      const float* srow = reinterpret_cast<const float*>(smem + kSmemRing / sizeof(uint16_t));
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4_t sa = *reinterpret_cast<const f32x4_t*>(
+            &srow[half * 160 + i * 32 + 8 * g4 + 4 * (lane >> 5)]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j][4 * g4 + k] *= sa[k];
+      }
+    }
     uint16_t* ep = smem + (wave * 2 + (i & 1)) * 32 * C;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
@@ -481,6 +542,8 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
     case kEpiSwigluBwd: return tiled_launch<kEpiSwigluBwd>(p, p.N / 128, max_tiles, stream);
     case kEpiSwiglu8: return tiled_launch<kEpiSwiglu8>(p, p.N / 128, max_tiles, stream);
     case kEpiBf16_8: return tiled_launch<kEpiBf16_8>(p, p.N / kTN, max_tiles, stream);
+    case kEpiSwiglu88: return tiled_launch<kEpiSwiglu88>(p, p.N / 128, max_tiles, stream);
+    case kEpiBf16_88: return tiled_launch<kEpiBf16_88>(p, p.N / kTN, max_tiles, stream);
     case kEpiBf16: return tiled_launch<kEpiBf16>(p, p.N / kTN, max_tiles, stream);
     default: return tiled_launch<kEpiF32>(p, p.N / kTN, max_tiles, stream);
   }

@@ -44,6 +44,20 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
+
+// D(32x32) += A(32x64) * B(64x32) on FP8 E4M3 codes (the gfx950 FP8 MFMA; the block scales it
+// takes are 1.0, E8M0 127). Lane l supplies 32 codes of row l%32 of A and of column l%32 of B,
+// and D is laid out as for mfma32x32x16. The two lane halves and the 32 byte positions each
+// stand for one K index, the same for A and B, so any one-to-one placement of the 64 K values
+// on (lane half, byte) that A and B share gives the same product.
+__device__ __forceinline__ f32x16_t mfma32x32x64_fp8(u32x8_t a, u32x8_t b, f32x16_t c) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8_t, a),
+                                                         __builtin_bit_cast(i32x8_t, b), c, 0, 0,
+                                                         0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
+
 // Eight OCP E4M3 codes (two dwords, code 0 in the low byte) -> the eight bf16 of one MFMA
 // operand. Exact: every E4M3 value is a bf16 value (the gfx950 scaled convert, scale 1).
 __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {

@@ -72,10 +72,22 @@ struct FfnProblem {
   uint16_t* h;                // [rows_max, I]
   uint16_t* y;                // [rows_max, H]
   int32_t* tiles;             // tile table scratch (tile_table_bytes(max_tiles_for(...)))
+  // FP8 activations (a8, with w8): x [T, H] and h [rows_max, I] are quantised per row to E4M3
+  // codes (xq, hq) with one fp32 scale per row (sx, sh) before the projection that reads them
+  bool a8;
+  uint8_t* xq;
+  float* sx;
+  uint8_t* hq;
+  float* sh;
 };
 // ev (may be NULL): three events recorded after the tile table, the gate/up GEMM and the
 // down GEMM (each entry may be NULL).
 hipError_t launch_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t const* ev = nullptr);
+
+// Per-row dynamic E4M3 quantisation (quant.hip): codes [rows, cols], scales [rows]; rows at or
+// past *rows_dev (when given) are left untouched. cols a multiple of 8.
+hipError_t launch_quant_rows(const uint16_t* v, int rows, int cols, const int32_t* rows_dev,
+                             uint8_t* codes, float* scales, hipStream_t stream);
 
 // Dense C[rows, N] (fp32) = A[rows, Kd] . W[N, Kd]^T on the tiled MFMA kernel (router logits
 // at large T). Supported when N == 256 and Kd % 64 == 0. The reduction is split into

@@ -54,6 +54,7 @@ class Workload:
     zipf: float = 0.0           # router bias b_e = zipf * ln(1/(e+1)); 0 = no bias
     seed: int = 0
     fp8: bool = False           # expert weights as FP8 E4M3 codes + per-row fp32 scales
+    act_fp8: bool = False       # with fp8: expert activations quantised per row to E4M3 (W8A8)
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -93,6 +94,17 @@ WORKLOADS = {
     "hy4_prefill_t8192_fp8": Workload(
         "hy4_prefill_t8192_fp8", T=8192, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
         w_std=0.006, router_std=0.006, seed=7, fp8=True),
+    # the same FP8 deployment with the FP8 matrix cores doing the products: activations quantised
+    # per row to E4M3 as well (W8A8)
+    "hy4_decode_t64_w8a8": Workload(
+        "hy4_decode_t64_w8a8", T=64, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, seed=8, fp8=True, act_fp8=True),
+    "hy4_prefill_t8192_w8a8": Workload(
+        "hy4_prefill_t8192_w8a8", T=8192, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, seed=9, fp8=True, act_fp8=True),
+    "hy4_skew_t65536_w8a8": Workload(
+        "hy4_skew_t65536_w8a8", T=65536, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, zipf=1.2, seed=10, fp8=True, act_fp8=True),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -149,6 +161,7 @@ def generate(wl: Workload, device="cpu", shared: bool = True):
             for e in range(wl.E):
                 w[e] = _randn_bf16(shp, wl.w_std, g, dev)
         out[name] = w
+    out["act_fp8"] = wl.act_fp8
     for name, shp in (("s_gate", (wl.I, wl.H)), ("s_up", (wl.I, wl.H)), ("s_down", (wl.H, wl.I))):
         if shared and wl.n_shared:
             g = _gen(wl, name, dev)

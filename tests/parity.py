@@ -154,8 +154,8 @@ def host(wts: dict) -> dict:
     """Host copies (uint16 / float32 numpy) of a generated input dict."""
     out = {}
     for k, v in wts.items():
-        if v is None:
-            out[k] = None
+        if v is None or not isinstance(v, torch.Tensor):
+            out[k] = v
         elif v.dtype == torch.bfloat16:
             out[k] = as_u16(v)
         else:
@@ -186,6 +186,11 @@ def run_layer_gpu(wl, dev: dict):
     y = layer.intermediate("y", torch.int16, (rows, H)).cpu().numpy().view(np.uint16)
     g["h_shared"], g["h_routed"] = (h[:n_id], h[n_id:]) if n_id else (None, h)
     g["y_shared"], g["y_routed"] = (y[:n_id], y[n_id:]) if n_id else (None, y)
+    if layer.act_fp8:  # the quantised activations (W8A8)
+        g["xq"] = layer.intermediate("xq", torch.uint8, (T, H)).cpu().numpy()
+        g["x_scale"] = layer.intermediate("x_scale", torch.float32, (T,)).cpu().numpy()
+        g["hq"] = layer.intermediate("hq", torch.uint8, (rows, I)).cpu().numpy()
+        g["h_scale"] = layer.intermediate("h_scale", torch.float32, (rows,)).cpu().numpy()
     return g, layer, out
 
 
