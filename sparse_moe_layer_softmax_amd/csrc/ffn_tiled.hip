@@ -171,16 +171,13 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   auto wrow = [&](int b) { return GATED ? nb * 128 + (b >> 6) * 32 + (b & 31) : nb * kTN + b; };
   // the weight rows a wavefront moves all come from one matrix: block w + 8i holds tile rows
   // 8(w + 8i) .. +8, whose 32-row fragment index is (w >> 2) + 2i, so for gate/up the half of
-  // the wavefront picks gate (0) or up (1). A uniform base and 32-bit offsets then address them.
+  // the wavefront picks gate (0) or up (1). Block i's weight rows are block 0's plus 32i (gate/up:
+  // wrow(b + 64i) = wrow(b) + 32i) or plus 64i (down), so one 32-bit offset and a uniform step
+  // address all of them.
   const uint16_t* Wb = GATED && half ? W1 : W0;
-  uint32_t boff[kDmaB];
-  if (!W8) {
-#pragma unroll
-    for (int i = 0; i < kDmaB; ++i) {
-      const int b = (wave + 8 * i) * 8 + lrow;
-      boff[i] = static_cast<uint32_t>(wrow(b)) * Kd + kb * kBK + lchunk * 8;
-    }
-  }
+  const size_t bstep = static_cast<size_t>(GATED ? 32 : 64) * Kd;
+  uint32_t boff0 = 0;
+  if (!W8) boff0 = static_cast<uint32_t>(wrow(wave * 8 + lrow)) * Kd + kb * kBK + lchunk * 8;
   // W8: a B stage is [256 rows][64 codes]; a 1 KB DMA block holds 16 rows. Lane i fills row
   // i/4 of the block, physical 16-byte chunk i%4, which holds logical chunk
   // (i%4) ^ ((row / 4) % 4); wavefront w fills blocks w + 8i, i < 2.
@@ -212,7 +209,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     } else {
 #pragma unroll
       for (int i = 0; i < kDmaB; ++i)
-        lds_dma16<true>(Wb + boff[i] + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
+        lds_dma16<true>(Wb + i * bstep + boff0 + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
     }
   };
 
@@ -232,9 +229,11 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // K-step ks of slice h reads elements 32h + 16q + 8ks + [0, 8) (q = lane / 32), so that one
   // 16-byte LDS read returns a lane's codes for both K-steps of the slice.
   int lds_off[kBK / 16];
+  if constexpr (!A8) {
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks)
-    lds_off[ks] = W8 ? swz(fr, 32 * (ks >> 1) + 2 * fk + 8 * (ks & 1)) : swz(fr, ks * 16 + fk);
+    for (int ks = 0; ks < kBK / 16; ++ks)
+      lds_off[ks] = W8 ? swz(fr, 32 * (ks >> 1) + 2 * fk + 8 * (ks & 1)) : swz(fr, ks * 16 + fk);
+  }
   // W8 B read: row quarter*64 + 32j + fr, logical chunk 2h + q of the 64-byte row
   const int boff8 = ((fr >> 2) & 3);
   u32x4_t af[2][MV], bf[2][2];
@@ -244,15 +243,19 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     const uint16_t* a = sA + stage * kStageA + half * 160 * kBK;
     const uint16_t* b = sB + stage * kStageB + quarter * 64 * kBK;
     if constexpr (A8) {
+      // h is not a compile-time constant here (the slice loop is not unrolled): the two offsets
+      // (those of K-steps 2h and 2h + 1) are computed, not looked up in lds_off, whose dynamic
+      // indexing would put it in scratch memory and which would hold four more registers
+      const int o0 = swz(fr, 32 * h + fk), o1 = swz(fr, 32 * h + 16 + fk);
 #pragma unroll
       for (int i = 0; i < MIV; ++i) {
-        af8[i].lo = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h]]);
-        af8[i].hi = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h + 1]]);
+        af8[i].lo = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + o0]);
+        af8[i].hi = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + o1]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bf8[j].lo = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h]]);
-        bf8[j].hi = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + lds_off[2 * h + 1]]);
+        bf8[j].lo = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + o0]);
+        bf8[j].hi = *reinterpret_cast<const u32x4_t*>(&b[j * 32 * kBK + o1]);
       }
       return;
     }

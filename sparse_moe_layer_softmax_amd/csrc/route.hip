@@ -76,6 +76,11 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// BATCH: partial planes whose loads one lane issues together (per expert of its four). Few
+// tokens (decode) leave the GPU mostly idle, so a deep batch hides the load latency within the
+// wavefront; many tokens hide it across wavefronts, and a shallow batch keeps the register
+// count (and so the occupancy) low.
+template <int BATCH>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ part, int S, const float* __restrict__ bias,
     const float* __restrict__ noise, float* __restrict__ logits, float* __restrict__ topk_w, int32_t* __restrict__ topk_idx,
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   if (t >= T) return;
   const size_t plane = static_cast<size_t>(T) * E;
   // each lane sums the S partials of its experts e = lane + 64q in split order; the loads of a
-  // batch of 16 splits for all four experts are issued together so their latencies overlap
+  // batch of BATCH splits for all four experts are issued together so their latencies overlap
   // (lanes past E read expert 0's column and discard it)
   // (-0 + p == p for every p, so starting from -0 keeps the split-order sum exact)
   const float* src[4];
@@ -97,27 +102,16 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     v[q] = -0.f;
   }
   int z = 0;
-  for (; z + 16 <= S; z += 16) {
-    float pz[4][16];
+  for (; z + BATCH <= S; z += BATCH) {
+    float pz[4][BATCH];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) pz[q][u] = src[q][(z + u) * plane];
+      for (int u = 0; u < BATCH; ++u) pz[q][u] = src[q][(z + u) * plane];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) v[q] += pz[q][u];
-  }
-  for (; z + 4 <= S; z += 4) {
-    float pz[4][4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) pz[q][u] = src[q][(z + u) * plane];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) v[q] += pz[q][u];
+      for (int u = 0; u < BATCH; ++u) v[q] += pz[q][u];
   }
   for (; z < S; ++z)
 #pragma unroll
@@ -216,9 +210,14 @@ hipError_t launch_route(const moe_shape& s, const uint16_t* x, const uint16_t* w
     hipLaunchKernelGGL(route_gemm_kernel, g1, dim3(256), 0, stream, x, w_router, partials, s.T,
                        s.H, s.E, s.H / S);
   }
-  hipLaunchKernelGGL(route_topk_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream, partials, S,
-                     bias, noise, logits, topk_w, topk_idx, s.T, s.E, s.K, s.norm_topk_prob,
-                     s.routed_scaling);
+  if (s.T < 1024)
+    hipLaunchKernelGGL(route_topk_kernel<16>, dim3((s.T + 3) / 4), dim3(256), 0, stream, partials,
+                       S, bias, noise, logits, topk_w, topk_idx, s.T, s.E, s.K, s.norm_topk_prob,
+                       s.routed_scaling);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<2>, dim3((s.T + 3) / 4), dim3(256), 0, stream, partials,
+                       S, bias, noise, logits, topk_w, topk_idx, s.T, s.E, s.K, s.norm_topk_prob,
+                       s.routed_scaling);
   return hipGetLastError();
 }
 
