@@ -102,7 +102,8 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA. Both
   // kernels have an FP8-weight form.
   const bool tiled = q.rows_max >= 64 * q.n_groups;
-  const int bm = tiled ? kTiledRows : kSkinnyRows;
+  const bool small = !tiled && q.rows_max <= kSkinnyRowsSmall * q.n_groups;
+  const int bm = tiled ? kTiledRows : (small ? kSkinnyRowsSmall : kSkinnyRows);
   const int max_tiles = max_tiles_for(q.rows_max, q.n_groups, bm);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, q.offsets, q.n_groups, bm,
                      max_tiles, q.tiles);
@@ -153,7 +154,7 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   if (tiled)
     e = launch_tiled(q.a8 ? kEpiSwiglu88 : (q.w8 ? kEpiSwiglu8 : kEpiSwiglu), p, max_tiles, stream);
   else
-    e = launch_skinny(true, q.w8, q.a8, p, max_tiles, stream);
+    e = launch_skinny(true, q.w8, q.a8, p, max_tiles, bm, stream);
   if (e != hipSuccess) return e;
   mark(1);
 
@@ -187,7 +188,7 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   if (tiled)
     e = launch_tiled(q.a8 ? kEpiBf16_88 : (q.w8 ? kEpiBf16_8 : kEpiBf16), p, max_tiles, stream);
   else
-    e = launch_skinny(false, q.w8, q.a8, p, max_tiles, stream);
+    e = launch_skinny(false, q.w8, q.a8, p, max_tiles, bm, stream);
   if (e != hipSuccess) return e;
   mark(2);
   return hipGetLastError();

@@ -49,13 +49,17 @@ struct GroupedParams {
 };
 
 
-// Weight-streaming kernel for few rows per group (ffn_skinny.hip): row tiles of kSkinnyRows.
+// Weight-streaming kernel for few rows per group (ffn_skinny.hip): row tiles of kSkinnyRows, or
+// of kSkinnyRowsSmall when the groups hold at most that many rows on average (decode): a
+// narrower tile lets the kernel run at a higher occupancy, at the price of re-reading the weights
+// of a group once per extra tile.
 constexpr int kSkinnyRows = 64;
+constexpr int kSkinnyRowsSmall = 16;
 // gated: gate/up + SwiGLU over N = I columns (64 per workgroup); else down (128 per workgroup).
 // w8: the weights are the FP8 Q*/S* operands. a8 (with w8): A holds E4M3 codes [rows, Kd] with
 // one fp32 scale per row in a_scale.
 hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
-                         hipStream_t stream);
+                         int tile_rows, hipStream_t stream);
 
 // LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
 constexpr int kTiledRows = 320;

@@ -244,21 +244,24 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
     }
 }
 
-template <bool GATED, bool W8, bool A8 = false>
+// MAXNS: the most 16-row sub-blocks a tile may hold (the tile table's row tile is 16 * MAXNS).
+// The register count follows the largest sub-block count compiled in, so a table of 16-row tiles
+// with MAXNS = 1 runs at several times the occupancy of the 64-row form.
+template <bool GATED, bool W8, bool A8 = false, int MAXNS = 4>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
   const int tile = blockIdx.x;
   if (tile >= p.tiles[0]) return;
   const int g = p.tiles[1 + tile];
   const int r0 = p.tiles[1 + p.max_tiles + tile];
-  const int r1 = min(min(r0 + kSkinnyRows, p.offsets[g + 1]), p.rows_max);
+  const int r1 = min(min(r0 + 16 * MAXNS, p.offsets[g + 1]), p.rows_max);
   if (r0 < 0 || r1 <= r0) return;
   const int wave = threadIdx.x >> 6;
   const int col0 = GATED ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
   switch ((r1 - r0 + 15) >> 4) {
     case 1: skinny_tile<GATED, 1, W8, A8>(p, g, r0, r1, col0); break;
-    case 2: skinny_tile<GATED, 2, W8, A8>(p, g, r0, r1, col0); break;
-    case 3: skinny_tile<GATED, 3, W8, A8>(p, g, r0, r1, col0); break;
-    case 4: skinny_tile<GATED, 4, W8, A8>(p, g, r0, r1, col0); break;
+    case 2: if constexpr (MAXNS >= 2) skinny_tile<GATED, 2, W8, A8>(p, g, r0, r1, col0); break;
+    case 3: if constexpr (MAXNS >= 3) skinny_tile<GATED, 3, W8, A8>(p, g, r0, r1, col0); break;
+    case 4: if constexpr (MAXNS >= 4) skinny_tile<GATED, 4, W8, A8>(p, g, r0, r1, col0); break;
     default: break;
   }
 }
@@ -266,21 +269,30 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
 
 }  // namespace
 
-hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
-                         hipStream_t stream) {
-  const dim3 grid(max_tiles, gated ? p.N / 64 : p.N / 128);
+template <int MAXNS>
+static void skinny_dispatch(bool gated, bool w8, bool a8, const GroupedParams& p, dim3 grid,
+                            hipStream_t stream) {
   if (a8 && gated)
-    hipLaunchKernelGGL((ffn_skinny_kernel<true, true, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ffn_skinny_kernel<true, true, true, MAXNS>), grid, dim3(256), 0, stream, p);
   else if (a8)
-    hipLaunchKernelGGL((ffn_skinny_kernel<false, true, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ffn_skinny_kernel<false, true, true, MAXNS>), grid, dim3(256), 0, stream, p);
   else if (gated && w8)
-    hipLaunchKernelGGL((ffn_skinny_kernel<true, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ffn_skinny_kernel<true, true, false, MAXNS>), grid, dim3(256), 0, stream, p);
   else if (gated)
-    hipLaunchKernelGGL((ffn_skinny_kernel<true, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ffn_skinny_kernel<true, false, false, MAXNS>), grid, dim3(256), 0, stream, p);
   else if (w8)
-    hipLaunchKernelGGL((ffn_skinny_kernel<false, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ffn_skinny_kernel<false, true, false, MAXNS>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((ffn_skinny_kernel<false, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((ffn_skinny_kernel<false, false, false, MAXNS>), grid, dim3(256), 0, stream, p);
+}
+
+hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
+                         int tile_rows, hipStream_t stream) {
+  const dim3 grid(max_tiles, gated ? p.N / 64 : p.N / 128);
+  if (tile_rows == 16)
+    skinny_dispatch<1>(gated, w8, a8, p, grid, stream);
+  else
+    skinny_dispatch<4>(gated, w8, a8, p, grid, stream);
   return hipGetLastError();
 }
 
