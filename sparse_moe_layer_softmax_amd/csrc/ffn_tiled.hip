@@ -367,19 +367,39 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
         for (int v = 0; v < 16; ++v) acc[i][j][v] *= sc[j];
   }
   if (EPI == kEpiF32) {
+    // fp32 results go through LDS so that global stores are whole 16-byte row segments (a
+    // quarter of the store instructions of per-lane 4-byte stores). Each wavefront stages one
+    // 32-row x 64-column fragment row at a time in two private 8 KB buffers of the (now idle)
+    // stage ring, used by alternate fragment rows; the 16-byte chunks are XOR-swizzled by bit 2
+    // of the row, so the two lane halves of a column write (rows 4 apart) use different banks.
+    __syncthreads();  // every DMA has landed and every wavefront left the ring
+    const size_t plane = static_cast<size_t>(p.rows_max) * p.N;
+    float* ob = p.out_f32 + split * plane;
+    if (p.k_tiles && split >= p.g_split) ob = p.out_f32_b + (split - p.g_split) * plane;
+    const int col0 = nb * kTN + quarter * 64;
+    auto foff = [](int row, int col) {
+      return row * 64 + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (col & 3);
+    };
 #pragma unroll
-    for (int i = 0; i < MIV; ++i)
+    for (int i = 0; i < MIV; ++i) {
+      float* ep = reinterpret_cast<float*>(smem) + (wave * 2 + (i & 1)) * 32 * 64;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = rbase + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r >= r1) continue;
-        const size_t plane = static_cast<size_t>(p.rows_max) * p.N;
-        float* ob = p.out_f32 + split * plane;
-        if (p.k_tiles && split >= p.g_split) ob = p.out_f32_b + (split - p.g_split) * plane;
-        float* o = ob + static_cast<size_t>(r) * p.N + nb * kTN + quarter * 64 + fr;
+        const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) o[j * 32] = acc[i][j][v];
+        for (int j = 0; j < 2; ++j) ep[foff(row, j * 32 + fr)] = acc[i][j][v];
       }
+      // the buffers are private to this wavefront and its LDS accesses complete in order
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4);
+        const int ch = lane & 15;
+        const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&ep[foff(row, ch * 4)]);
+        const int r = rbase + i * 32 + row;
+        if (r < r1) *reinterpret_cast<f32x4_t*>(ob + static_cast<size_t>(r) * p.N + col0 + ch * 4) = val;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     return;
   }
   if (EPI == kEpiSwigluBwd) {
