@@ -47,19 +47,34 @@ __global__ __launch_bounds__(256) void ktile_transpose_kernel(
   const int g = tiles[1 + t], r0 = tiles[1 + max_tiles + t];
   const int r_end = min(offsets[g + 1], rows_max);
   const int c0 = blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) {
+  // 16-byte global accesses: thread (a, b) moves columns 8b..8b+8 of tile rows a and a + 32 in,
+  // then elements 8b..8b+8 of output rows a and a + 32 out
+  const int a = threadIdx.x >> 3, b = threadIdx.x & 7;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + a;
     const int r = r0 + i;
-    uint16_t v = 0;
+    u32x4_t v = {0u, 0u, 0u, 0u};
     if (r < r_end) {
       const int sr = gather ? (r < n_ident ? r : gather[r - n_ident] / topk) : r;
-      v = src[static_cast<size_t>(sr) * C + c0 + tx];
+      v = ld16(src + static_cast<size_t>(sr) * C + c0 + 8 * b);
     }
-    tile[i][tx] = v;
+    uint32_t* tp = reinterpret_cast<uint32_t*>(&tile[i][8 * b]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tp[m] = v[m];
   }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4)
-    dst[static_cast<size_t>(c0 + i) * ld_dst + static_cast<size_t>(t) * kKT + tx] = tile[tx][i];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int o = pass * 32 + a;  // output row = source column c0 + o
+    u32x4_t w;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      w[m] = static_cast<uint32_t>(tile[8 * b + 2 * m][o]) |
+             (static_cast<uint32_t>(tile[8 * b + 2 * m + 1][o]) << 16);
+    *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(c0 + o) * ld_dst +
+                                static_cast<size_t>(t) * kKT + 8 * b) = w;
+  }
 }
 
 // kt[2g], kt[2g+1]: first K-tile and K-tile count of group g (the tile table's order).
@@ -124,14 +139,32 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
                                                         size_t src_bstride, int R, int C,
                                                         uint16_t* __restrict__ dst,
                                                         size_t dst_bstride, int dst_ld, int col0) {
+  // 64x64 tiles through LDS (row pitch 66: the column gathers are conflict free), 16-byte
+  // global loads and stores (thread (a, b): columns 8b..8b+8 of rows a and a + 32)
   __shared__ uint16_t tile[64][66];
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const uint16_t* s = src + blockIdx.z * src_bstride;
   uint16_t* d = dst + blockIdx.z * dst_bstride;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int i = ty; i < 64; i += 4) tile[i][tx] = s[static_cast<size_t>(r0 + i) * C + c0 + tx];
+  const int a = threadIdx.x >> 3, b = threadIdx.x & 7;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int i = pass * 32 + a;
+    const u32x4_t v = ld16(s + static_cast<size_t>(r0 + i) * C + c0 + 8 * b);
+    uint32_t* tp = reinterpret_cast<uint32_t*>(&tile[i][8 * b]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tp[m] = v[m];
+  }
   __syncthreads();
-  for (int i = ty; i < 64; i += 4) d[static_cast<size_t>(c0 + i) * dst_ld + col0 + r0 + tx] = tile[tx][i];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int o = pass * 32 + a;
+    u32x4_t w;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      w[m] = static_cast<uint32_t>(tile[8 * b + 2 * m][o]) |
+             (static_cast<uint32_t>(tile[8 * b + 2 * m + 1][o]) << 16);
+    *reinterpret_cast<u32x4_t*>(d + static_cast<size_t>(c0 + o) * dst_ld + col0 + r0 + 8 * b) = w;
+  }
 }
 
 __global__ void zero_i32_kernel(int32_t* p, int n) {
