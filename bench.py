@@ -236,10 +236,13 @@ def main():
     if tiled:
         kname = "ffn_tiled_kernel<%s>" % ("kEpiSwiglu88" if wl.act_fp8 else
                                           "kEpiSwiglu8" if wl.fp8 else "kEpiSwiglu")
-    elif wl.act_fp8:
-        kname = "ffn_skinny_kernel<true, true, true>"
     else:
-        kname = "ffn_skinny_kernel<true, %s>" % ("true" if wl.fp8 else "false")
+        # the weight-streaming kernel: <gated, FP8 weights, FP8 activations, 16-row sub-blocks per
+        # tile>; 16-row tiles (one sub-block) when the groups average at most 16 rows
+        rows = wl.T * wl.K + wl.n_shared * wl.T
+        maxns = 1 if rows <= 16 * (wl.E + wl.n_shared) else 4
+        kname = "ffn_skinny_kernel<true, %s, %s, %d>" % ("true" if wl.fp8 else "false",
+                                                         "true" if wl.act_fp8 else "false", maxns)
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
