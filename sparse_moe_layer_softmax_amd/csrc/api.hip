@@ -516,7 +516,7 @@ int moe_layer_forward_w8a8(const moe_shape* s, const uint16_t* x, const uint16_t
 namespace {
 struct BwdWs {
   size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles_tiled, d_topk_w, d_logits, wdT, wguT;
-  size_t dyT, hT, dguT, xgT, ktiles, kt;
+  size_t dyT, hT, dguT, xgT, ktiles, kt, router_part;
   size_t total;
 };
 BwdWs bwd_ws(const moe_shape& s) {
@@ -549,6 +549,8 @@ BwdWs bwd_ws(const moe_shape& s) {
   w.xgT = take(sizeof(uint16_t) * s.H * ldk);
   w.ktiles = take(moe::tile_table_bytes(mtk));
   w.kt = take(sizeof(int32_t) * 2 * (s.E + s.n_shared));
+  const int rs = moe::router_splits(s.T);
+  w.router_part = take(rs > 1 ? sizeof(float) * rs * static_cast<size_t>(s.E) * s.H : 0);
   w.total = o;
   return w;
 }
@@ -638,6 +640,7 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
   b.xgT = reinterpret_cast<uint16_t*>(at(ws, w.xgT));
   b.ktiles = reinterpret_cast<int32_t*>(at(ws, w.ktiles));
   b.kt = reinterpret_cast<int32_t*>(at(ws, w.kt));
+  b.router_part = reinterpret_cast<float*>(at(ws, w.router_part));
   b.d_topk_w = d_topk_w ? d_topk_w : reinterpret_cast<float*>(at(ws, w.d_topk_w));
   b.d_logits = d_logits ? d_logits : reinterpret_cast<float*>(at(ws, w.d_logits));
   b.d_x = d_x;

@@ -259,21 +259,24 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
 }
 
 // C[M,N] (fp32, row-major) = sum_k A(m,k) B(k,n), A fp32 at A[m*sam + k*sak], B bf16 at
-// B[k*sbk + n*sbn]: the router's small products in fp32. 64x64 tiles, K in steps of 16.
+// B[k*sbk + n*sbn]: the router's small products in fp32. 64x64 tiles, K in steps of 16. With
+// gridDim.z > 1, workgroup z reduces K range [z*kc, z*kc + kc) into plane z of C (M*N each).
 __global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__ A, long sam,
                                                        long sak, const uint16_t* __restrict__ B,
                                                        long sbk, long sbn, int M, int N, int K,
-                                                       float* __restrict__ C) {
+                                                       int kc, float* __restrict__ C) {
   __shared__ float As[16][65], Bs[16][65];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
+  C += static_cast<size_t>(blockIdx.z) * M * N;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  for (int k0 = kb; k0 < ke; k0 += 16) {
     for (int i = threadIdx.x; i < 16 * 64; i += 256) {
       const int kk = i >> 6, o = i & 63;
       const int k = k0 + kk;
-      As[kk][o] = (k < K && m0 + o < M) ? A[(m0 + o) * sam + k * sak] : 0.f;
-      Bs[kk][o] = (k < K && n0 + o < N) ? bf16_to_f32(B[k * sbk + (n0 + o) * sbn]) : 0.f;
+      As[kk][o] = (k < ke && m0 + o < M) ? A[(m0 + o) * sam + k * sak] : 0.f;
+      Bs[kk][o] = (k < ke && n0 + o < N) ? bf16_to_f32(B[k * sbk + (n0 + o) * sbn]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -291,6 +294,16 @@ __global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__
       const int m = m0 + ty * 4 + a, n = n0 + tx * 4 + b;
       if (m < M && n < N) C[static_cast<size_t>(m) * N + n] = acc[a][b];
     }
+}
+
+// out[i] = sum over the S planes in order (plane stride n).
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float* __restrict__ part, int S,
+                                                         long n, float* __restrict__ out) {
+  const long i = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float s = part[i];
+  for (int z = 1; z < S; ++z) s += part[z * n + i];
+  out[i] = s;
 }
 
 // dx[t] = bf16( sum_j dx_row(t,j) (slot order, kept slots) + dx_shared[t] + dx_router[t] ).
@@ -465,12 +478,19 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, b.logits,
                      b.topk_idx, b.d_topk_w, b.cnt, T, E, K, s.norm_topk_prob, s.routed_scaling,
                      b.d_aux, b.d_logits);
-  hipLaunchKernelGGL(f32_gemm_kernel, dim3((H + 63) / 64, (E + 63) / 64), dim3(256), 0, stream,
+  const int rs = router_splits(T);
+  const int rkc = (T + rs - 1) / rs;
+  hipLaunchKernelGGL(f32_gemm_kernel, dim3((H + 63) / 64, (E + 63) / 64, rs), dim3(256), 0, stream,
                      b.d_logits, 1L, static_cast<long>(E), b.x, static_cast<long>(H), 1L, E, H, T,
-                     b.d_w_router);
+                     rkc, rs > 1 ? b.router_part : b.d_w_router);
+  if (rs > 1) {
+    const long n = static_cast<long>(E) * H;
+    hipLaunchKernelGGL(sum_planes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
+                       0, stream, b.router_part, rs, n, b.d_w_router);
+  }
   hipLaunchKernelGGL(f32_gemm_kernel, dim3((H + 63) / 64, (T + 63) / 64), dim3(256), 0, stream,
                      b.d_logits, static_cast<long>(E), 1L, b.w_router, static_cast<long>(H), 1L, T,
-                     H, E, b.dx_router);
+                     H, E, E, b.dx_router);
   // 8. dx
   const long nthr = static_cast<long>(T) * (H / 8);
   hipLaunchKernelGGL(dx_sum_kernel, dim3(static_cast<unsigned>((nthr + 255) / 256)), dim3(256), 0,

@@ -483,10 +483,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   const int n_tiles = dense ? (p.rows_max + kBM - 1) / kBM : p.tiles[0];
   const int splits = dense && p.k_splits > 1 ? p.k_splits : 1;
   const int total = n_tiles * nblk * splits;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int ws = (blockIdx.x % kXcds) * per_xcd + slot;
+  // Work item of this workgroup. Normally XCD-contiguous slices of the list (workgroup i runs on
+  // XCD i % 8), so that the workgroups of one XCD share operands through its L2. With per-split K
+  // ranges (one split per expert, weight gradients) the splits differ in length by orders of
+  // magnitude and the long ones are adjacent, so there the items go round-robin over the XCDs in
+  // list order: the long splits (the list's first) spread over the whole GPU and start first.
+  int ws;
+  if (p.k_tiles) {
+    ws = blockIdx.x;
+  } else {
+    const int per_xcd = (total + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    if (slot >= per_xcd) return;
+    ws = (blockIdx.x % kXcds) * per_xcd + slot;
+  }
   if (ws >= total) return;
   // dense mode: the K splits of one output tile are adjacent items. With per-split K-tile ranges
   // (k_tiles: one output matrix per split, over its own rows of K) the splits are outermost.
