@@ -515,7 +515,7 @@ int moe_layer_forward_w8a8(const moe_shape* s, const uint16_t* x, const uint16_t
 
 namespace {
 struct BwdWs {
-  size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles_tiled, d_topk_w, d_logits, wdT, wguT;
+  size_t dy, dh, dgu, dx_rows, dx_router, cnt, tiles_tiled, d_topk_w, d_logits;
   size_t dyT, hT, dguT, xgT, ktiles, kt, router_part;
   size_t total;
 };
@@ -538,9 +538,6 @@ BwdWs bwd_ws(const moe_shape& s) {
       moe::max_tiles_for(static_cast<int>(rows), s.E + s.n_shared, moe::kTiledRows)));
   w.d_topk_w = take(sizeof(float) * static_cast<size_t>(s.T) * s.K);
   w.d_logits = take(sizeof(float) * static_cast<size_t>(s.T) * s.E);
-  const size_t nmat = static_cast<size_t>(s.E + s.n_shared) * s.I * s.H;
-  w.wdT = take(sizeof(uint16_t) * nmat);
-  w.wguT = take(sizeof(uint16_t) * 2 * nmat);
   const int mtk = moe::backward_ktiles(static_cast<int>(rows), s.E + s.n_shared);
   const size_t ldk = static_cast<size_t>(mtk) * 64;
   w.dyT = take(sizeof(uint16_t) * s.H * ldk);
@@ -632,8 +629,6 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
   b.dx_router = reinterpret_cast<float*>(at(ws, w.dx_router));
   b.cnt = reinterpret_cast<int32_t*>(at(ws, w.cnt));
   b.tiles_tiled = reinterpret_cast<int32_t*>(at(ws, w.tiles_tiled));
-  b.wdT = reinterpret_cast<uint16_t*>(at(ws, w.wdT));
-  b.wguT = reinterpret_cast<uint16_t*>(at(ws, w.wguT));
   b.dyT = reinterpret_cast<uint16_t*>(at(ws, w.dyT));
   b.hT = reinterpret_cast<uint16_t*>(at(ws, w.hT));
   b.dguT = reinterpret_cast<uint16_t*>(at(ws, w.dguT));

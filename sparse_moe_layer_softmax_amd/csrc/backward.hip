@@ -4,10 +4,10 @@
 // load-balancing loss; Hy4 deep-dive `MoERouter` scores noise) but no backward is printed, so
 // this differentiates the forward in reverse:
 //   combine   dy_row = w_j * dout[t] (bf16); d w_j = <dout[t], y_row>          combine_bwd
-//   down      dh = dy Wd (bf16)                                  tiled kernel, Wd transposed
+//   down      dh = dy Wd (bf16)                                  tiled kernel, Wd as stored
 //   SwiGLU    g, u recomputed (x Wg^T, x Wu^T); dg = dh clamp(u) silu'(clamp g) [|g| <= L],
 //             du = dh silu(clamp g) [|u| <= L] (bf16)           tiled kernel, backward epilogue
-//   gate/up   dx_row = dg Wg + du Wu (bf16)                      tiled kernel, [Wg;Wu] transposed
+//   gate/up   dx_row = dg Wg + du Wu (bf16)                      tiled kernel, Wg, Wu as stored
 //   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x (fp32, per expert)
 //                                   tiled kernel over row-contiguous (transposed) operands
 //   routing   d logits through renormalisation, scaling and softmax, plus the load-balancing
@@ -15,9 +15,9 @@
 //   dx        the token's routed rows in slot order, the shared row, the router term  dx_sum
 // The shared expert is group 0 of the grouped products (identity rows), as in the forward.
 //
-// Every MFMA product runs on the forward's LDS-tiled kernel (ffn_tiled.hip), which reads both
-// operands along the reduction dimension. For the data gradients the weights are transposed once
-// per call. The weight gradients reduce over the rows of each expert: their operands (dy, h,
+// Every MFMA product runs on the forward's LDS-tiled kernel (ffn_tiled.hip). The data gradients
+// read the weights as they are stored (reduction dimension = weight rows) through the kernel's
+// LDS transpose-read form. The weight gradients reduce over the rows of each expert: their operands (dy, h,
 // [dg | du], the gathered x) are transposed so that each expert's rows form one contiguous,
 // 64-aligned K range, and the tiled kernel runs in dense mode with one K range and one fp32
 // output matrix per expert (an expert without rows gets zeros).
@@ -129,41 +129,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
     if (lane == 0) d_topk_w[s] = acc;
-  }
-}
-
-// dst[b][c][col0 + r] = src[b][r][c] for r < R, c < C (bf16; R and C multiples of 64): the
-// weights in the layout that lets the tiled kernel read the data-gradient products' weight
-// operand along its reduction dimension.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ src,
-                                                        size_t src_bstride, int R, int C,
-                                                        uint16_t* __restrict__ dst,
-                                                        size_t dst_bstride, int dst_ld, int col0) {
-  // 64x64 tiles through LDS (row pitch 66: the column gathers are conflict free), 16-byte
-  // global loads and stores (thread (a, b): columns 8b..8b+8 of rows a and a + 32)
-  __shared__ uint16_t tile[64][66];
-  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
-  const uint16_t* s = src + blockIdx.z * src_bstride;
-  uint16_t* d = dst + blockIdx.z * dst_bstride;
-  const int a = threadIdx.x >> 3, b = threadIdx.x & 7;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int i = pass * 32 + a;
-    const u32x4_t v = ld16(s + static_cast<size_t>(r0 + i) * C + c0 + 8 * b);
-    uint32_t* tp = reinterpret_cast<uint32_t*>(&tile[i][8 * b]);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) tp[m] = v[m];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int o = pass * 32 + a;
-    u32x4_t w;
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      w[m] = static_cast<uint32_t>(tile[8 * b + 2 * m][o]) |
-             (static_cast<uint32_t>(tile[8 * b + 2 * m + 1][o]) << 16);
-    *reinterpret_cast<u32x4_t*>(d + static_cast<size_t>(c0 + o) * dst_ld + col0 + r0 + 8 * b) = w;
   }
 }
 
@@ -350,26 +315,8 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   // 1. combine backward
   hipLaunchKernelGGL(combine_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, b.dout,
                      b.topk_w, b.slot_to_row, b.y, n_ident, T, K, H, b.dy, b.d_topk_w);
-  // 2. weights transposed for the tiled kernel: WdT [I][H] and [Wg;Wu]T [H][2I] per expert
-  const size_t IH = static_cast<size_t>(I) * H;
-  auto transpose = [&](const uint16_t* src, int nb, int R, int C, uint16_t* dst, int ld, int col0) {
-    hipLaunchKernelGGL(transpose_kernel, dim3(C / 64, R / 64, nb), dim3(256), 0, stream, src, IH, R,
-                       C, dst, static_cast<size_t>(ld) * C, ld, col0);
-  };
-  uint16_t* wdT_s = b.wdT;
-  uint16_t* wdT_r = b.wdT + (b.shared ? IH : 0);
-  uint16_t* wguT_s = b.wguT;
-  uint16_t* wguT_r = b.wguT + (b.shared ? 2 * IH : 0);
-  if (b.shared) {
-    transpose(b.s_down, 1, H, I, wdT_s, H, 0);
-    transpose(b.s_gate, 1, I, H, wguT_s, 2 * I, 0);
-    transpose(b.s_up, 1, I, H, wguT_s, 2 * I, I);
-  }
-  transpose(b.w_down, E, H, I, wdT_r, H, 0);
-  transpose(b.w_gate, E, I, H, wguT_r, 2 * I, 0);
-  transpose(b.w_up, E, I, H, wguT_r, 2 * I, I);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // 3. dh = dy Wd, 4. dg, du with g, u recomputed, 5. dx rows = dg Wg + du Wu: the tiled kernel
+  // 2. dh = dy Wd, 3. dg, du with g, u recomputed, 4. dx rows = dg Wg + du Wu: the tiled kernel
   const int mt = max_tiles_for(rows_max, G, kTiledRows);
   if ((e = launch_build_tiles(b.grp_offsets, G, kTiledRows, mt, b.tiles_tiled, stream)) != hipSuccess)
     return e;
@@ -382,13 +329,14 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     q.offsets = b.grp_offsets;
     q.tiles = b.tiles_tiled;
     q.max_tiles = mt;
-    q.W0a = wdT_s;
-    q.W0b = wdT_r;
+    q.W0a = b.s_down;  // Wd [H][I]: the reduction runs over its rows
+    q.W0b = b.w_down;
+    q.k_w0 = H;
     q.g_split = b.shared ? 1 : 0;
     q.out = b.dh;
     q.N = I;
     q.Kd = H;
-    if ((e = launch_tiled(kEpiBf16, q, mt, stream)) != hipSuccess) return e;
+    if ((e = launch_tiled(kEpiBf16T, q, mt, stream)) != hipSuccess) return e;
   }
   {
     // g and u recomputed by the tiled forward kernel, whose epilogue forms dg and du
@@ -423,15 +371,18 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     q.offsets = b.grp_offsets;
     q.tiles = b.tiles_tiled;
     q.max_tiles = mt;
-    q.W0a = wguT_s;
-    q.W0b = wguT_r;
+    q.W0a = b.s_gate;  // reduction rows [0, I): Wg [I][H] against dg, [I, 2I): Wu against du
+    q.W0b = b.w_gate;
+    q.W1a = b.s_up;
+    q.W1b = b.w_up;
+    q.k_w0 = I;
     q.g_split = b.shared ? 1 : 0;
     q.out = b.dx_rows;
     q.N = H;
     q.Kd = 2 * I;
-    if ((e = launch_tiled(kEpiBf16, q, mt, stream)) != hipSuccess) return e;
+    if ((e = launch_tiled(kEpiBf16T, q, mt, stream)) != hipSuccess) return e;
   }
-  // 6. weight gradients, one output matrix per group (zero for a group without rows): the
+  // 5. weight gradients, one output matrix per group (zero for a group without rows): the
   // operands transposed so that each group's rows are a contiguous, 64-aligned K range, then the
   // tiled kernel in dense mode with one K range and one output plane per group
   {
@@ -471,7 +422,7 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     if ((e = wgrad(b.dguT + static_cast<size_t>(I) * ldk, I, b.xgT, H, b.d_s_up, b.d_w_up)) != hipSuccess)
       return e;
   }
-  // 7. router: selections per expert, logit gradients, dWr = dl^T x, dx_router = dl Wr
+  // 6. router: selections per expert, logit gradients, dWr = dl^T x, dx_router = dl Wr
   hipLaunchKernelGGL(zero_i32_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, b.cnt, E);
   hipLaunchKernelGGL(count_kernel, dim3((T * K + 255) / 256), dim3(256), 0, stream, b.topk_idx,
                      T * K, E, b.cnt);
@@ -491,7 +442,7 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   hipLaunchKernelGGL(f32_gemm_kernel, dim3((H + 63) / 64, (T + 63) / 64), dim3(256), 0, stream,
                      b.d_logits, static_cast<long>(E), 1L, b.w_router, static_cast<long>(H), 1L, T,
                      H, E, E, b.dx_router);
-  // 8. dx
+  // 7. dx
   const long nthr = static_cast<long>(T) * (H / 8);
   hipLaunchKernelGGL(dx_sum_kernel, dim3(static_cast<unsigned>((nthr + 255) / 256)), dim3(256), 0,
                      stream, b.dx_rows, b.dx_router, b.slot_to_row, n_ident, T, K, H, b.d_x);

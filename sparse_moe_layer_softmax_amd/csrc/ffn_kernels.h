@@ -46,6 +46,10 @@ struct GroupedParams {
   float* out_f32_b;
   // FP8 activations (W8A8): A holds E4M3 codes, one fp32 scale per A row (indexed like A's rows)
   const float* a_scale;
+  // kEpiBf16T: the weights are stored [Kd][N] (N contiguous). Rows k < k_w0 of a group's weight
+  // are row k of its W0* matrix ([k_w0][N] per group), the others row k - k_w0 of its W1*
+  // matrix ([Kd - k_w0][N] per group). A multiple of 64.
+  int32_t k_w0;
 };
 
 
@@ -71,8 +75,11 @@ constexpr int kTiledRows = 320;
 // codes, Kd counts pairs of codes (K / 2, so the byte tiles move exactly as bf16 tiles do), the
 // products run on the FP8 MFMA, and the S* weight-row scales times a_scale of the row multiply
 // the fp32 sums.
+// kEpiBf16T: kEpiBf16 over weights stored with the output columns contiguous ([Kd][N], see
+// k_w0), as the data gradients of the backward pass read them: out = A W. The weight tile lands
+// in LDS as it lies in memory and the MFMA operands are read from it with the LDS transpose read.
 enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3, kEpiSwiglu8 = 4,
-                kEpiBf16_8 = 5, kEpiSwiglu88 = 6, kEpiBf16_88 = 7 };
+                kEpiBf16_8 = 5, kEpiSwiglu88 = 6, kEpiBf16_88 = 7, kEpiBf16T = 8 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 }  // namespace moe

@@ -47,6 +47,10 @@ namespace {
 //    n-block) and the band's activation rows through L2, and a group with at most kBand row
 //    tiles reads each of its weight tiles from HBM once.
 //  - bf16 results are staged through LDS and written as whole 16-byte row segments.
+//  - kEpiBf16T (the backward's data gradients, out = A W with W stored [K][N]): the weight tile
+//    is moved into LDS as it lies in memory, [64 k][256 n], and each MFMA B operand is put
+//    together by two LDS transpose reads (ds_read_b64_tr_b16), so the weights need no
+//    transposed copy in HBM.
 constexpr int kThreads = 512;
 constexpr int kBM = 320;  // rows per tile
 constexpr int kMI = 5;    // 32-row fragments per wavefront (160 rows: half the tile)
@@ -68,6 +72,25 @@ constexpr int kDmaB = kTN / 8 / 8;  // weight-tile DMA instructions per wavefron
 // distinct 16-byte bank groups of the 64-bank LDS.
 __device__ __forceinline__ int swz(int row, int k) {
   return row * kBK + (((k >> 3) ^ (row & 7) ^ ((row >> 3) & 1)) << 3) + (k & 7);
+}
+
+// Weight stage of kEpiBf16T: [64 k][256 n] bf16 as the weight lies in memory. The 32 16-byte
+// chunks of row k sit at slot chunk ^ tsw(k). A transpose read serves a 16-lane group 4 k-rows
+// x 16 columns; one instruction covers 8 k-rows (k % 4 all four values, k / 8 both parities)
+// and 4 consecutive chunks, and tsw sends those 16 (row, chunk) pairs to 16 distinct 16-byte
+// bank groups however the hardware pairs the lane groups.
+__device__ __forceinline__ int tsw(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// LDS transpose read of 4 16-bit values. In each group of 16 lanes, lane i returns element
+// i % 4 of the 8 bytes addressed by lanes 4r + i / 4 of its group, r = 0..3, in that order:
+// with lane 4r + q pointing at row r, columns 4q..4q+3 of a 4 x 16 block, lane i gets column i.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* l) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(l));
+  return __builtin_bit_cast(u32x2_t, v);
 }
 
 // s_waitcnt with only vmcnt constrained (expcnt and lgkmcnt left at their maxima).
@@ -113,6 +136,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
                                            int kb, int nk, int split) {
   constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;     // FP8 weights, bf16 activations
   constexpr bool A8 = EPI == kEpiSwiglu88 || EPI == kEpiBf16_88;  // FP8 weights and activations
+  constexpr bool BT = EPI == kEpiBf16T;  // weights [Kd][N], read with the LDS transpose read
   constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8 ||
                          EPI == kEpiSwiglu88;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
@@ -177,7 +201,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   const uint16_t* Wb = GATED && half ? W1 : W0;
   const size_t bstep = static_cast<size_t>(GATED ? 32 : 64) * Kd;
   uint32_t boff0 = 0;
-  if (!W8) boff0 = static_cast<uint32_t>(wrow(wave * 8 + lrow)) * Kd + kb * kBK + lchunk * 8;
+  if (!W8 && !BT) boff0 = static_cast<uint32_t>(wrow(wave * 8 + lrow)) * Kd + kb * kBK + lchunk * 8;
   // W8: a B stage is [256 rows][64 codes]; a 1 KB DMA block holds 16 rows. Lane i fills row
   // i/4 of the block, physical 16-byte chunk i%4, which holds logical chunk
   // (i%4) ^ ((row / 4) % 4); wavefront w fills blocks w + 8i, i < 2.
@@ -194,6 +218,19 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       bsrc8[i] = Qm + static_cast<size_t>(wrow(b)) * Kd + kb * kBK + lc8 * 16;
     }
   }
+  // BT: a B stage is [64 k][256 n]; a 1 KB DMA block holds 2 k-rows of 32 chunks. Lane i fills
+  // row i / 32 of block w + 8i', physical chunk i % 32, which holds logical chunk
+  // (i % 32) ^ tsw(row); the wavefront's four blocks lie 16 rows apart, which tsw ignores.
+  const uint16_t* V0 = nullptr;
+  const uint16_t* V1 = nullptr;
+  uint32_t btoff = 0;
+  if constexpr (BT) {
+    const size_t s0 = static_cast<size_t>(p.k_w0) * p.N, s1 = static_cast<size_t>(Kd - p.k_w0) * p.N;
+    V0 = g < p.g_split ? p.W0a + g * s0 : p.W0b + (g - p.g_split) * s0;
+    V1 = g < p.g_split ? p.W1a + g * s1 : p.W1b + (g - p.g_split) * s1;
+    const int row = 2 * wave + (lane >> 5);
+    btoff = static_cast<uint32_t>(row) * p.N + nb * kTN + (((lane & 31) ^ tsw(row)) << 3);
+  }
   auto dma_a = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
@@ -201,7 +238,14 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
                 sA + stage * kStageA + (20 * half + quarter + 4 * i) * 512);
   };
   auto dma_b = [&](int kt, int stage) {
-    if (W8) {
+    if constexpr (BT) {
+      const int k0 = (kb + kt) * kBK;  // first weight row of the K-tile (one matrix per K-tile)
+      const uint16_t* src = k0 < p.k_w0 ? V0 + static_cast<size_t>(k0) * p.N
+                                        : V1 + static_cast<size_t>(k0 - p.k_w0) * p.N;
+#pragma unroll
+      for (int i = 0; i < kDmaB; ++i)
+        lds_dma16<true>(src + btoff + i * 16 * p.N, sB + stage * kStageB + (wave + 8 * i) * 512);
+    } else if (W8) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         lds_dma16<true>(reinterpret_cast<const uint16_t*>(bsrc8[i] + kt * kBK),
@@ -236,6 +280,20 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   }
   // W8 B read: row quarter*64 + 32j + fr, logical chunk 2h + q of the 64-byte row
   const int boff8 = ((fr >> 2) & 3);
+  // BT B read of fragment j at K-step ks: lane group G = lane / 16 covers columns
+  // quarter*64 + 32j + 16(G % 2) + [0, 16) and k-rows 16ks + 8(G / 2) + [0, 8) in two reads of
+  // 4 rows; lane 4r + q of a group points at row r, columns 4q..4q+3 of its 4 x 16 block. The
+  // k-row's tsw term is the same for every ks and both reads.
+  int bt_rd[2] = {0, 0};
+  if constexpr (BT) {
+    const int G = lane >> 4, q = lane & 15;
+    const int kr = 8 * (G >> 1) + (q >> 2);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n0 = quarter * 64 + 32 * j + 16 * (G & 1) + 4 * (q & 3);
+      bt_rd[j] = kr * kTN + (((n0 >> 3) ^ tsw(kr)) << 3) + (n0 & 7);
+    }
+  }
   u32x4_t af[2][MV], bf[2][2];
   u32x8_t af8[MV], bf8[2];  // W8A8: one 32-code operand per fragment, its two 16-byte halves
   // fragments of the 32-wide K slice h of a stage
@@ -264,7 +322,17 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       af[0][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h]]);
       af[1][i] = *reinterpret_cast<const u32x4_t*>(&a[i * 32 * kBK + lds_off[2 * h + 1]]);
     }
-    if (W8) {
+    if constexpr (BT) {
+      const uint16_t* bt = sB + bstage * kStageB;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int o = bt_rd[j] + (32 * h + 16 * kk) * kTN;
+          const u32x2_t lo = lds_read_tr16(bt + o), hi = lds_read_tr16(bt + o + 4 * kTN);
+          bf[kk][j] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        }
+    } else if (W8) {
       const uint8_t* b8 = sB8 + bstage * kStageB8 + quarter * 64 * 64;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -578,6 +646,7 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
     case kEpiSwiglu88: return tiled_launch<kEpiSwiglu88>(p, p.N / 128, max_tiles, stream);
     case kEpiBf16_88: return tiled_launch<kEpiBf16_88>(p, p.N / kTN, max_tiles, stream);
     case kEpiBf16: return tiled_launch<kEpiBf16>(p, p.N / kTN, max_tiles, stream);
+    case kEpiBf16T: return tiled_launch<kEpiBf16T>(p, p.N / kTN, max_tiles, stream);
     default: return tiled_launch<kEpiF32>(p, p.N / kTN, max_tiles, stream);
   }
 }

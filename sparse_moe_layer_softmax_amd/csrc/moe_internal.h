@@ -114,7 +114,6 @@ struct BwdProblem {
   float* dx_router;                   // [T, H]
   int32_t* cnt;                       // [E]
   int32_t* tiles_tiled;               // tile table of the tiled forward kernel's row tile
-  uint16_t *wdT, *wguT;               // transposed weights: [G][I][H], [G][H][2I] (shared first)
   // weight-gradient operands with the rows contiguous (ld = backward_ktile_ld(rows, G)):
   uint16_t *dyT, *hT, *dguT, *xgT;    // [H][ld], [I][ld], [2I][ld], [H][ld]
   int32_t *ktiles, *kt;               // K-tile table of 64-row tiles, [2G] per-group ranges
