@@ -137,14 +137,23 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
   if (i < n) p[i] = 0;
 }
 
-// Selections per expert (integer atomics: exact in any order).
-__global__ void count_kernel(const int32_t* __restrict__ topk_idx, int n, int E,
-                             int32_t* __restrict__ cnt) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) {
+// Selections per expert (integer atomics: exact in any order). Each workgroup counts a chunk of
+// kCountChunk selections into an LDS histogram and adds its nonzero bins to cnt, so a skewed
+// routing (one expert selected by every token) does not serialise on one global counter.
+constexpr int kCountChunk = 4096;
+__global__ __launch_bounds__(256) void count_kernel(const int32_t* __restrict__ topk_idx, int n,
+                                                    int E, int32_t* __restrict__ cnt) {
+  __shared__ int32_t hist[1024];  // E <= 1024
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int i0 = blockIdx.x * kCountChunk, i1 = min(n, i0 + kCountChunk);
+  for (int i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
     const int e = topk_idx[i];
-    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&cnt[e], 1);
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&hist[e], 1);
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    if (hist[e]) atomicAdd(&cnt[e], hist[e]);
 }
 
 // Logit gradients of one token per wavefront: the routing-weight gradients through the
@@ -223,42 +232,108 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(
     if (lane + 64 * q < E) dl[static_cast<size_t>(t) * E + lane + 64 * q] = p[q] * (dp[q] - dot);
 }
 
-// C[M,N] (fp32, row-major) = sum_k A(m,k) B(k,n), A fp32 at A[m*sam + k*sak], B bf16 at
-// B[k*sbk + n*sbn]: the router's small products in fp32. 64x64 tiles, K in steps of 16. With
-// gridDim.z > 1, workgroup z reduces K range [z*kc, z*kc + kc) into plane z of C (M*N each).
-__global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__ A, long sam,
-                                                       long sak, const uint16_t* __restrict__ B,
-                                                       long sbk, long sbn, int M, int N, int K,
-                                                       int kc, float* __restrict__ C) {
-  __shared__ float As[16][65], Bs[16][65];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+// C[M,N] (fp32, row-major) = sum_k A(m,k) B(k,n): the router's products in fp32. A is fp32 with
+// A(m,k) = A[m*lda + k] (AK) or A[k*lda + m]; B is bf16 [K][N] with row pitch ldb (N a multiple of
+// 128, ldb of 8). 128x128 tiles, K in steps of 16 through a double-buffered LDS tile. Thread
+// (tx, ty) of the 16x16 grid owns rows ty*4 + {0..3} and 64 + ty*4 + {0..3} and columns
+// tx*4 + {0..3} and 64 + tx*4 + {0..3}, so each k costs it four 16-byte LDS reads for 64 FMAs.
+// Each output sums its k in increasing order. With gridDim.z > 1, workgroup z reduces the K
+// range [z*kc, z*kc + kc) into plane z of C (M*N each).
+template <bool AK>
+__global__ __launch_bounds__(256) void f32_gemm_kernel(const float* __restrict__ A, long lda,
+                                                       const uint16_t* __restrict__ B, long ldb,
+                                                       int M, int N, int K, int kc,
+                                                       float* __restrict__ C) {
+  constexpr int TM = 128, TN = 128, BK = 16, PM = TM + 4;  // PM: A rows padded (AK stores)
+  __shared__ __attribute__((aligned(16))) float As[2][BK][PM];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][TN];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
   const int kb = blockIdx.z * kc, ke = min(K, kb + kc);
   C += static_cast<size_t>(blockIdx.z) * M * N;
-  float acc[4][4] = {};
-  for (int k0 = kb; k0 < ke; k0 += 16) {
-    for (int i = threadIdx.x; i < 16 * 64; i += 256) {
-      const int kk = i >> 6, o = i & 63;
-      const int k = k0 + kk;
-      As[kk][o] = (k < ke && m0 + o < M) ? A[(m0 + o) * sam + k * sak] : 0.f;
-      Bs[kk][o] = (k < ke && n0 + o < N) ? bf16_to_f32(B[k * sbk + (n0 + o) * sbn]) : 0.f;
+  // A element i of this thread: AK, 16 lanes read 16 consecutive k of a row; else consecutive
+  // lanes read consecutive m of a k-row. B: one 16-byte load of 8 bf16 per thread.
+  auto a_mk = [&](int i, int& m, int& k) {
+    if (AK) {
+      k = tid & 15;
+      m = (tid >> 4) + 16 * i;
+    } else {
+      m = tid & 127;
+      k = (tid >> 7) + 2 * i;
     }
-    __syncthreads();
+  };
+  float ra[8];
+  u32x4_t rb;
+  auto load = [&](int k0) {
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
+    for (int i = 0; i < 8; ++i) {
+      int m, k;
+      a_mk(i, m, k);
+      const int gm = m0 + m, gk = k0 + k;
+      ra[i] = gm < M && gk < ke ? (AK ? A[gm * lda + gk] : A[gk * lda + gm]) : 0.f;
+    }
+    const int gk = k0 + (tid >> 4);
+    rb = gk < ke ? ld16(B + gk * ldb + n0 + (tid & 15) * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto store = [&](int buf) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int i = 0; i < 8; ++i) {
+      int m, k;
+      a_mk(i, m, k);
+      As[buf][k][m] = ra[i];
+    }
+    float* bp = &Bs[buf][tid >> 4][(tid & 15) * 8];
+    f32x4_t lo, hi;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] += As[kk][ty * 4 + a] * Bs[kk][tx * 4 + b];
+    for (int q = 0; q < 2; ++q) {
+      lo[2 * q] = bf16_to_f32(static_cast<uint16_t>(rb[q] & 0xffffu));
+      lo[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(rb[q] >> 16));
+      hi[2 * q] = bf16_to_f32(static_cast<uint16_t>(rb[q + 2] & 0xffffu));
+      hi[2 * q + 1] = bf16_to_f32(static_cast<uint16_t>(rb[q + 2] >> 16));
+    }
+    *reinterpret_cast<f32x4_t*>(bp) = lo;
+    *reinterpret_cast<f32x4_t*>(bp + 4) = hi;
+  };
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  const int nk = ke > kb ? (ke - kb + BK - 1) / BK : 0;
+  if (nk > 0) {
+    load(kb);
+    store(0);
+  }
+  __syncthreads();
+  for (int t = 0; t < nk; ++t) {
+    const int cur = t & 1;
+    if (t + 1 < nk) load(kb + (t + 1) * BK);
+#pragma unroll 2
+    for (int kk = 0; kk < BK; ++kk) {
+      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(&As[cur][kk][ty * 4]);
+      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(&As[cur][kk][64 + ty * 4]);
+      const f32x4_t b0 = *reinterpret_cast<const f32x4_t*>(&Bs[cur][kk][tx * 4]);
+      const f32x4_t b1 = *reinterpret_cast<const f32x4_t*>(&Bs[cur][kk][64 + tx * 4]);
+      const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    // the other buffer was last read in step t - 1, which every thread finished before the
+    // barrier that ended it
+    if (t + 1 < nk) store(cur ^ 1);
     __syncthreads();
   }
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int m = m0 + ty * 4 + a, n = n0 + tx * 4 + b;
-      if (m < M && n < N) C[static_cast<size_t>(m) * N + n] = acc[a][b];
-    }
+  for (int i = 0; i < 8; ++i) {
+    const int m = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + i - 4);
+    if (m >= M) continue;
+    float* c = C + static_cast<size_t>(m) * N + n0 + tx * 4;
+    *reinterpret_cast<f32x4_t*>(c) = f32x4_t{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+    *reinterpret_cast<f32x4_t*>(c + 64) = f32x4_t{acc[i][4], acc[i][5], acc[i][6], acc[i][7]};
+  }
 }
 
 // out[i] = sum over the S planes in order (plane stride n).
@@ -424,24 +499,24 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
   }
   // 6. router: selections per expert, logit gradients, dWr = dl^T x, dx_router = dl Wr
   hipLaunchKernelGGL(zero_i32_kernel, dim3((E + 255) / 256), dim3(256), 0, stream, b.cnt, E);
-  hipLaunchKernelGGL(count_kernel, dim3((T * K + 255) / 256), dim3(256), 0, stream, b.topk_idx,
-                     T * K, E, b.cnt);
+  hipLaunchKernelGGL(count_kernel, dim3((T * K + kCountChunk - 1) / kCountChunk), dim3(256), 0,
+                     stream, b.topk_idx, T * K, E, b.cnt);
   hipLaunchKernelGGL(router_bwd_kernel, dim3((T + 3) / 4), dim3(256), 0, stream, b.logits,
                      b.topk_idx, b.d_topk_w, b.cnt, T, E, K, s.norm_topk_prob, s.routed_scaling,
                      b.d_aux, b.d_logits);
   const int rs = router_splits(T);
   const int rkc = (T + rs - 1) / rs;
-  hipLaunchKernelGGL(f32_gemm_kernel, dim3((H + 63) / 64, (E + 63) / 64, rs), dim3(256), 0, stream,
-                     b.d_logits, 1L, static_cast<long>(E), b.x, static_cast<long>(H), 1L, E, H, T,
+  hipLaunchKernelGGL(f32_gemm_kernel<false>, dim3(H / 128, (E + 127) / 128, rs), dim3(256), 0,
+                     stream, b.d_logits, static_cast<long>(E), b.x, static_cast<long>(H), E, H, T,
                      rkc, rs > 1 ? b.router_part : b.d_w_router);
   if (rs > 1) {
     const long n = static_cast<long>(E) * H;
     hipLaunchKernelGGL(sum_planes_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256),
                        0, stream, b.router_part, rs, n, b.d_w_router);
   }
-  hipLaunchKernelGGL(f32_gemm_kernel, dim3((H + 63) / 64, (T + 63) / 64), dim3(256), 0, stream,
-                     b.d_logits, static_cast<long>(E), 1L, b.w_router, static_cast<long>(H), 1L, T,
-                     H, E, E, b.dx_router);
+  hipLaunchKernelGGL(f32_gemm_kernel<true>, dim3(H / 128, (T + 127) / 128), dim3(256), 0, stream,
+                     b.d_logits, static_cast<long>(E), b.w_router, static_cast<long>(H), T, H, E, E,
+                     b.dx_router);
   // 7. dx
   const long nthr = static_cast<long>(T) * (H / 8);
   hipLaunchKernelGGL(dx_sum_kernel, dim3(static_cast<unsigned>((nthr + 255) / 256)), dim3(256), 0,

@@ -464,7 +464,10 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
         const int ch = lane & 15;
         const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&ep[foff(row, ch * 4)]);
         const int r = rbase + i * 32 + row;
-        if (r < r1) *reinterpret_cast<f32x4_t*>(ob + static_cast<size_t>(r) * p.N + col0 + ch * 4) = val;
+        // non-temporal: nothing in this kernel reads the planes back, and the weight gradients
+        // write far more than the L2 holds
+        if (r < r1)
+          __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(ob + static_cast<size_t>(r) * p.N + col0 + ch * 4));
       }
       __builtin_amdgcn_sched_barrier(0);
     }

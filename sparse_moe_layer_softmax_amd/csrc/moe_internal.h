@@ -126,10 +126,10 @@ struct BwdProblem {
 hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream);
 // Row stride of the transposed weight-gradient operands, and the K-tile table's tile bound.
 inline int backward_ktiles(int rows_max, int n_groups) { return max_tiles_for(rows_max, n_groups, 64); }
-// The router weight gradient dWr = dlogits^T x reduces over all T tokens with only E/64 x H/64
-// output tiles; it is split into this many token ranges of at least 4096 (at most 16), each with
+// The router weight gradient dWr = dlogits^T x reduces over all T tokens with only E/128 x H/128
+// output tiles; it is split into this many token ranges of at least 1024 (at most 16), each with
 // its own fp32 partial plane, summed in order afterwards.
-inline int router_splits(int T) { return T <= 4096 ? 1 : (T + 4095) / 4096 < 16 ? (T + 4095) / 4096 : 16; }
+inline int router_splits(int T) { return T <= 1024 ? 1 : (T + 1023) / 1024 < 16 ? (T + 1023) / 1024 : 16; }
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,
