@@ -289,12 +289,12 @@ def main():
 
 def train_flops(wl, counts):
     """Algorithmic FLOPs of one training step from the run's routing: the forward, and a backward
-    of dh, dx rows, dWd, dWg/dWu (2+4+2+4 H I per row), the recomputed gate/up (4 H I per row) and
-    the router's two products (2 T E H each)."""
+    of dh, dx rows, dWd, dWg/dWu (2+4+2+4 H I per row) and the router's two products (2 T E H
+    each). The training forward stores the gate/up sums, so the backward recomputes nothing."""
     T, H, E, I, S = wl.T, wl.H, wl.E, wl.I, wl.n_shared
     rows = int(counts.sum()) + S * T
     fwd = 2 * T * H * E + 6 * H * I * rows
-    bwd = 16 * H * I * rows + 4 * T * E * H
+    bwd = 12 * H * I * rows + 4 * T * E * H
     return fwd, bwd
 
 
@@ -375,7 +375,8 @@ def cpu_baseline_train(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
 
 
 def train_step(args, wl, dev, layer):
-    """One step = moe_layer_forward + moe_layer_backward (d_aux 0.01), HIP events around each."""
+    """One step = moe_layer_forward_train + moe_layer_backward (d_aux 0.01), HIP events around
+    each."""
     import torch
 
     if wl.fp8:
@@ -387,13 +388,13 @@ def train_step(args, wl, dev, layer):
     dout = torch.randn(wl.T, wl.H, generator=gen, device="cuda").to(torch.bfloat16)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     for _ in range(args.warmup):
-        layer.forward(dev["x"], out)
+        layer.forward(dev["x"], out, train=True)
         layer.backward(dout, 0.01)
     torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
-        layer.forward(dev["x"], out)
+        layer.forward(dev["x"], out, train=True)
         layer.backward(dout, 0.01)
     stop.record(stream)
     torch.cuda.synchronize()
@@ -402,7 +403,7 @@ def train_step(args, wl, dev, layer):
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         ev[i][0].record(stream)
-        layer.forward(dev["x"], out)
+        layer.forward(dev["x"], out, train=True)
         ev[i][1].record(stream)
         layer.backward(dout, 0.01)
         ev[i][2].record(stream)

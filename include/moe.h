@@ -295,8 +295,9 @@ int moe_layer_forward_w8a8(const moe_shape* shape, const uint16_t* x, const uint
  * training). The pages print no backward; this is the derivative of moe_layer_forward:
  *   combine   dy_row = bf16(w_j dout[t]) for each kept slot; d w_j = <dout[t], y_row>
  *   down      dh = bf16(dy Wd)
- *   SwiGLU    g = x Wg^T, u = x Wu^T recomputed in fp32; dg = bf16(dh clamp(u) silu'(clamp g)
- *             [-L <= g <= L]), du = bf16(dh silu(clamp g) [-L <= u <= L]) (no masks for L <= 0)
+ *   SwiGLU    g = x Wg^T, u = x Wu^T in fp32 (stored by moe_layer_forward_train, or recomputed);
+ *             dg = bf16(dh clamp(u) silu'(clamp g) [-L <= g <= L]),
+ *             du = bf16(dh silu(clamp g) [-L <= u <= L]) (no masks for L <= 0)
  *   gate/up   dx_row = bf16(dg Wg + du Wu)
  *   weights   dWd = dy^T h, dWg = dg^T x, dWu = du^T x per expert (and the shared expert, whose
  *             dy is dout), fp32 sums over the expert's rows; an expert without rows gets zeros
@@ -307,8 +308,10 @@ int moe_layer_forward_w8a8(const moe_shape* shape, const uint16_t* x, const uint
  *   dx        bf16( sum over the token's kept slots in slot order of dx_row, + the shared
  *             row's dx_row, + dx_router )
  * Inputs: the layer's bf16 weights (FP8 weights are not supported here), x, and the workspace
- * of a moe_layer_forward call with the same shape and inputs (fwd_ws, its logits, routing,
- * dispatch, h and y are read), d_out [T,H] bf16, d_aux (0 for no loss term).
+ * of a moe_layer_forward or moe_layer_forward_train call with the same shape and inputs
+ * (fwd_ws, its logits, routing, dispatch, h and y are read), d_out [T,H] bf16, d_aux (0 for no
+ * loss term). gu: the gate/up sums that moe_layer_forward_train stored (16-byte aligned), or
+ * NULL to recompute them; the result is the same either way.
  * Outputs: d_x [T,H] bf16; d_w_router [E,H], d_w_gate/d_w_up [E,I,H], d_w_down [E,H,I] fp32;
  * d_s_gate/d_s_up [I,H], d_s_down [H,I] fp32 (NULL iff n_shared = 0); d_topk_w [T,K] and
  * d_logits [T,E] fp32 or NULL (then kept in the workspace). d_out and d_x 16-byte aligned.
@@ -329,11 +332,27 @@ int moe_layer_backward_workspace_layout(const moe_shape* shape, moe_bwd_ws_layou
 int moe_layer_backward(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
                        const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                        const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
-                       const void* fwd_ws, size_t fwd_ws_bytes, const uint16_t* d_out,
-                       float d_aux, uint16_t* d_x, float* d_w_router, float* d_w_gate,
-                       float* d_w_up, float* d_w_down, float* d_s_gate, float* d_s_up,
-                       float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
+                       const void* fwd_ws, size_t fwd_ws_bytes, const float* gu,
+                       const uint16_t* d_out, float d_aux, uint16_t* d_x, float* d_w_router,
+                       float* d_w_gate, float* d_w_up, float* d_w_down, float* d_s_gate,
+                       float* d_s_up, float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/* The forward of a training step: moe_layer_forward, which also stores for moe_layer_backward
+ * the fp32 gate and up sums g = x Wg^T, u = x Wu^T of every layer row (the pre-activation
+ * values of the SwiGLU step above; Hy3 deep-dive `MoEFeedForward`, Hy4 config walkthrough
+ * "MoE routed experts"). The backward then reads them and skips recomputing the gate/up GEMM.
+ * gu: [T + T*K, 2I] fp32, device, 16-byte aligned, caller-owned: row r (layer order, shared rows
+ * first, as in the workspace's h) holds g in columns [0, I) and u in [I, 2I); rows past the
+ * layer's row count (capacity drops) are not written. The gate/up and down projections always
+ * run on the LDS-tiled MFMA kernel here, whatever the rows per expert, so the stored sums are the
+ * ones the backward's recompute forms, bit for bit. Everything else, workspace included, as
+ * moe_layer_forward; NULL gu is MOE_ERR_INVALID_ARG.                                            */
+int moe_layer_forward_train(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                            const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
+                            const uint16_t* w_down, const uint16_t* s_gate, const uint16_t* s_up,
+                            const uint16_t* s_down, uint16_t* out, float* gu, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

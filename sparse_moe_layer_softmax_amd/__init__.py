@@ -26,7 +26,7 @@ EXPORTED = (
     "moe_strerror", "moe_route_workspace_size", "moe_route", "moe_permute_workspace_size",
     "moe_permute", "moe_expert_ffn_workspace_size", "moe_expert_ffn", "moe_combine",
     "moe_layer_workspace_size", "moe_layer_workspace_layout", "moe_layer_forward",
-    "moe_layer_forward_profiled", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
+    "moe_layer_forward_profiled", "moe_layer_forward_train", "moe_expert_ffn_fp8", "moe_layer_forward_fp8",
     "moe_route_train_workspace_size", "moe_route_train", "moe_layer_backward_workspace_size",
     "moe_layer_backward_workspace_layout", "moe_layer_backward", "moe_quantize_rows_e4m3",
     "moe_layer_w8a8_workspace_size", "moe_layer_w8a8_workspace_layout", "moe_layer_forward_w8a8",
@@ -105,12 +105,13 @@ def _load():
         "moe_layer_workspace_layout": ([sp, ctypes.POINTER(moe_layer_ws_layout)], ctypes.c_int),
         "moe_layer_forward": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P], ctypes.c_int),
         "moe_layer_forward_profiled": ([sp, P, P, P, P, P, P, P, P, P, P, P, S, P, P], ctypes.c_int),
+        "moe_layer_forward_train": ([sp] + [P] * 12 + [S, P], ctypes.c_int),
         "moe_expert_ffn_fp8": ([sp, I32, I32] + [P] * 12 + [S, P], ctypes.c_int),
         "moe_route_train_workspace_size": ([sp], S),
         "moe_route_train": ([sp] + [P] * 12 + [ctypes.c_float, P, S, P], ctypes.c_int),
         "moe_layer_backward_workspace_size": ([sp], S),
         "moe_layer_backward_workspace_layout": ([sp, ctypes.POINTER(moe_bwd_ws_layout)], ctypes.c_int),
-        "moe_layer_backward": ([sp] + [P] * 9 + [S, P, ctypes.c_float] + [P] * 10 + [P, S, P],
+        "moe_layer_backward": ([sp] + [P] * 9 + [S, P, P, ctypes.c_float] + [P] * 10 + [P, S, P],
                                ctypes.c_int),
         "moe_layer_forward_fp8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
         "moe_quantize_rows_e4m3": ([P, I32, I32, P, P, P], ctypes.c_int),
@@ -224,11 +225,13 @@ def moe_layer_backward_workspace_layout(shape: Shape) -> dict:
 
 def moe_layer_backward(shape: Shape, x, w_router, w_gate, w_up, w_down, s_gate, s_up, s_down,
                        fwd_ws, d_out, d_aux, d_x, d_w_router, d_w_gate, d_w_up, d_w_down,
-                       d_s_gate, d_s_up, d_s_down, d_topk_w, d_logits, ws, stream=None):
-    """Backward of moe_layer_forward from its workspace fwd_ws (see include/moe.h)."""
+                       d_s_gate, d_s_up, d_s_down, d_topk_w, d_logits, ws, stream=None, gu=None):
+    """Backward of moe_layer_forward (or moe_layer_forward_train, whose stored gate/up sums gu
+    it then reads) from its workspace fwd_ws (see include/moe.h)."""
     _check(library().moe_layer_backward(
         ctypes.byref(shape.c()), _p(x), _p(w_router), _p(w_gate), _p(w_up), _p(w_down),
-        _p(s_gate), _p(s_up), _p(s_down), _p(fwd_ws), fwd_ws.numel(), _p(d_out), float(d_aux),
+        _p(s_gate), _p(s_up), _p(s_down), _p(fwd_ws), fwd_ws.numel(), _p(gu), _p(d_out),
+        float(d_aux),
         _p(d_x), _p(d_w_router), _p(d_w_gate), _p(d_w_up), _p(d_w_down), _p(d_s_gate),
         _p(d_s_up), _p(d_s_down), _p(d_topk_w), _p(d_logits), _p(ws),
         ws.numel() if ws is not None else 0, _stream(stream)), "moe_layer_backward")
@@ -252,6 +255,16 @@ def moe_expert_ffn(shape: Shape, n_groups: int, rows_max: int, x, row_to_slot, g
 def moe_combine(shape: Shape, y_routed, topk_w, slot_to_row, y_shared, out, stream=None):
     _check(library().moe_combine(ctypes.byref(shape.c()), _p(y_routed), _p(topk_w), _p(slot_to_row),
                            _p(y_shared), _p(out), _stream(stream)), "moe_combine")
+
+
+def moe_layer_forward_train(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,
+                            s_down, out, gu, ws, stream=None):
+    """moe_layer_forward that also stores the fp32 gate/up sums gu [T + T*K, 2I] for the backward."""
+    _check(library().moe_layer_forward_train(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias),
+                                       _p(w_gate), _p(w_up), _p(w_down), _p(s_gate), _p(s_up),
+                                       _p(s_down), _p(out), _p(gu), _p(ws),
+                                       ws.numel() if ws is not None else 0, _stream(stream)),
+           "moe_layer_forward_train")
 
 
 def moe_layer_forward(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,
@@ -363,12 +376,24 @@ class MoELayer:
         return cls(shape, d["w_router"], d["w_gate"], d["w_up"], d["w_down"], d["s_gate"], d["s_up"],
                    d["s_down"], d["router_bias"], scales=scales, act_fp8=bool(d.get("act_fp8")))
 
-    def forward(self, x, out=None, stream=None, phase_events=None):
+    def forward(self, x, out=None, stream=None, phase_events=None, train=False):
+        """The layer's output. train=True: moe_layer_forward_train, keeping the fp32 gate/up sums
+        (self.gu) that backward() then reads instead of recomputing them."""
         if out is None:
             out = torch.empty((self.shape.T, self.shape.H), dtype=torch.bfloat16, device=self.device)
         wr, b, wg, wu, wd, sg, su, sd = self.w
         self._x = x
-        if self.fp8:
+        self._gu = None
+        if train:
+            if self.fp8:
+                raise ValueError("the training forward takes bf16 expert weights")
+            s = self.shape
+            rows = s.T * s.K + (s.T if s.n_shared else 0)
+            if getattr(self, "gu", None) is None or tuple(self.gu.shape) != (rows, 2 * s.I):
+                self.gu = torch.empty((rows, 2 * s.I), dtype=torch.float32, device=self.device)
+            moe_layer_forward_train(s, x, wr, b, wg, wu, wd, sg, su, sd, out, self.gu, self.ws, stream)
+            self._gu = self.gu
+        elif self.fp8:
             sc = self.scales
             fwd = moe_layer_forward_w8a8 if self.act_fp8 else moe_layer_forward_fp8
             fwd(self.shape, x, wr, b, wg, sc["w_gate"], wu, sc["w_up"], wd, sc["w_down"], sg,
@@ -406,7 +431,7 @@ class MoELayer:
         moe_layer_backward(s, self._x, wr, wg, wu, wd, sg, su, sd, self.ws, d_out, d_aux,
                            g["d_x"], g["d_w_router"], g["d_w_gate"], g["d_w_up"], g["d_w_down"],
                            g.get("d_s_gate"), g.get("d_s_up"), g.get("d_s_down"), g["d_topk_w"],
-                           g["d_logits"], self.bws, stream)
+                           g["d_logits"], self.bws, stream, gu=getattr(self, "_gu", None))
         return g
 
     def bwd_intermediate(self, name: str, dtype, shape):

@@ -211,7 +211,8 @@ A8Ws a8_ws(const moe_shape& s) {
 
 int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, const float* bias,
                const Weights& routed, const Weights& shared_w, uint16_t* out, void* ws,
-               size_t ws_bytes, hipStream_t stream, hipEvent_t const* ev, bool a8 = false) {
+               size_t ws_bytes, hipStream_t stream, hipEvent_t const* ev, bool a8 = false,
+               float* gu = nullptr) {
   auto mark = [&](int i) {
     if (ev && ev[i]) (void)hipEventRecord(ev[i], stream);
   };
@@ -275,6 +276,7 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
   p.h = h;
   p.y = y;
   p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
+  p.gu = gu;
   if (a8) {
     p.a8 = true;
     p.xq = reinterpret_cast<uint8_t*>(at(ws, wa.pub.xq));
@@ -454,6 +456,17 @@ int moe_layer_forward(const moe_shape* s, const uint16_t* x, const uint16_t* w_r
                                     s_down, out, ws, ws_bytes, stream, nullptr);
 }
 
+int moe_layer_forward_train(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                            const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
+                            const uint16_t* w_down, const uint16_t* s_gate, const uint16_t* s_up,
+                            const uint16_t* s_down, uint16_t* out, float* gu, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (!gu || (reinterpret_cast<uintptr_t>(gu) & 15u)) return MOE_ERR_INVALID_ARG;
+  return layer_impl(s, x, w_router, bias, Weights::bf16(w_gate, w_up, w_down),
+                    Weights::bf16(s_gate, s_up, s_down), out, ws, ws_bytes, stream, nullptr, false,
+                    gu);
+}
+
 int moe_layer_forward_profiled(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
                                const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
                                const uint16_t* w_down, const uint16_t* s_gate,
@@ -577,10 +590,10 @@ int moe_layer_backward_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* l
 int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
                        const uint16_t* w_gate, const uint16_t* w_up, const uint16_t* w_down,
                        const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
-                       const void* fwd_ws, size_t fwd_ws_bytes, const uint16_t* d_out,
-                       float d_aux, uint16_t* d_x, float* d_w_router, float* d_w_gate,
-                       float* d_w_up, float* d_w_down, float* d_s_gate, float* d_s_up,
-                       float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
+                       const void* fwd_ws, size_t fwd_ws_bytes, const float* gu,
+                       const uint16_t* d_out, float d_aux, uint16_t* d_x, float* d_w_router,
+                       float* d_w_gate, float* d_w_up, float* d_w_down, float* d_s_gate,
+                       float* d_s_up, float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
   int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
@@ -594,7 +607,8 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
     return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(d_aux)) return MOE_ERR_INVALID_ARG;
   if (s->H % 128 != 0 || s->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
-  if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_x)) & 15u)
+  if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_x) |
+       reinterpret_cast<uintptr_t>(gu)) & 15u)
     return MOE_ERR_INVALID_ARG;  // 16-byte vector accesses
   const LayerWs fw = layer_ws(*s);
   if (fwd_ws_bytes < fw.pub.total || !aligned(fwd_ws)) return MOE_ERR_WORKSPACE;
@@ -636,6 +650,7 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
   b.ktiles = reinterpret_cast<int32_t*>(at(ws, w.ktiles));
   b.kt = reinterpret_cast<int32_t*>(at(ws, w.kt));
   b.router_part = reinterpret_cast<float*>(at(ws, w.router_part));
+  b.gu = gu;
   b.d_topk_w = d_topk_w ? d_topk_w : reinterpret_cast<float*>(at(ws, w.d_topk_w));
   b.d_logits = d_logits ? d_logits : reinterpret_cast<float*>(at(ws, w.d_logits));
   b.d_x = d_x;

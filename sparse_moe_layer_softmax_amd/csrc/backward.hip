@@ -132,6 +132,34 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   }
 }
 
+// dg, du (bf16, [rows][2I]: dg in columns [0, I), du in [I, 2I)) from the forward's fp32 gate and
+// up sums gu (same layout) and dh [rows][I]; four columns per thread. Rows at or past *rows_dev
+// (the layer's row count) are left untouched.
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const float* __restrict__ gu,
+                                                         const uint16_t* __restrict__ dh,
+                                                         const int32_t* __restrict__ rows_dev,
+                                                         int rows_max, int I, float L,
+                                                         uint16_t* __restrict__ dgu) {
+  const int per_row = I / 4;
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<long>(rows_max) * per_row) return;
+  const int r = static_cast<int>(idx / per_row), c = static_cast<int>(idx % per_row) * 4;
+  if (r >= *rows_dev) return;
+  const size_t ld = 2 * static_cast<size_t>(I);
+  const f32x4_t g = *reinterpret_cast<const f32x4_t*>(gu + r * ld + c);
+  const f32x4_t u = *reinterpret_cast<const f32x4_t*>(gu + r * ld + I + c);
+  const uint2 d = *reinterpret_cast<const uint2*>(dh + static_cast<size_t>(r) * I + c);
+  const float dhv[4] = {bf16_to_f32(static_cast<uint16_t>(d.x & 0xffffu)),
+                        bf16_to_f32(static_cast<uint16_t>(d.x >> 16)),
+                        bf16_to_f32(static_cast<uint16_t>(d.y & 0xffffu)),
+                        bf16_to_f32(static_cast<uint16_t>(d.y >> 16))};
+  float dg[4], du[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) swiglu_bwd(g[q], u[q], dhv[q], L, dg[q], du[q]);
+  *reinterpret_cast<uint2*>(dgu + r * ld + c) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+  *reinterpret_cast<uint2*>(dgu + r * ld + I + c) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+}
+
 __global__ void zero_i32_kernel(int32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -413,7 +441,12 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     q.Kd = H;
     if ((e = launch_tiled(kEpiBf16T, q, mt, stream)) != hipSuccess) return e;
   }
-  {
+  if (b.gu) {
+    // g and u as the forward stored them: dg and du elementwise
+    const long n = static_cast<long>(rows_max) * (I / 4);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+                       stream, b.gu, b.dh, b.grp_offsets + G, rows_max, I, s.swiglu_limit, b.dgu);
+  } else {
     // g and u recomputed by the tiled forward kernel, whose epilogue forms dg and du
     GroupedParams q{};
     q.A = b.x;

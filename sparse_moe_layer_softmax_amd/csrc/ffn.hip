@@ -101,7 +101,7 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   };
   // Few rows per group (decode): stream the weights. Many rows per group: LDS-tiled MFMA. Both
   // kernels have an FP8-weight form.
-  const bool tiled = q.rows_max >= 64 * q.n_groups;
+  const bool tiled = q.gu || q.rows_max >= 64 * q.n_groups;
   const bool small = !tiled && q.rows_max <= kSkinnyRowsSmall * q.n_groups;
   const int bm = tiled ? kTiledRows : (small ? kSkinnyRowsSmall : kSkinnyRows);
   const int max_tiles = max_tiles_for(q.rows_max, q.n_groups, bm);
@@ -151,8 +151,11 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.out = q.h;
   p.N = q.I;
   p.Kd = q.a8 && tiled ? q.H / 2 : q.H;
+  p.gu = q.gu;
+  if (q.gu && (q.w8 || q.a8)) return hipErrorInvalidValue;
   if (tiled)
-    e = launch_tiled(q.a8 ? kEpiSwiglu88 : (q.w8 ? kEpiSwiglu8 : kEpiSwiglu), p, max_tiles, stream);
+    e = launch_tiled(q.a8 ? kEpiSwiglu88 : (q.w8 ? kEpiSwiglu8 : (q.gu ? kEpiSwigluSave : kEpiSwiglu)),
+                     p, max_tiles, stream);
   else
     e = launch_skinny(true, q.w8, q.a8, p, max_tiles, bm, stream);
   if (e != hipSuccess) return e;

@@ -50,6 +50,8 @@ struct GroupedParams {
   // are row k of its W0* matrix ([k_w0][N] per group), the others row k - k_w0 of its W1*
   // matrix ([Kd - k_w0][N] per group). A multiple of 64.
   int32_t k_w0;
+  // kEpiSwigluSave: [rows, 2N] fp32, the gate sums in columns [0, N) and the up sums in [N, 2N)
+  float* gu;
 };
 
 
@@ -78,8 +80,11 @@ constexpr int kTiledRows = 320;
 // kEpiBf16T: kEpiBf16 over weights stored with the output columns contiguous ([Kd][N], see
 // k_w0), as the data gradients of the backward pass read them: out = A W. The weight tile lands
 // in LDS as it lies in memory and the MFMA operands are read from it with the LDS transpose read.
+// kEpiSwigluSave: kEpiSwiglu that also stores the fp32 gate and up sums (gu), which the
+// backward pass then reads instead of recomputing them.
 enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3, kEpiSwiglu8 = 4,
-                kEpiBf16_8 = 5, kEpiSwiglu88 = 6, kEpiBf16_88 = 7, kEpiBf16T = 8 };
+                kEpiBf16_8 = 5, kEpiSwiglu88 = 6, kEpiBf16_88 = 7, kEpiBf16T = 8,
+                kEpiSwigluSave = 9 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 }  // namespace moe

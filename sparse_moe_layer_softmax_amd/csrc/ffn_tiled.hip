@@ -138,7 +138,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   constexpr bool A8 = EPI == kEpiSwiglu88 || EPI == kEpiBf16_88;  // FP8 weights and activations
   constexpr bool BT = EPI == kEpiBf16T;  // weights [Kd][N], read with the LDS transpose read
   constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8 ||
-                         EPI == kEpiSwiglu88;
+                         EPI == kEpiSwiglu88 || EPI == kEpiSwigluSave;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   // DMA instructions of this wavefront that may still be in flight when a K-tile's operands
   // must have landed: FP8 weight tiles run one K-tile further ahead (the next-but-one tile's)
@@ -485,15 +485,11 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       for (int v = 0; v < 16; ++v) {
         const int r = rbase + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (r >= r1) continue;
-        const float gv = acc[i][0][v], uv = acc[i][1][v];
-        const float gc = L > 0.f ? fminf(fmaxf(gv, -L), L) : gv;
-        const float uc = L > 0.f ? fminf(fmaxf(uv, -L), L) : uv;
-        const float sg = 1.f / (1.f + expf(-gc));
-        const float dhv = bf16_to_f32(p.dh[static_cast<size_t>(r) * p.N + c]);
-        const bool pg = !(L > 0.f) || (gv >= -L && gv <= L);
-        const bool pu = !(L > 0.f) || (uv >= -L && uv <= L);
-        p.out[r * ld + c] = f32_to_bf16(pg ? dhv * uc * (sg * (1.f + gc * (1.f - sg))) : 0.f);
-        p.out[r * ld + p.N + c] = f32_to_bf16(pu ? dhv * (gc * sg) : 0.f);
+        float dg, du;
+        swiglu_bwd(acc[i][0][v], acc[i][1][v], bf16_to_f32(p.dh[static_cast<size_t>(r) * p.N + c]),
+                   L, dg, du);
+        p.out[r * ld + c] = f32_to_bf16(dg);
+        p.out[r * ld + p.N + c] = f32_to_bf16(du);
       }
     return;
   }
@@ -543,6 +539,37 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     }
     // one fragment row at a time: keeps the scheduler from reading every accumulator at once
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (EPI == kEpiSwigluSave) {
+    // the fp32 gate and up sums: each fragment row (32 rows x 32 gate + 32 up columns) goes
+    // through a private 8 KB LDS buffer, as in the fp32 epilogue, for 16-byte row stores
+    __syncthreads();  // every wavefront has left its bf16 staging buffers
+    const int c0 = nb * 128 + quarter * 32;
+    const size_t ldg = 2 * static_cast<size_t>(p.N);
+    auto foff = [](int row, int col) {
+      return row * 64 + (((col >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (col & 3);
+    };
+#pragma unroll
+    for (int i = 0; i < MIV; ++i) {
+      float* fp = reinterpret_cast<float*>(smem) + (wave * 2 + (i & 1)) * 32 * 64;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) fp[foff(row, j * 32 + fr)] = acc[i][j][v];
+      }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int row = it * 4 + (lane >> 4);
+        const int ch = lane & 15;  // chunks 0..7: gate columns, 8..15: up columns
+        const f32x4_t val = *reinterpret_cast<const f32x4_t*>(&fp[foff(row, ch * 4)]);
+        const int r = rbase + i * 32 + row;
+        const int col = ch < 8 ? c0 + ch * 4 : p.N + c0 + (ch - 8) * 4;
+        if (r < r1)
+          __builtin_nontemporal_store(val, reinterpret_cast<f32x4_t*>(p.gu + static_cast<size_t>(r) * ldg + col));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -644,6 +671,7 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
   switch (epi) {
     case kEpiSwiglu: return tiled_launch<kEpiSwiglu>(p, p.N / 128, max_tiles, stream);
     case kEpiSwigluBwd: return tiled_launch<kEpiSwigluBwd>(p, p.N / 128, max_tiles, stream);
+    case kEpiSwigluSave: return tiled_launch<kEpiSwigluSave>(p, p.N / 128, max_tiles, stream);
     case kEpiSwiglu8: return tiled_launch<kEpiSwiglu8>(p, p.N / 128, max_tiles, stream);
     case kEpiBf16_8: return tiled_launch<kEpiBf16_8>(p, p.N / kTN, max_tiles, stream);
     case kEpiSwiglu88: return tiled_launch<kEpiSwiglu88>(p, p.N / 128, max_tiles, stream);

@@ -44,6 +44,21 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(u32x4_t a, u32x4_t b, f32x16_t 
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Gradients of the clamped SwiGLU h = silu(clamp(g, +-L)) * clamp(u, +-L) at the fp32 sums g, u
+// given dh (no clamp for L <= 0): dg = dh clamp(u) silu'(clamp g), passed only where
+// -L <= g <= L, and du = dh silu(clamp g), passed only where -L <= u <= L. One definition for
+// every kernel that forms them, so they agree bit for bit.
+__device__ __forceinline__ void swiglu_bwd(float gv, float uv, float dhv, float L, float& dg,
+                                           float& du) {
+  const float gc = L > 0.f ? fminf(fmaxf(gv, -L), L) : gv;
+  const float uc = L > 0.f ? fminf(fmaxf(uv, -L), L) : uv;
+  const float sg = 1.f / (1.f + expf(-gc));
+  const bool pg = !(L > 0.f) || (gv >= -L && gv <= L);
+  const bool pu = !(L > 0.f) || (uv >= -L && uv <= L);
+  dg = pg ? dhv * uc * (sg * (1.f + gc * (1.f - sg))) : 0.f;
+  du = pu ? dhv * (gc * sg) : 0.f;
+}
+
 typedef uint32_t u32x8_t __attribute__((ext_vector_type(8)));
 
 // D(32x32) += A(32x64) * B(64x32) on FP8 E4M3 codes (the gfx950 FP8 MFMA; the block scales it

@@ -79,6 +79,11 @@ struct FfnProblem {
   float* sx;
   uint8_t* hq;
   float* sh;
+  // bf16 weights only: when set, the gate/up projection also stores its fp32 gate and up sums,
+  // [rows_max, 2I] (gate in columns [0, I), up in [I, 2I)), and both projections take the tiled
+  // kernel, whatever the rows per group, so that the sums are the ones the backward's recompute
+  // would form
+  float* gu;
 };
 // ev (may be NULL): three events recorded after the tile table, the gate/up GEMM and the
 // down GEMM (each entry may be NULL).
@@ -117,7 +122,8 @@ struct BwdProblem {
   // weight-gradient operands with the rows contiguous (ld = backward_ktile_ld(rows, G)):
   uint16_t *dyT, *hT, *dguT, *xgT;    // [H][ld], [I][ld], [2I][ld], [H][ld]
   int32_t *ktiles, *kt;               // K-tile table of 64-row tiles, [2G] per-group ranges
-  float* router_part;                 // [router_splits(T), E, H] fp32 partial planes of dWr
+  float* router_part;
+  const float* gu;                    // the forward's fp32 gate/up sums [rows, 2I], or NULL (recompute)                 // [router_splits(T), E, H] fp32 partial planes of dWr
   // outputs
   float *d_topk_w, *d_logits;         // [T, K], [T, E]
   uint16_t* d_x;                      // [T, H]

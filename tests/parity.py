@@ -163,11 +163,12 @@ def host(wts: dict) -> dict:
     return out
 
 
-def run_layer_gpu(wl, dev: dict):
-    """moe_layer_forward on the GPU; returns host copies of out and every intermediate."""
+def run_layer_gpu(wl, dev: dict, train: bool = False):
+    """moe_layer_forward (train: moe_layer_forward_train) on the GPU; returns host copies of out
+    and every intermediate."""
     shape = moe.Shape.of(wl)
     layer = moe.MoELayer.from_inputs(shape, dev)
-    out = layer.forward(dev["x"])
+    out = layer.forward(dev["x"], train=train)
     torch.cuda.synchronize()
     T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
     n_id = T if wl.n_shared else 0

@@ -1,6 +1,7 @@
 """GPU parity of the layer backward (moe_layer_backward) against the oracle, through the C ABI.
 
-The forward runs first (moe_layer_forward); the backward reads its workspace. Comparisons are
+The forward runs first (moe_layer_forward, or moe_layer_forward_train, which also stores the
+fp32 gate/up sums for the backward); the backward reads its workspace. Comparisons are
 chained, as for the forward: every stage of the GPU backward is compared with the oracle's step
 applied to the same inputs the GPU stage consumed (its own dy, dh, dg/du, d logits):
   * bf16 tensors (dy, dh, dg, du, per-row dx, dx): |gpu - oracle| <= 1e-2 |oracle| + 1e-3 rms.
@@ -62,14 +63,20 @@ def _close_sum(got, ref, abs_sum, steps, what):
         what, bad.sum(), bad.size, err[bad].max(), tol[bad][np.argmax(err[bad])])
 
 
-def _run(wl, d_aux):
+def _dout(wl):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(1000 * wl.seed + 77)
+    return torch.randn(wl.T, wl.H, generator=gen, device=DEV).to(torch.bfloat16)
+
+
+def _run(wl, d_aux, train=False):
+    """Forward (train: moe_layer_forward_train, whose stored gate/up sums the backward then
+    reads), backward, and host copies of every stage."""
     dev = generate(wl, DEV)
     s = moe.Shape.of(wl)
     layer = moe.MoELayer.from_inputs(s, dev)
-    layer.forward(dev["x"])
-    gen = torch.Generator(device=DEV)
-    gen.manual_seed(1000 * wl.seed + 77)
-    dout = torch.randn(wl.T, wl.H, generator=gen, device=DEV).to(torch.bfloat16)
+    layer.forward(dev["x"], train=train)
+    dout = _dout(wl)
     g = layer.backward(dout, d_aux)
     torch.cuda.synchronize()
     T, E, K, H, I = wl.T, wl.E, wl.K, wl.H, wl.I
@@ -103,6 +110,57 @@ def test_layer_backward_small(name):
     wl, d_aux = CASES[name]
     dev, hw, dout, fw, bw, gg = _run(wl, d_aux)
     check_backward(wl, d_aux, hw, dout, fw, bw, gg)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_layer_backward_small_stored_gate_up(name):
+    """The same chained checks with the gate/up sums that moe_layer_forward_train stored."""
+    assert torch.cuda.is_available()
+    wl, d_aux = CASES[name]
+    dev, hw, dout, fw, bw, gg = _run(wl, d_aux, train=True)
+    check_backward(wl, d_aux, hw, dout, fw, bw, gg)
+
+
+@pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "aux_ragged_t130_h256_e256_k8",
+                                  "capacity_drops_t200_e8_k2", "clamp_forced_t128",
+                                  "dense_e1_k1_t100"])
+def test_stored_gate_up_equals_recompute(name):
+    """moe_layer_forward_train: its output passes the forward's parity checks against the oracle
+    (it takes the tiled kernel at every shape), and the backward's gradients from its stored
+    gate/up sums equal, bit for bit, the gradients of the recompute on the same forward
+    workspace: the stored sums are the recompute's own."""
+    assert torch.cuda.is_available()
+    wl, d_aux = CASES[name]
+    dev = generate(wl, DEV)
+    hw = P.host(dev)
+    g, layer, _ = P.run_layer_gpu(wl, dev, train=True)
+    P.compare_layer(wl, hw, g, P.oracle_same_logits(wl, hw, g["logits"]))
+    assert layer._gu is not None
+    dout = _dout(wl)
+    rows = wl.T * wl.K + (wl.T if wl.n_shared else 0)
+    host = lambda gr: {k: (as_u16(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())
+                       for k, v in gr.items()}
+    stored = host(layer.backward(dout, d_aux))
+    dgu_stored = as_u16(layer.bwd_intermediate("dgu", torch.bfloat16, (rows, 2 * wl.I)))
+    layer._gu = None  # the same workspace, g and u recomputed
+    recomputed = host(layer.backward(dout, d_aux))
+    dgu_re = as_u16(layer.bwd_intermediate("dgu", torch.bfloat16, (rows, 2 * wl.I)))
+    R = int(g["offsets"][-1]) + (wl.T if wl.n_shared else 0)
+    np.testing.assert_array_equal(dgu_stored[:R], dgu_re[:R], err_msg="dg | du")
+    for k in stored:
+        np.testing.assert_array_equal(stored[k], recomputed[k], err_msg=k)
+
+
+def test_forward_train_rejects_null_gate_up():
+    assert torch.cuda.is_available()
+    wl = BASE
+    dev = generate(wl, DEV)
+    s = moe.Shape.of(wl)
+    layer = moe.MoELayer.from_inputs(s, dev)
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    wr, b, wg, wu, wd, sg, su, sd = layer.w
+    with pytest.raises(RuntimeError):
+        moe.moe_layer_forward_train(s, dev["x"], wr, b, wg, wu, wd, sg, su, sd, out, None, layer.ws)
 
 
 def check_backward(wl, d_aux, hw, dout, fw, bw, gg):
