@@ -151,6 +151,31 @@ def test_stored_gate_up_equals_recompute(name):
         np.testing.assert_array_equal(stored[k], recomputed[k], err_msg=k)
 
 
+@pytest.mark.timeout(600)
+def test_stored_gate_up_equals_recompute_full_size():
+    """hy4_prefill_t8192 at full size: the backward from moe_layer_forward_train's stored gate/up
+    sums equals, bit for bit, the backward that recomputes them on the same forward workspace,
+    and the training forward's output equals the plain forward's (both take the tiled kernel at
+    this shape)."""
+    assert torch.cuda.is_available()
+    wl = WORKLOADS["hy4_prefill_t8192"]
+    print("\n[stored gate/up, full size] %s T=%d" % (wl.name, wl.T), flush=True)
+    dev = generate(wl, DEV)
+    layer = moe.MoELayer.from_inputs(moe.Shape.of(wl), dev)
+    plain = as_u16(layer.forward(dev["x"]))
+    trained = as_u16(layer.forward(dev["x"], train=True))
+    np.testing.assert_array_equal(trained, plain, err_msg="out")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4243)
+    dout = torch.randn(wl.T, wl.H, generator=gen, device=DEV).to(torch.bfloat16)
+    bits = lambda v: v.view(torch.int16 if v.dtype == torch.bfloat16 else torch.int32)
+    stored = layer.backward(dout, 0.01)
+    layer._gu = None
+    recomputed = layer.backward(dout, 0.01)
+    for k in stored:  # bit patterns compared on the device (the weight gradients are 39 GB)
+        assert torch.equal(bits(stored[k]), bits(recomputed[k])), k
+
+
 def test_forward_train_rejects_null_gate_up():
     assert torch.cuda.is_available()
     wl = BASE
