@@ -136,6 +136,22 @@ def test_stored_gate_up_equals_recompute(name):
     g, layer, _ = P.run_layer_gpu(wl, dev, train=True)
     P.compare_layer(wl, hw, g, P.oracle_same_logits(wl, hw, g["logits"]))
     assert layer._gu is not None
+    # the stored sums against their definition g = x Wg^T, u = x Wu^T (fp64), within the bound
+    # of 16-wide fp32 partial sums over H
+    gu = layer.gu.cpu().numpy()
+    n_id, I, K = (wl.T if wl.n_shared else 0), wl.I, wl.K
+    x = f64(hw["x"])
+    groups = [(np.arange(n_id), np.arange(wl.T), P.shared_weights(hw))] if n_id else []
+    off, r2s = g["offsets"], g["row_to_slot"]
+    for e in range(wl.E):
+        a, b = int(off[e]), int(off[e + 1])
+        if a < b:
+            groups.append((n_id + np.arange(a, b), r2s[a:b] // K, P.routed_weights(hw, e)))
+    for rows, tok, (wg, wu, _) in groups:
+        for w, cols, what in ((wg, slice(0, I), "g"), (wu, slice(I, 2 * I), "u")):
+            wf = f64(w)
+            _close_sum(gu[rows, cols], x[tok] @ wf.T, np.abs(x[tok]) @ np.abs(wf).T,
+                       wl.H / 16 + 16, "stored %s" % what)
     dout = _dout(wl)
     rows = wl.T * wl.K + (wl.T if wl.n_shared else 0)
     host = lambda gr: {k: (as_u16(v) if v.dtype == torch.bfloat16 else v.cpu().numpy())
