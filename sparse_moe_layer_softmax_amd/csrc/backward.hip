@@ -36,23 +36,25 @@ constexpr int kKT = 64;  // rows per K-tile of the weight gradients (the tiled k
 // Weight-gradient operands with the layer rows (their reduction dimension) contiguous:
 // dst[c][t * 64 + j] = src[row(r0_t + j)][c] for the rows of K-tile t of the tile table (rows
 // past the group's end read as 0), so each group's rows start at a multiple of 64.
-// row(r) = r, or with gather the token of layer row r (identity rows first).
+// row(r) = r, or with gather the token of layer row r (identity rows first). A workgroup moves
+// 64 rows x kKtCols columns (C a multiple of kKtCols) through LDS, 512 bytes of each source row.
+constexpr int kKtCols = 256;
 __global__ __launch_bounds__(256) void ktile_transpose_kernel(
     const uint16_t* __restrict__ src, int C, const int32_t* __restrict__ tiles, int max_tiles,
     const int32_t* __restrict__ offsets, int rows_max, const int32_t* __restrict__ gather,
     int n_ident, int topk, int ld_dst, uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][66];
+  // row pitch kKtCols + 2 (129 dwords): the column gathers below hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64][kKtCols + 2];
   const int t = blockIdx.y;
   if (t >= tiles[0]) return;
   const int g = tiles[1 + t], r0 = tiles[1 + max_tiles + t];
   const int r_end = min(offsets[g + 1], rows_max);
-  const int c0 = blockIdx.x * 64;
-  // 16-byte global accesses: thread (a, b) moves columns 8b..8b+8 of tile rows a and a + 32 in,
-  // then elements 8b..8b+8 of output rows a and a + 32 out
-  const int a = threadIdx.x >> 3, b = threadIdx.x & 7;
+  const int c0 = blockIdx.x * kKtCols;
+  // in: thread (a, b) moves columns 8b..8b+8 of tile rows a + 8p, p < 8 (16-byte loads)
+  const int a = threadIdx.x >> 5, b = threadIdx.x & 31;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int i = pass * 32 + a;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int i = pass * 8 + a;
     const int r = r0 + i;
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (r < r_end) {
@@ -64,16 +66,18 @@ __global__ __launch_bounds__(256) void ktile_transpose_kernel(
     for (int m = 0; m < 4; ++m) tp[m] = v[m];
   }
   __syncthreads();
+  // out: thread (o, q) writes elements 8q..8q+8 of output rows (source columns) c0 + o + 32p
+  const int q = threadIdx.x & 7, o0 = threadIdx.x >> 3;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int o = pass * 32 + a;  // output row = source column c0 + o
+  for (int pass = 0; pass < 8; ++pass) {
+    const int o = pass * 32 + o0;
     u32x4_t w;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
-      w[m] = static_cast<uint32_t>(tile[8 * b + 2 * m][o]) |
-             (static_cast<uint32_t>(tile[8 * b + 2 * m + 1][o]) << 16);
+      w[m] = static_cast<uint32_t>(tile[8 * q + 2 * m][o]) |
+             (static_cast<uint32_t>(tile[8 * q + 2 * m + 1][o]) << 16);
     *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(c0 + o) * ld_dst +
-                                static_cast<size_t>(t) * kKT + 8 * b) = w;
+                                static_cast<size_t>(t) * kKT + 8 * q) = w;
   }
 }
 
@@ -499,7 +503,7 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     if ((e = launch_build_tiles(b.grp_offsets, G, kKT, mtk, b.ktiles, stream)) != hipSuccess) return e;
     hipLaunchKernelGGL(group_ktiles_kernel, dim3(1), dim3(1), 0, stream, b.grp_offsets, G, b.kt);
     auto ktr = [&](const uint16_t* src, int C, const int32_t* gather, uint16_t* dst) {
-      hipLaunchKernelGGL(ktile_transpose_kernel, dim3(C / 64, mtk), dim3(256), 0, stream, src, C,
+      hipLaunchKernelGGL(ktile_transpose_kernel, dim3(C / kKtCols, mtk), dim3(256), 0, stream, src, C,
                          b.ktiles, mtk, b.grp_offsets, rows_max, gather, n_ident, K, ldk, dst);
     };
     ktr(b.dy, H, nullptr, b.dyT);
