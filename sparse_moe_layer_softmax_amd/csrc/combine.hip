@@ -5,7 +5,8 @@
 // (routed_output + shared_output). Hy4 config walkthrough (lshu.cn), section "MoE routed
 // experts": routed_scaling_factor scales the routed part only (already folded into topk_w).
 //
-// One workgroup per (token, column block); each thread owns 8 consecutive columns (16-byte
+// One workgroup per token (H / 8 threads, up to 1024; wider rows in 2048-column blocks), so each
+// gathered row is read whole by one workgroup; each thread owns 8 consecutive columns (16-byte
 // loads and stores). The sum runs in fp32 in slot order j = 0..K-1, then the shared row, and is
 // rounded to bf16 once, so the result does not depend on scheduling.
 #include "moe_device.h"
@@ -16,12 +17,12 @@ namespace {
 
 constexpr int kCombineThreads = 256;
 
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+__global__ __launch_bounds__(1024) void combine_kernel(
     const uint16_t* __restrict__ y_routed, const float* __restrict__ topk_w,
     const int32_t* __restrict__ slot_to_row, const uint16_t* __restrict__ y_shared,
     uint16_t* __restrict__ out, int H, int K) {
   const int t = blockIdx.x;
-  const int c = (blockIdx.y * kCombineThreads + threadIdx.x) * 8;
+  const int c = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
   if (c >= H) return;
   float acc[8];
 #pragma unroll
@@ -56,9 +57,12 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
 hipError_t launch_combine(const moe_shape& s, const uint16_t* y_routed, const float* topk_w,
                           const int32_t* slot_to_row, const uint16_t* y_shared, uint16_t* out,
                           hipStream_t stream) {
-  const int cols_per_block = kCombineThreads * 8;
+  // one workgroup per token when its row fits (H / 8 <= 1024 threads): each gathered row is then
+  // read whole by one workgroup
+  const int threads = s.H / 8 <= 1024 ? s.H / 8 : kCombineThreads;
+  const int cols_per_block = threads * 8;
   dim3 grid(s.T, (s.H + cols_per_block - 1) / cols_per_block);
-  hipLaunchKernelGGL(combine_kernel, grid, dim3(kCombineThreads), 0, stream, y_routed, topk_w,
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(threads), 0, stream, y_routed, topk_w,
                      slot_to_row, y_shared, out, s.H, s.K);
   return hipGetLastError();
 }
