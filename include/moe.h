@@ -36,7 +36,12 @@
  *    Faults inside kernels surface at the caller's next synchronisation (HIP convention).
  *  - Inputs must be finite. Results are deterministic: the same inputs give the same bits.
  *  - Supported shapes: 1 <= K <= 16, K <= E <= 256, H and I multiples of 256, T >= 1 with
- *    T*K < 2^31. Others return MOE_ERR_UNSUPPORTED.
+ *    T*(K+1) < 2^31, and every operand that the LDS-tiled MFMA kernel reads at most 64 GiB
+ *    (it addresses rows in 16-byte units with 32-bit offsets): x [T,H], one expert matrix
+ *    [I,H], and the layer rows h [T*(K+1), I] (moe_expert_ffn: [rows_max, I]). At the Hy4 shape
+ *    that allows T <= 1,864,135. moe_layer_backward also needs dy [rows,H], [dg|du] [rows,2I]
+ *    and its row-contiguous copies [H][ld], [2I][ld] (ld about the layer row count plus 64 per
+ *    expert) within 64 GiB: T <= 619,548 at the Hy4 shape. Others return MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_H
 #define MOE_H

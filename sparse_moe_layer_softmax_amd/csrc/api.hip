@@ -13,6 +13,22 @@ using moe::align_up;
 
 namespace {
 
+// The tiled MFMA kernel addresses each operand row in 16-byte units with a 32-bit offset from the
+// operand's base: no activation or weight operand it reads may exceed 64 GiB.
+constexpr unsigned long long kMaxOperandBytes = 1ull << 36;
+
+// Bytes of a [rows, cols] bf16 operand fit the tiled kernel's addressing.
+bool operand_fits(long long rows, long long cols) {
+  return static_cast<unsigned long long>(rows) * static_cast<unsigned long long>(cols) * 2ull <=
+         kMaxOperandBytes;
+}
+
+// The forward's operands: x [T, H] (rows gathered by token), h [rows, I] with rows layer rows,
+// and one expert's weight matrix [I, H] or [H, I].
+bool forward_operands_fit(const moe_shape& s, long long rows) {
+  return operand_fits(s.T, s.H) && operand_fits(rows, s.I) && operand_fits(s.I, s.H);
+}
+
 int check_shape(const moe_shape* s) {
   if (!s) return MOE_ERR_INVALID_ARG;
   if (s->T < 1 || s->H < 1 || s->E < 1 || s->K < 1 || s->I < 1) return MOE_ERR_INVALID_ARG;
@@ -22,7 +38,9 @@ int check_shape(const moe_shape* s) {
   if (s->K > 16 || s->E > 256) return MOE_ERR_UNSUPPORTED;
   if (s->H % 256 != 0 || s->I % 256 != 0) return MOE_ERR_UNSUPPORTED;
   // row indices are int32 and rows_max = T + T*K must fit
-  if (static_cast<long long>(s->T) * (s->K + 1) >= INT_MAX) return MOE_ERR_UNSUPPORTED;
+  const long long rows = static_cast<long long>(s->T) * (s->K + 1);
+  if (rows >= INT_MAX) return MOE_ERR_UNSUPPORTED;
+  if (!forward_operands_fit(*s, rows)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -159,6 +177,7 @@ int expert_ffn_impl(const moe_shape* s, int32_t n_groups, int32_t rows_max, cons
   if (n_groups < 1 || n_groups > 1024 || rows_max < 1) return MOE_ERR_INVALID_ARG;
   if (!row_to_slot && rows_max > s->T) return MOE_ERR_INVALID_ARG;
   if (!group_offsets && n_groups != 1) return MOE_ERR_INVALID_ARG;
+  if (!forward_operands_fit(*s, rows_max)) return MOE_ERR_UNSUPPORTED;
   const FfnWs w = ffn_ws(*s, n_groups, rows_max, h == nullptr);
   if (ws_bytes < w.total || !aligned(ws)) return MOE_ERR_WORKSPACE;
   const int32_t* offs = group_offsets;
@@ -564,16 +583,27 @@ BwdWs bwd_ws(const moe_shape& s) {
   w.total = o;
   return w;
 }
+// The backward's tiled-kernel operands: dy [rows, H] and [dg | du] [rows, 2I] (data gradients),
+// and the row-contiguous copies [H][ld], [I][ld], [2I][ld] of the weight gradients, whose
+// reduction dimension ld is about the layer row count.
+bool backward_operands_fit(const moe_shape& s) {
+  const long long rows = static_cast<long long>(s.T) * s.K + (s.n_shared ? s.T : 0);
+  const long long ld = static_cast<long long>(
+                           moe::backward_ktiles(static_cast<int>(rows), s.E + s.n_shared)) * 64;
+  return operand_fits(rows, s.H) && operand_fits(rows, 2LL * s.I) && operand_fits(s.H, ld) &&
+         operand_fits(2LL * s.I, ld);
+}
 }  // namespace
 
 size_t moe_layer_backward_workspace_size(const moe_shape* s) {
-  if (check_shape(s) != MOE_OK) return 0;
+  if (check_shape(s) != MOE_OK || !backward_operands_fit(*s)) return 0;
   return bwd_ws(*s).total;
 }
 
 int moe_layer_backward_workspace_layout(const moe_shape* s, moe_bwd_ws_layout* layout) {
   const int rc = check_shape(s);
   if (rc != MOE_OK) return rc;
+  if (!backward_operands_fit(*s)) return MOE_ERR_UNSUPPORTED;
   if (!layout) return MOE_ERR_INVALID_ARG;
   const BwdWs w = bwd_ws(*s);
   layout->dy = w.dy;
@@ -606,7 +636,7 @@ int moe_layer_backward(const moe_shape* s, const uint16_t* x, const uint16_t* w_
   if (!shared && (s_gate || s_up || s_down || d_s_gate || d_s_up || d_s_down))
     return MOE_ERR_INVALID_ARG;
   if (!std::isfinite(d_aux)) return MOE_ERR_INVALID_ARG;
-  if (s->H % 128 != 0 || s->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!backward_operands_fit(*s)) return MOE_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(d_out) | reinterpret_cast<uintptr_t>(d_x) |
        reinterpret_cast<uintptr_t>(gu)) & 15u)
     return MOE_ERR_INVALID_ARG;  // 16-byte vector accesses

@@ -5,6 +5,7 @@
 // walkthrough (lshu.cn), section "MoE routed experts" (swiglu_limit, silu); Hy3 explainer
 // (tqpw.cn) section 2.1: each expert runs on the rows routed to it.
 #include <algorithm>
+#include <atomic>
 
 #include "ffn_kernels.h"
 #include "moe_device.h"
@@ -175,16 +176,19 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // fragments (fragment i = blocks 20*half + 4i .. +4). B stage: wavefront w fills blocks w+8i.
   // Every block index used here is congruent to the quarter mod 2, so a row's (row / 8) % 2 is
   // quarter % 2, and its row % 8 is lane / 8.
+  // Activation rows are addressed in 16-byte units by a 32-bit offset from A, so any row of an
+  // operand of up to 64 GiB is reachable (row * Kd passes 2^32 elements for the activations of a
+  // long prefill, e.g. h [T + T*K, I]); the host rejects larger operands.
   const int lrow = lane >> 3;
   const int lchunk = (lane & 7) ^ lrow ^ (quarter & 1);
-  uint32_t aoff[MV];
+  uint32_t a16[MV];
 #pragma unroll
   for (int i = 0; i < MIV; ++i) {
     const int r = r0 + (20 * half + quarter + 4 * i) * 8 + lrow;
     int src = 0;
     if (r < r1) src = r < p.n_ident ? r : p.gather[r - p.n_ident] / p.topk;
     if (static_cast<unsigned>(src) >= static_cast<unsigned>(p.a_rows)) src = 0;
-    aoff[i] = static_cast<uint32_t>(src) * Kd + kb * kBK + lchunk * 8;
+    a16[i] = static_cast<uint32_t>((static_cast<size_t>(src) * Kd + lchunk * 8) >> 3);
   }
   const size_t wst = static_cast<size_t>(p.N) * Kd;
   const uint16_t* W0 = g < p.g_split ? p.W0a + g * wst : p.W0b + (g - p.g_split) * wst;
@@ -196,12 +200,14 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // the weight rows a wavefront moves all come from one matrix: block w + 8i holds tile rows
   // 8(w + 8i) .. +8, whose 32-row fragment index is (w >> 2) + 2i, so for gate/up the half of
   // the wavefront picks gate (0) or up (1). Block i's weight rows are block 0's plus 32i (gate/up:
-  // wrow(b + 64i) = wrow(b) + 32i) or plus 64i (down), so one 32-bit offset and a uniform step
+  // wrow(b + 64i) = wrow(b) + 32i) or plus 64i (down), so one row address and a uniform step
   // address all of them.
   const uint16_t* Wb = GATED && half ? W1 : W0;
   const size_t bstep = static_cast<size_t>(GATED ? 32 : 64) * Kd;
-  uint32_t boff0 = 0;
-  if (!W8 && !BT) boff0 = static_cast<uint32_t>(wrow(wave * 8 + lrow)) * Kd + kb * kBK + lchunk * 8;
+  // weight rows likewise in 16-byte units from Wb (the weight gradients' B operands, [N][K] with
+  // K about 9T, pass 2^32 elements at long prefills)
+  uint32_t b16 = 0;
+  if (!W8 && !BT) b16 = static_cast<uint32_t>((static_cast<size_t>(wrow(wave * 8 + lrow)) * Kd + lchunk * 8) >> 3);
   // W8: a B stage is [256 rows][64 codes]; a 1 KB DMA block holds 16 rows. Lane i fills row
   // i/4 of the block, physical 16-byte chunk i%4, which holds logical chunk
   // (i%4) ^ ((row / 4) % 4); wavefront w fills blocks w + 8i, i < 2.
@@ -223,7 +229,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   // (i % 32) ^ tsw(row); the wavefront's four blocks lie 16 rows apart, which tsw ignores.
   const uint16_t* V0 = nullptr;
   const uint16_t* V1 = nullptr;
-  uint32_t btoff = 0;
+  uint32_t btoff = 0;  // within 16 k-rows of one K-tile: < 16 N
   if constexpr (BT) {
     const size_t s0 = static_cast<size_t>(p.k_w0) * p.N, s1 = static_cast<size_t>(Kd - p.k_w0) * p.N;
     V0 = g < p.g_split ? p.W0a + g * s0 : p.W0b + (g - p.g_split) * s0;
@@ -234,7 +240,8 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   auto dma_a = [&](int kt, int stage) {
 #pragma unroll
     for (int i = 0; i < MIV; ++i)
-      lds_dma16(p.A + aoff[i] + kt * kBK,
+      lds_dma16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const u32x4_t*>(p.A) + a16[i]) +
+                    (kb + kt) * kBK,
                 sA + stage * kStageA + (20 * half + quarter + 4 * i) * 512);
   };
   auto dma_b = [&](int kt, int stage) {
@@ -253,7 +260,9 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     } else {
 #pragma unroll
       for (int i = 0; i < kDmaB; ++i)
-        lds_dma16<true>(Wb + i * bstep + boff0 + kt * kBK, sB + stage * kStageB + (wave + 8 * i) * 512);
+        lds_dma16<true>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const u32x4_t*>(Wb + i * bstep) + b16) +
+                            (kb + kt) * kBK,
+                        sB + stage * kStageB + (wave + 8 * i) * 512);
     }
   };
 
@@ -642,14 +651,16 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
 }
 
 
-// One-time opt-in to the large dynamic LDS allocation of a tiled kernel instantiation.
+// Opt-in to the large dynamic LDS allocation of a tiled kernel instantiation. Calls may come
+// from several host threads at once (one per stream): the flag is atomic, and a repeated opt-in
+// by two first callers is harmless (the attribute is simply set twice to the same value).
 template <int EPI>
 hipError_t tiled_prepare() {
-  static bool done = false;
-  if (done) return hipSuccess;
+  static std::atomic<bool> done{false};
+  if (done.load(std::memory_order_acquire)) return hipSuccess;
   const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_tiled_kernel<EPI>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, kSmem);
-  if (e == hipSuccess) done = true;
+  if (e == hipSuccess) done.store(true, std::memory_order_release);
   return e;
 }
 

@@ -170,3 +170,57 @@ def test_binding_argument_counts_match_the_header(m):
         n = 0 if decl.strip() in ("", "void") else decl.count(",") + 1
         fn = getattr(lib, name)
         assert fn.argtypes is not None and len(fn.argtypes) == n, (name, n, fn.argtypes)
+
+
+# The LDS-tiled MFMA kernel reaches operand rows through 32-bit offsets in 16-byte units, so no
+# operand it reads may pass 64 GiB; the host rejects larger shapes (MOE_ERR_UNSUPPORTED) before
+# any launch. The thresholds below are the exact largest token counts at the Hy4 shape.
+FWD_T_MAX = (1 << 36) // (2 * 9 * 2048)   # h [T*(K+1), I] bf16 at K = 8, I = 2048
+
+
+def _bwd_t_max(H=6144, I=2048, E=256, K=8):
+    def fits(T):
+        rows = T * (K + 1)
+        ld = ((rows + 63) // 64 + E + 1) * 64  # row-contiguous copies of the weight gradients
+        lim = 1 << 36
+        return rows * H * 2 <= lim and rows * 2 * I * 2 <= lim and H * ld * 2 <= lim and 2 * I * ld * 2 <= lim
+    lo, hi = 1, 1 << 24
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if fits(mid) else (lo, mid - 1)
+    return lo
+
+
+def test_operand_size_limit_forward(m):
+    assert FWD_T_MAX == 1864135  # the figure the header states
+    ok = m.Shape(**dict(HY4, T=FWD_T_MAX))
+    big = m.Shape(**dict(HY4, T=FWD_T_MAX + 1))
+    assert m.moe_layer_workspace_size(ok) > 0
+    assert m.moe_layer_workspace_size(big) == 0
+    assert _call_route(m, big) == m.MOE_ERR_UNSUPPORTED
+    assert _call_route(m, ok) != m.MOE_ERR_UNSUPPORTED
+    # moe_expert_ffn checks its own row bound: rows_max * I * 2 bytes <= 64 GiB
+    s = m.Shape(**dict(HY4, T=1 << 20, K=1))
+    rmax = (1 << 36) // (2 * 2048)
+    assert m.moe_expert_ffn_workspace_size(s, 1, rmax) > 0
+    lib = m.library()
+    sc = ctypes.byref(s.c())
+    args = (16, 16, 16, 16, 16, 16, None, 16, 256, 1 << 60, None)
+    assert lib.moe_expert_ffn(sc, 1, rmax + 1, *args) == m.MOE_ERR_UNSUPPORTED
+    # x [T, H] alone past 64 GiB
+    wide = m.Shape(**dict(HY4, T=(1 << 36) // (2 * 6144) + 1, K=1, E=1, n_shared=0))
+    assert m.moe_layer_workspace_size(wide) == 0
+
+
+def test_operand_size_limit_backward(m):
+    tb = _bwd_t_max()
+    assert tb == 619548  # the figure the header states
+    assert m.moe_layer_backward_workspace_size(m.Shape(**dict(HY4, T=tb))) > 0
+    assert m.moe_layer_backward_workspace_size(m.Shape(**dict(HY4, T=tb + 1))) == 0
+    # the forward alone still accepts that size
+    assert m.moe_layer_workspace_size(m.Shape(**dict(HY4, T=tb + 1))) > 0
+    lib = m.library()
+    sc = ctypes.byref(m.Shape(**dict(HY4, T=tb + 1)).c())
+    rc = lib.moe_layer_backward(sc, 16, 16, 16, 16, 16, 16, 16, 16, 256, 1 << 60, None, 16, 0.0,
+                                16, 16, 16, 16, 16, 16, 16, 16, None, None, 256, 1 << 60, None)
+    assert rc == m.MOE_ERR_UNSUPPORTED
