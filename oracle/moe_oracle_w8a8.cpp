@@ -12,10 +12,11 @@
 //   amax  = max_c |v[c]|                      (v: the row's bf16 values, as fp32)
 //   scale = amax / 448, inv = 448 / amax      (fp32, each one correctly rounded division)
 //   code  = E4M3_RNE(clamp(v[c] * inv, -448, 448))   (fp32 product, then nearest-even E4M3)
-//   an all-zero row has scale 1 and zero codes
+//   a row whose 448 / amax overflows fp32 (amax > 0 below 448 / FLT_MAX, about 1.3e-36) and an
+//   all-zero row are quantised unscaled: scale 1, code = E4M3_RNE(v[c]) (all zero codes there)
 // and computes each projection as (sum_k e4m3(a_code[k]) * e4m3(w_code[k])) * w_scale * a_scale
 // with the code products summed sequentially in fp64 (each product of two E4M3 values is
-// exact), then rounded where the bf16 path rounds (h, y).
+// exact), rounded to an fp32 value, then rounded where the bf16 path rounds (h, y).
 
 #include "moe_oracle.h"
 
@@ -88,10 +89,13 @@ void oracle_quant_rows_e4m3(int rows, int cols, const uint16_t* v, uint8_t* code
       const float a = std::fabs(bf32(vr[c]));
       if (a > amax) amax = a;
     }
-    float inv = 0.f, scale = 1.f;
+    float inv = 1.f, scale = 1.f;
     if (amax > 0.f) {
-      inv = 448.0f / amax;
-      scale = amax / 448.0f;
+      const float q = 448.0f / amax;
+      if (std::isfinite(q)) {  // else the row is below what a scaled E4M3 code can reach
+        inv = q;
+        scale = amax / 448.0f;
+      }
     }
     scales[r] = scale;
     uint8_t* cr = codes + static_cast<size_t>(r) * cols;
@@ -120,9 +124,10 @@ void oracle_gateup_rows_w8a8(int n, int H, int I, double limit, const uint8_t* x
       g += av * e4m3_value(wg[k]);
       u += av * e4m3_value(wu[k]);
     }
-    g = g * static_cast<double>(cg[i]) * static_cast<double>(sx[r]);
-    u = u * static_cast<double>(cu[i]) * static_cast<double>(sx[r]);
-    h[static_cast<size_t>(r) * I + i] = oracle_bf16_from_double(clamped_swiglu(g, u, limit));
+    // the scaled projections as fp32 values, as in the bf16 form
+    const double g32 = static_cast<float>(g * static_cast<double>(cg[i]) * static_cast<double>(sx[r]));
+    const double u32 = static_cast<float>(u * static_cast<double>(cu[i]) * static_cast<double>(sx[r]));
+    h[static_cast<size_t>(r) * I + i] = oracle_bf16_from_double(clamped_swiglu(g32, u32, limit));
   }
 }
 
@@ -138,7 +143,7 @@ void oracle_down_rows_w8a8(int n, int H, int I, const uint8_t* hq, const float* 
     double s = 0.0;
     for (int i = 0; i < I; ++i) s += e4m3_value(a[i]) * e4m3_value(w[i]);
     s = s * static_cast<double>(cd[c]) * static_cast<double>(sh[r]);
-    y[static_cast<size_t>(r) * H + c] = oracle_bf16_from_double(s);
+    y[static_cast<size_t>(r) * H + c] = oracle_bf16_from_double(static_cast<float>(s));
   }
 }
 

@@ -4,13 +4,17 @@
 // The pages deploy the model from an FP8 checkpoint (Tencent Hunyuan Hy4 Preview deep technical
 // analysis, deployment commands) without defining the format. Each row v gets
 //   amax = max |v|,  scale = amax / 448,  code = E4M3_RNE(clamp(v * (448 / amax), +-448))
-// (both divisions correctly rounded fp32, the product one fp32 multiply; an all-zero row gets
-// scale 1 and zero codes), so the row is scale * e4m3(code) to within half an E4M3 step.
+// (both divisions correctly rounded fp32, the product one fp32 multiply), so the row is
+// scale * e4m3(code) to within half an E4M3 step. An all-zero row, and a row so small that
+// 448 / amax overflows fp32 (amax below 448 / FLT_MAX, about 1.3e-36), is quantised unscaled:
+// scale 1 and code = E4M3_RNE(v), which is a zero code for every such value.
 //
 // One wavefront per row, two passes over it (the second one hits L2): the absolute maximum by
 // a wavefront max-reduction (exact, order-free), then eight values per lane and step turned
 // into codes by the hardware conversion v_cvt_pk_fp8_f32 (nearest-even) and stored as one
 // 8-byte segment per lane.
+#include <float.h>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -46,10 +50,13 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  float inv = 0.f, scale = 1.f;
+  float inv = 1.f, scale = 1.f;
   if (amax > 0.f) {
-    inv = __fdiv_rn(448.f, amax);
-    scale = __fdiv_rn(amax, 448.f);
+    const float q = __fdiv_rn(448.f, amax);
+    if (q <= FLT_MAX) {  // else (+inf) the row is below what a scaled E4M3 code can reach
+      inv = q;
+      scale = __fdiv_rn(amax, 448.f);
+    }
   }
   if (lane == 0) scales[r] = scale;
   uint8_t* cr = codes + static_cast<size_t>(r) * cols;

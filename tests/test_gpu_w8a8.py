@@ -52,6 +52,11 @@ def _quant_cases():
     row = np.concatenate([row, np.zeros((-len(row)) % 8)])
     cases["ties_%d" % len(row)] = np.stack([row, -row, row * 0.5 + 0.0])
     cases["narrow_8"] = rng.standard_normal((5, 8))
+    # rows so small that 448 / amax overflows fp32 (quantised unscaled to signed-zero codes),
+    # rows around that threshold and rows whose scale amax / 448 is an fp32 subnormal
+    tiny = rng.standard_normal((6, 64))
+    tiny *= np.array([1e-37, 1e-36, 1.3e-36, 1.4e-36, 3e-36, 1e-35])[:, None] / np.abs(tiny).max(1, keepdims=True)
+    cases["tiny_rows_64"] = tiny
     cases["odd_520"] = rng.standard_normal((9, 520)) * 3.0
     return cases
 

@@ -107,6 +107,26 @@ def test_quant_rows_properties(orc):
     np.testing.assert_array_equal(c2, codes ^ np.uint8(0x80))
 
 
+def test_quant_rows_tiny_rows_are_unscaled(orc):
+    """A row whose 448 / amax overflows fp32 is quantised with scale 1 and E4M3_RNE(v): at those
+    magnitudes (below 448 / FLT_MAX, about 1.3e-36, far under the smallest E4M3 subnormal 2^-9)
+    every code is a signed zero, and nothing is NaN or saturated. Rows just above the threshold
+    keep the scaled form, so the row maximum still maps to code 0x7E."""
+    cols = 16
+    tiny = np.array([1e-38, -3e-37, 2.0 ** -133, -(2.0 ** -126), 0.0, -0.0, 1.2e-36, 5e-37] * 2)
+    just_above = np.linspace(-1.0, 1.0, cols) * 2e-36       # amax 2e-36: 448 / amax is finite
+    v = torch.from_numpy(np.stack([tiny, just_above])).to(torch.bfloat16)
+    v16 = v.view(torch.int16).numpy().view(np.uint16)
+    codes, scales = orc.quant_rows_e4m3(v16)
+    x = v.to(torch.float64).numpy()
+    assert scales[0] == 1.0
+    np.testing.assert_array_equal(codes[0], np.where(np.signbit(x[0]), 0x80, 0x00).astype(np.uint8))
+    amax = np.float32(np.abs(x[1]).max())
+    assert np.isfinite(np.float32(448.0) / amax)
+    assert scales[1] == amax / np.float32(448.0)
+    assert (codes[1][np.abs(x[1]).argmax()] & 0x7F) == 0x7E
+
+
 def _exact_rows(rng, rows, cols, exps):
     """bf16 rows whose values are E4M3 values times 2^k (k per row) with the row maximum exactly
     448 * 2^k, so that quantisation is exact: codes back, scale 2^k. Returns (bf16 rows, codes,
