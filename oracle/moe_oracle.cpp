@@ -3,8 +3,12 @@
 // TEST INFRASTRUCTURE: loaded only by the tests, the smoke check and the CPU-baseline leg of
 // the benchmark. Written from the pages' statement of the layer (see moe_oracle.h for the
 // source list); it shares nothing with the HIP library. Every dot product is a sequential
-// double-precision sum; bf16 rounding happens only where the layer stores bf16 tensors
-// (h, y, y_shared, out), with this file's own round-to-nearest-even.
+// double-precision sum. The layer's projections produce fp32 values (the pages' checkpoint is
+// bf16 and its matrix products accumulate in fp32): the router logits, the gate and up
+// pre-activations g, u and the down projection are each the fp32 rounding of their double sum,
+// and the router bias is an fp32 add to the fp32 logit. bf16 rounding happens only where the
+// layer stores bf16 tensors (h, y, y_shared, out), with this file's own round-to-nearest-even;
+// the SwiGLU of the fp32 g, u and the combine are evaluated in double.
 //
 // Parity pins live in tests/test_oracle_*.py (bf16 bit patterns, softmax closed forms, tie
 // order, counting-sort vs a library stable sort, dense-vs-sparse, E=1/k=1 vs a float64 SwiGLU
@@ -105,7 +109,9 @@ static void gateup_impl(int n, int H, int I, double limit, const uint16_t* x_row
       g += xv * wg(i, k);
       u += xv * wu(i, k);
     }
-    h[static_cast<size_t>(r) * I + i] = oracle_bf16_from_double(clamped_swiglu(g, u, limit));
+    // g and u are fp32 values: the fp32 rounding of the exact projections
+    const double g32 = static_cast<float>(g), u32 = static_cast<float>(u);
+    h[static_cast<size_t>(r) * I + i] = oracle_bf16_from_double(clamped_swiglu(g32, u32, limit));
   }
 }
 
@@ -118,7 +124,8 @@ static void down_impl(int n, int H, int I, const uint16_t* h, W wd, uint16_t* y)
     const uint16_t* hr = h + static_cast<size_t>(r) * I;
     double s = 0.0;
     for (int i = 0; i < I; ++i) s += bf(hr[i]) * wd(c, i);
-    y[static_cast<size_t>(r) * H + c] = oracle_bf16_from_double(s);
+    // the fp32 projection, stored as bf16
+    y[static_cast<size_t>(r) * H + c] = oracle_bf16_from_double(static_cast<float>(s));
   }
 }
 
@@ -296,8 +303,10 @@ void oracle_router_logits(int T, int H, int E, const uint16_t* x, const uint16_t
       double s = 0.0;
       for (int h = 0; h < H; ++h)
         s += bf(x[static_cast<size_t>(t) * H + h]) * bf(wr[static_cast<size_t>(e) * H + h]);
-      if (bias) s += static_cast<double>(bias[e]);
-      logits[static_cast<size_t>(t) * E + e] = static_cast<float>(s);
+      // the fp32 logit, then the bias as an fp32 add
+      float l = static_cast<float>(s);
+      if (bias) l = l + bias[e];
+      logits[static_cast<size_t>(t) * E + e] = l;
     }
   }
 }

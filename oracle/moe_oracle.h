@@ -35,8 +35,9 @@ uint16_t oracle_bf16_from_double(double v);
 double oracle_double_from_bf16(uint16_t b);
 
 /* Router projection, [Hy4-deep-dive] `MoERouter.gate` (a bias-free linear map hidden -> experts)
- * and [Hy3-deep-dive] `self.gate(x_flat)`. logits[t,e] = fp32( sum_h x[t,h]*wr[e,h] + bias[e] ),
- * the sum taken in double in ascending h. bias may be NULL (the pages' router has none).
+ * and [Hy3-deep-dive] `self.gate(x_flat)`. logits[t,e] = fp32( sum_h x[t,h]*wr[e,h] ) + bias[e],
+ * the sum taken in double in ascending h and rounded to fp32, the bias added in fp32.
+ * bias may be NULL (the pages' router has none).
  * Only tokens listed in `tokens` (n_tok entries) are computed when tokens != NULL; their rows
  * of `logits` (full [T,E] array) are written, the rest are untouched. */
 void oracle_router_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
@@ -65,13 +66,14 @@ void oracle_dispatch(int T, int K, int E, int capacity, const int32_t* topk_idx,
 
 /* SwiGLU gate/up half of one expert on n gathered rows, [Hy3-deep-dive] `MoEFeedForward`
  * (gate_proj, up_proj, silu) with the [Hy4-config] `swiglu_limit` clamp of both pre-activations:
- * g = sum_h x*wg[i,h], u = sum_h x*wu[i,h] (double), g,u clamped to [-limit, limit] when
- * limit > 0, h[r,i] = bf16( g/(1+exp(-g)) * u ). wg, wu are [I,H]; x_rows is [n,H]. */
+ * g = fp32( sum_h x*wg[i,h] ), u = fp32( sum_h x*wu[i,h] ) (sums in double, then rounded to
+ * fp32), g,u clamped to [-limit, limit] when limit > 0, h[r,i] = bf16( g/(1+exp(-g)) * u ) with
+ * the SwiGLU in double. wg, wu are [I,H]; x_rows is [n,H]. */
 void oracle_gateup_rows(int n, int H, int I, double limit, const uint16_t* x_rows,
                         const uint16_t* wg, const uint16_t* wu, uint16_t* h);
 
-/* Down projection of one expert, [Hy3-deep-dive] `down_proj`: y[r,c] = bf16( sum_i h[r,i]*wd[c,i] ),
- * wd is [H,I], h is [n,I]. */
+/* Down projection of one expert, [Hy3-deep-dive] `down_proj`:
+ * y[r,c] = bf16( fp32( sum_i h[r,i]*wd[c,i] ) ) (the sum in double), wd is [H,I], h is [n,I]. */
 void oracle_down_rows(int n, int H, int I, const uint16_t* h, const uint16_t* wd, uint16_t* y);
 
 /* Weighted combine, [Hy4-deep-dive] `MoELayer.forward` (routed sum plus shared expert output):

@@ -15,8 +15,9 @@
 //   loss term    d_aux * E * sum_e P_e f_e with f fixed (a selection frequency)
 // Every sum is a sequential double sum. With round_bf16 set, the tensors the GPU stores in bf16
 // are rounded to bf16 at the same points (dy, dh, dg, du, the per-row dx, the final dx, and the
-// recomputed forward h and y); with it clear everything stays exact double, which is what the
-// pins against automatic differentiation use.
+// recomputed forward h and y), and the recomputed g, u and y sums are fp32 values first, as in
+// the forward; with it clear everything stays exact double, which is what the pins against
+// automatic differentiation use.
 
 #include <algorithm>
 #include <cmath>
@@ -37,6 +38,9 @@ inline double bf(uint16_t b) {
 inline double rnd(double v, int round) {
   return round ? bf(oracle_bf16_from_double(v)) : v;
 }
+
+// the fp32 value of a projection (g, u, y), as the forward forms it, when rounding
+inline double f32r(double v, int round) { return round ? static_cast<double>(static_cast<float>(v)) : v; }
 
 inline double clampv(double v, double limit) {
   if (limit <= 0.0) return v;
@@ -99,6 +103,8 @@ void oracle_swiglu_bwd_rows(int n, int H, int I, double limit, int round, const 
       g += xv * bf(wg[static_cast<size_t>(i) * H + k]);
       u += xv * bf(wu[static_cast<size_t>(i) * H + k]);
     }
+    g = f32r(g, round);
+    u = f32r(u, round);
     const double gc = clampv(g, limit), uc = clampv(u, limit);
     const double sg = sigmoid(gc);
     const double silu = gc * sg;
@@ -200,6 +206,8 @@ void oracle_layer_backward(int T, int H, int E, int K, int I, int norm_topk, dou
         gv += xv * bf(g[static_cast<size_t>(i) * H + k]);
         uv += xv * bf(u[static_cast<size_t>(i) * H + k]);
       }
+      gv = f32r(gv, round);
+      uv = f32r(uv, round);
       const double gc = clampv(gv, limit), uc = clampv(uv, limit);
       hh[ri] = rnd(gc * sigmoid(gc) * uc, round);
     }
@@ -208,7 +216,7 @@ void oracle_layer_backward(int T, int H, int E, int K, int I, int norm_topk, dou
       const long r = rc / H, c = rc % H;
       double s = 0.0;
       for (int i = 0; i < I; ++i) s += hh[static_cast<size_t>(r) * I + i] * bf(d[static_cast<size_t>(c) * I + i]);
-      yy[rc] = rnd(s, round);
+      yy[rc] = rnd(f32r(s, round), round);
     }
   };
   const size_t IH = static_cast<size_t>(I) * H;

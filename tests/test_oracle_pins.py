@@ -271,18 +271,22 @@ def test_single_expert_equals_dense_swiglu_ffn(orc, limit):
     wd = _rand_bf16(rng, (1, H, I), 0.05)
     r = orc.layer_forward(x, wr, wg, wu, wd, 1, scale=1.0, limit=limit)
     X, G, U, D = _f64(x), _f64(wg[0]), _f64(wu[0]), _f64(wd[0])
-    g, u = X @ G.T, X @ U.T
+    # the projections are fp32 values: float64 matmuls rounded to float32 (the order of a float64
+    # sum moves it by ~1e-16 relative, far from any fp32 or bf16 rounding boundary here)
+    g, u = (X @ G.T).float().double(), (X @ U.T).float().double()
     if limit > 0:
         assert (g.abs() > limit).any(), "test inputs must exercise the clamp"
         g, u = g.clamp(-limit, limit), u.clamp(-limit, limit)
     h_ref = torch.nn.functional.silu(g) * u
     h_ref_b = _bf16_torch(h_ref)
-    assert _ulp_close(r["h_routed"], h_ref_b).all()
-    assert (r["h_routed"] == h_ref_b).mean() > 0.99
-    y_ref = _f64(r["h_routed"]) @ D.T  # same bf16 h on both sides
-    y_ref_b = _bf16_torch(y_ref)
-    assert _ulp_close(r["y_routed"], y_ref_b).all()
-    assert (r["y_routed"] == y_ref_b).mean() > 0.99
+    np.testing.assert_array_equal(r["h_routed"], h_ref_b)
+    y_ref = (_f64(r["h_routed"]) @ D.T).float()  # same bf16 h on both sides
+    y_ref_b = y_ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(r["y_routed"], y_ref_b)
+    # the fp32 rounding of g, u and y is a step of its own: a reference that skips it differs
+    h_direct = _bf16_torch(torch.nn.functional.silu((X @ G.T).clamp(-limit, limit) if limit > 0 else X @ G.T)
+                           * ((X @ U.T).clamp(-limit, limit) if limit > 0 else X @ U.T))
+    assert _ulp_close(r["h_routed"], h_direct).all()
     # with one expert, k = 1 and s = 1 the renormalised weight is exactly 1 and out == y
     assert np.all(r["topk_idx"] == 0) and np.all(r["topk_w"] == 1.0)
     np.testing.assert_array_equal(r["out"], r["y_routed"])
@@ -380,8 +384,9 @@ def test_router_logits_against_float64_matmul(orc):
     x, wr = _rand_bf16(rng, (T, H), 1.0), _rand_bf16(rng, (E, H), 0.02)
     bias = (1.2 * np.log(1.0 / (np.arange(E) + 1.0))).astype(np.float32)
     lg = orc.router_logits(x, wr, bias)
-    ref = (_f64(x) @ _f64(wr).T).numpy() + bias.astype(np.float64)
-    np.testing.assert_allclose(lg, ref.astype(np.float32), rtol=1e-6, atol=1e-7)
+    # fp32 logit (float64 matmul rounded to float32), then the bias as a float32 add
+    ref = (_f64(x) @ _f64(wr).T).numpy().astype(np.float32) + bias
+    np.testing.assert_array_equal(lg, ref)
     # the token subset mode writes only the listed rows
     lg2 = orc.router_logits(x, wr, bias, tokens=[3, 17])
     np.testing.assert_array_equal(lg2[[3, 17]], lg[[3, 17]])
