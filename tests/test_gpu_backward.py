@@ -134,7 +134,7 @@ def test_stored_gate_up_equals_recompute(name):
     dev = generate(wl, DEV)
     hw = P.host(dev)
     g, layer, _ = P.run_layer_gpu(wl, dev, train=True)
-    P.compare_layer(wl, hw, g, P.oracle_same_logits(wl, hw, g["logits"]))
+    P.compare_layer(wl, hw, g, P.oracle_same_logits(wl, hw, g["logits"]), train=True)
     assert layer._gu is not None
     # the stored sums against their definition g = x Wg^T, u = x Wu^T (fp64), within the bound
     # of 16-wide fp32 partial sums over H

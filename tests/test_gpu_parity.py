@@ -1,9 +1,13 @@
 """GPU parity: the HIP library against the CPU oracle, through the C ABI.
 
 Small shapes are compared element by element (all tokens, all rows); they span several tiles
-of every kernel and end on ragged tails. Full workload sizes are checked on sampled tokens
-(every routed row of each sampled token, the shared row, the combined output) plus properties
-that hold at any size. Routing integers are compared bit-exactly from the same fp32 logits.
+of every kernel and end on ragged tails, and one runs at the Hy4 width (H = 6144, I = 2048).
+Full workload sizes are checked on the first and last row of every row tile of every group
+(expert and shared) and on every row and the output of sampled tokens, plus properties that
+hold at any size. Routing integers are compared bit-exactly from the same fp32 logits. Every
+bf16 tensor must lie in its a-priori rounding interval (tests/parity.py): bit-equal to the
+oracle except where the oracle's value lies within the fp32 arithmetic's error bound of a bf16
+rounding midpoint.
 """
 from __future__ import annotations
 
@@ -62,8 +66,10 @@ SMALL = {
                                            I=256, scale=2.827, seed=23),
 }
 
-# FP8 expert weights (E4M3 codes, per-row fp32 scales); every FFN shape runs the weight-streaming
-# kernel, so these span one and many 64-row tiles per group, ragged tails and the clamp
+# FP8 expert weights (E4M3 codes, per-row fp32 scales): the weight-streaming kernel's FP8 form
+# (tiny, ragged, no shared, clamp, capacity: few rows per expert) and the tiled kernel's FP8 form
+# (multi_tile and bands: 64 or more rows per expert), with one and many tiles per group, ragged
+# tails and the clamp
 SMALL.update({
     "fp8_tiny_t128_h512_e32_k2": BASE.with_(name="fp8_tiny_t128_h512_e32_k2", fp8=True, seed=40),
     "fp8_ragged_t130_h256_e256_k8": SMALL["ragged_t130_h256_e256_k8"].with_(
@@ -77,6 +83,19 @@ SMALL.update({
     "fp8_capacity_drops_t200_e8_k2": SMALL["capacity_drops_t200_e8_k2"].with_(
         name="fp8_capacity_drops_t200_e8_k2", fp8=True, seed=46),
 })
+
+# the Hy4 width (H = 6144, I = 2048) element by element: 512 tokens, 8 experts, top-2 (about 128
+# rows per expert: tiled kernel, one partly filled tile per expert, the shared expert over two
+# tiles with a ragged second one)
+SMALL["hy4_width_t512_e8_k2"] = Workload("hy4_width_t512_e8_k2", T=512, H=6144, E=8, K=2, I=2048,
+                                         scale=2.827, w_std=0.006, router_std=0.006, seed=28)
+# weight-streaming kernel with 64-row tiles (16 to 64 rows per group on average): the skewed
+# router leaves groups of 1 to 64+ rows, so tiles hold 1, 2, 3 and 4 sixteen-row sub-blocks
+SMALL["skinny_ns_t160_e16_k4"] = Workload("skinny_ns_t160_e16_k4", T=160, H=512, E=16, K=4, I=256,
+                                          scale=2.827, zipf=0.5, seed=29)
+# tiled kernel with groups of every size class: tiles whose halves hold 0..5 live 32-row fragments
+SMALL["tiled_miv_t1200_e12_k3"] = Workload("tiled_miv_t1200_e12_k3", T=1200, H=256, E=12, K=3, I=256,
+                                           scale=2.827, zipf=0.4, seed=32)
 
 # routing only: the tiled router with its hidden dimension split 12 ways (2 K-tiles per split)
 ROUTE_ONLY = {
@@ -108,6 +127,42 @@ def test_layer_forward_small(name):
     if name.endswith("clamp_forced_t128"):
         hv = P.f64(g["h_routed"][: int(g["offsets"][-1])])
         assert np.abs(hv).max() > 50, "this case must reach the clamp"
+
+
+def _tile_classes(sizes, rows_max):
+    """The kernel a layer launch takes and the tile shapes it runs: for the tiled kernel the
+    live 32-row fragments of each half of every 320-row tile (the main loop's specialisation),
+    for the weight-streaming kernel the 16-row sub-blocks of every tile."""
+    G = len(sizes)
+    if rows_max >= 64 * G:
+        out = set()
+        for n in sizes:
+            for t0 in range(0, n, 320):
+                nt = min(320, n - t0)
+                out.add(("half0", min(5, (min(nt, 160) + 31) // 32)))
+                out.add(("half1", min(5, max(0, (nt - 160 + 31) // 32))))
+        return "tiled", out
+    bm = 16 if rows_max <= 16 * G else 64
+    return "skinny%d" % bm, {("subblocks", (min(bm, n - t0) + 15) // 16) for n in sizes for t0 in range(0, n, bm)}
+
+
+def test_small_cases_reach_every_kernel_specialisation():
+    """The element-wise cases run every specialisation of both grouped-GEMM kernels: the tiled
+    kernel's halves with 0..5 live fragments and the weight-streaming kernel's 64-row tiles with
+    1..4 sub-blocks (computed from the oracle's routing of the same inputs, which the layer tests
+    require the GPU to match bit for bit)."""
+    seen = {}
+    for name in ("skinny_ns_t160_e16_k4", "tiled_miv_t1200_e12_k3", "hy4_width_t512_e8_k2"):
+        wl = SMALL[name]
+        hw = P.host(generate(wl, "cpu"))
+        lo = oracle.router_logits(hw["x"], hw["w_router"], hw["router_bias"])
+        idx, _ = oracle.route_from_logits(lo, wl.K, wl.scale, wl.norm_topk)
+        counts = oracle.dispatch(idx, wl.E, wl.capacity)[0]
+        sizes = ([wl.T] if wl.n_shared else []) + [int(c) for c in counts if c > 0]
+        kern, cls = _tile_classes(sizes, wl.T * wl.K + (wl.T if wl.n_shared else 0))
+        seen.setdefault(kern, set()).update(cls)
+    assert {("half0", m) for m in range(1, 6)} | {("half1", m) for m in range(6)} <= seen["tiled"]
+    assert {("subblocks", n) for n in range(1, 5)} <= seen["skinny64"]
 
 
 def test_layer_is_deterministic():
@@ -263,17 +318,15 @@ def test_moe_expert_ffn_routed_and_identity(name):
     torch.cuda.synchronize()
     R = int(offsets[-1])
     hg, yg = as_u16(h)[:R], as_u16(y)[:R]
+    stats = P.Stats()
+    chain = P.chain_for(P.kernel_of(TK, wl.E), wl.fp8, False)
     for e in range(wl.E):
         a, b = offsets[e], offsets[e + 1]
         if a == b:
             continue
         xr = hw["x"][r2s[a:b] // wl.K]
-        w3 = P.routed_weights(hw, e)
-        rh, ry = P.ffn_rows(xr, w3, wl.limit)
-        P.assert_bf16_close(hg[a:b], rh, "h expert %d" % e)
-        P.assert_bf16_close(yg[a:b], P.down_rows(hg[a:b], w3[2]), "y expert %d (chained)" % e)
-        P.assert_bf16_close(yg[a:b], ry, "y expert %d (end to end)" % e,
-                            extra=P.propagated_h_diff(hg[a:b], rh, w3[2]))
+        P.check_ffn_rows("expert %d" % e, xr, P.routed_weights(hw, e), wl.limit, chain, hg[a:b],
+                         yg[a:b], stats=stats)
     # identity rows, one group, no offsets: the shared-expert form, once with h kept in the
     # workspace and once with h returned; both runs must agree bit for bit
     sw = _dev_weights(dev, ("s_gate", "s_up", "s_down"), lead=True)
@@ -286,12 +339,10 @@ def test_moe_expert_ffn_routed_and_identity(name):
                 _ws(moe.moe_expert_ffn_workspace_size(s, 1, wl.T)))
     torch.cuda.synchronize()
     assert torch.equal(ys, ys2)
-    s3 = P.shared_weights(hw)
-    rhs, rys = P.ffn_rows(hw["x"], s3, wl.limit)
-    P.assert_bf16_close(as_u16(hs), rhs, "identity-row h")
-    P.assert_bf16_close(as_u16(ys), P.down_rows(as_u16(hs), s3[2]), "identity-row y (chained)")
-    P.assert_bf16_close(as_u16(ys), rys, "identity-row y (end to end)",
-                        extra=P.propagated_h_diff(as_u16(hs), rhs, s3[2]))
+    P.check_ffn_rows("identity rows", hw["x"], P.shared_weights(hw), wl.limit,
+                     P.chain_for(P.kernel_of(wl.T, 1), wl.fp8, False), as_u16(hs), as_u16(ys),
+                     stats=stats)
+    print("[parity] moe_expert_ffn %s: %s" % (name, stats.line()), flush=True)
 
 
 @pytest.mark.parametrize("name", ["tiny_t128_h512_e32_k2", "capacity_drops_t200_e8_k2", "no_shared_t128"])
@@ -310,7 +361,10 @@ def test_moe_combine(name):
     moe.moe_combine(s, from_u16(yr, DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(s2r).to(DEV),
                     None if ysh is None else from_u16(ysh, DEV), out)
     torch.cuda.synchronize()
-    P.assert_bf16_close(as_u16(out), oracle.combine(w, s2r, yr, ysh), "combine")
+    ref = oracle.combine(w, s2r, yr, ysh)
+    v, d, ab = P.combine_value(w, s2r.reshape(wl.T, wl.K), P.f64(yr), None if ysh is None else P.f64(ysh))
+    P.check_reconstruction(v, ref, "combine", 2.0 ** -45 * ab + 1e-300)
+    P.check_interval(as_u16(out), v, d, "combine", ref, bare=True)
 
 
 # ----------------------------------------------------------------------------- full sizes, sampled
@@ -318,7 +372,7 @@ FULL = ["hy4_decode_t64", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2", "h
         "hy4_decode_t64_fp8", "dense_ffn_t8192_h6144_i18432", "hy4_prefill_t8192_fp8"]
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
     _require_gpu()
@@ -356,10 +410,9 @@ def test_full_size_sampled(name):
     assert R == T * K - int((g_s2r < 0).sum())
     np.testing.assert_array_equal(np.sort(g_r2s[:R]), np.sort(np.nonzero(g_s2r >= 0)[0]))
 
-    # sampled tokens: logits, every routed row, the shared row and the output
+    # sampled tokens (plus one with a dropped slot): logits, routing from independent logits
     rng = np.random.default_rng(1234)
-    n_s = 8 if T <= 64 else 5
-    toks = np.sort(rng.choice(T, n_s, replace=False))
+    toks = np.sort(rng.choice(T, 8 if T <= 64 else 5, replace=False))
     if wl.capacity:
         dropped_tok = np.nonzero((g_s2r < 0).reshape(T, K).any(1))[0]
         if len(dropped_tok):
@@ -368,63 +421,128 @@ def test_full_size_sampled(name):
     bias = None if dev["router_bias"] is None else dev["router_bias"].cpu().numpy()
     lo_s = oracle.router_logits(x_s, as_u16(dev["w_router"]), bias)
     P.assert_logits_close(logits[toks], lo_s, "sampled logits")
-    _, _, probs = oracle.route_from_logits(lo_s, K, wl.scale, wl.norm_topk, want_probs=True)
+    idx_i, _, probs = oracle.route_from_logits(lo_s, K, wl.scale, wl.norm_topk, want_probs=True)
     ok = P.margin_ok(probs, K)
-    idx_i, _ = oracle.route_from_logits(lo_s, K, wl.scale, wl.norm_topk)
     np.testing.assert_array_equal(g_idx[toks][ok], idx_i[ok])
 
+    # rows to check: the first and last row of every row tile of every group, and every row of
+    # the sampled tokens. Groups: the shared expert on layer rows [0, T), expert e on
+    # [n_id + offsets[e], n_id + offsets[e + 1]).
+    G = E + (1 if wl.n_shared else 0)
+    kern = P.kernel_of(n_id + T * K, G)
+    bm = 320 if kern == "tiled" else (16 if n_id + T * K <= 16 * G else 64)
+    chain = P.chain_for(kern, wl.fp8, False)
+    tok_set = set(int(t) for t in toks)
+    groups = []  # (label, weights key, first layer row, rows of the group -> token)
+    if n_id:
+        groups.append(("shared", None, 0, np.arange(T)))
+    for e in range(E):
+        a, b = int(g_off[e]), int(g_off[e + 1])
+        if a < b:
+            groups.append(("expert %d" % e, e, n_id + a, g_r2s[a:b] // K))
     cache = {}
 
-    def host_w(n, e=None):
-        t = dev[n] if e is None else dev[n][e]
-        if t.dtype == torch.uint8:
-            sc = dev[n + "_scale"] if e is None else dev[n + "_scale"][e]
-            return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
-        return as_u16(t)
+    def weights(key):
+        if key not in cache:
+            names = ("s_gate", "s_up", "s_down") if key is None else ("w_gate", "w_up", "w_down")
 
-    def expert(e):
-        if e not in cache:
-            cache[e] = tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down"))
-        return cache[e]
+            def one(n):
+                t = dev[n] if key is None else dev[n][key]
+                if t.dtype == torch.uint8:
+                    sc = dev[n + "_scale"] if key is None else dev[n + "_scale"][key]
+                    return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
+                return as_u16(t)
+            cache[key] = tuple(one(n) for n in names)
+        return cache[key]
 
-    for i, t in enumerate(toks):
-        rows = g_s2r[t * K:(t + 1) * K]
-        kept = [j for j in range(K) if rows[j] >= 0]
-        sel = torch.from_numpy((n_id + rows[kept]).astype(np.int64)).to(DEV)
-        gh = as_u16(h_all[sel])
-        gy = as_u16(y_all[sel])
-        ry = np.zeros((max(R, 1), H), np.uint16)
-        for n, j in enumerate(kept):
-            wg_, wu_, wd_ = expert(int(g_idx[t, j]))
-            rh1, ry1 = P.ffn_rows(x_s[i:i + 1], (wg_, wu_, wd_), wl.limit)
-            P.assert_bf16_close(gh[n:n + 1], rh1, "h token %d slot %d" % (t, j))
-            P.assert_bf16_close(gy[n:n + 1], P.down_rows(gh[n:n + 1], wd_),
-                                "y token %d slot %d (chained)" % (t, j))
-            P.assert_bf16_close(gy[n:n + 1], ry1, "y token %d slot %d (end to end)" % (t, j),
-                                extra=P.propagated_h_diff(gh[n:n + 1], rh1, wd_))
-            ry[rows[j]] = ry1[0]
-        ys_r = None
-        if wl.n_shared:
-            if "shared" not in cache:
-                cache["shared"] = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down"))
-            sd_ = cache["shared"][2]
-            rhs, ys_r = P.ffn_rows(x_s[i:i + 1], cache["shared"], wl.limit)
-            ghs = as_u16(h_all[int(t):int(t) + 1])
-            gys = as_u16(y_all[int(t):int(t) + 1])
-            P.assert_bf16_close(ghs, rhs, "h_shared token %d" % t)
-            P.assert_bf16_close(gys, P.down_rows(ghs, sd_), "y_shared token %d (chained)" % t)
-            P.assert_bf16_close(gys, ys_r, "y_shared token %d (end to end)" % t,
-                                extra=P.propagated_h_diff(ghs, rhs, sd_))
-        g_out = as_u16(out[int(t):int(t) + 1])
-        w1 = g_w[t:t + 1]
-        s2r1 = g_s2r[t * K:(t + 1) * K]
-        # chained: oracle combine of the GPU rows
-        gy_full = np.zeros((max(R, 1), H), np.uint16)
-        gy_full[rows[kept]] = gy
-        if not wl.n_shared:
-            gys = None
-        P.assert_bf16_close(g_out, oracle.combine(w1, s2r1, gy_full, gys), "out (chained) token %d" % t)
-        # independent: oracle rows, with the measured y differences propagated
-        r_out = oracle.combine(w1, s2r1, ry, ys_r)
-        extra = P.propagated_y_diff(w1, s2r1, gy_full, ry, gys, ys_r)
-        P.assert_bf16_close(g_out, r_out, "out (end to end) token %d" % t, extra=extra)
+    stats = P.Stats()
+    y_rows = {}  # layer row -> (gpu y, oracle y) for the sampled tokens' rows
+    n_rows = 0
+    for label, key, r0, tok_of in groups:
+        n = len(tok_of)
+        local = set()
+        for t0 in range(0, n, bm):
+            local.update((t0, min(t0 + bm, n) - 1))
+        local.update(int(i) for i in np.nonzero(np.isin(tok_of, toks))[0])
+        local = np.array(sorted(local))
+        lrows = r0 + local
+        sel = torch.from_numpy(lrows.astype(np.int64)).to(DEV)
+        gh, gy = as_u16(h_all[sel]), as_u16(y_all[sel])
+        x_rows = as_u16(dev["x"][torch.from_numpy(tok_of[local].astype(np.int64)).to(DEV)])
+        w3 = weights(key)
+        rh, ry = P.ffn_rows(x_rows, w3, wl.limit)
+        P.check_ffn_rows("%s rows %s" % (label, local[:4].tolist()), x_rows, w3, wl.limit, chain,
+                         gh, gy, rh, ry, stats)
+        for i, lr in enumerate(lrows):
+            if int(tok_of[local[i]]) in tok_set:
+                y_rows[int(lr)] = (gy[i], ry[i])
+        n_rows += len(local)
+        if key in cache and key is not None and len(cache) > 8:
+            del cache[key]  # keep host copies of a few experts only
+    # the sampled tokens' outputs: chained and end to end
+    s2r_t = g_s2r.reshape(T, K)[toks]
+    rows_t = np.where(s2r_t >= 0, n_id + s2r_t, -1)
+    uniq = sorted(set(int(r) for r in rows_t.ravel() if r >= 0))
+    pos = {r: i for i, r in enumerate(uniq)}
+    loc = np.vectorize(lambda r: pos[int(r)] if r >= 0 else -1)(rows_t) if len(uniq) else rows_t
+    yg = np.stack([y_rows[r][0] for r in uniq]) if uniq else np.zeros((1, H), np.uint16)
+    yo = np.stack([y_rows[r][1] for r in uniq]) if uniq else np.zeros((1, H), np.uint16)
+    ysg = yso = None
+    if n_id:
+        ysg = np.stack([y_rows[int(t)][0] for t in toks])
+        yso = np.stack([y_rows[int(t)][1] for t in toks])
+    out_orc = oracle.combine(r_w[toks], loc.astype(np.int32).ravel(), yo, yso)
+    P.check_out("tokens %s" % toks.tolist(), g_w[toks], r_w[toks], loc, yg, yo, ysg, yso,
+                as_u16(out[torch.from_numpy(toks).to(DEV)]), out_orc, stats)
+    print("[parity] %s: %d rows over %d groups (%s, %d-row tiles); %s"
+          % (name, n_rows, len(groups), kern, bm, stats.line()), flush=True)
+
+
+# ----------------------------------------------------------------------------- large operands
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", ["identity_h_rows", "gathered_x_rows"])
+def test_rows_past_2_31_elements(case):
+    """The tiled kernel reaches activation rows whose element offset passes 2^31 (and 2^32
+    bytes): the down projection over h [T, I] of 1.1M identity rows at I = 2048, and the gate/up
+    projection gathering rows of x [1.1M, 2048] near its end. Checked against the oracle on the
+    rows at and past the 2^31-element boundary and on the last rows."""
+    _require_gpu()
+    T = 1_100_000
+    H, I = (256, 2048) if case == "identity_h_rows" else (2048, 256)
+    print("\n[large] %s T=%d H=%d I=%d" % (case, T, H, I), flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(4242)
+    x = torch.randn((T, H), generator=gen, device=DEV).to(torch.bfloat16)
+    w = [(torch.randn(shp, generator=gen, device=DEV) * 0.02).to(torch.bfloat16)
+         for shp in ((1, I, H), (1, I, H), (1, H, I))]
+    s = moe.Shape(T=T, H=H, E=1, K=1, I=I, n_shared=0)
+    boundary = (1 << 31) // (I if case == "identity_h_rows" else H)  # first row past 2^31 elements
+    if case == "identity_h_rows":
+        rows = T
+        h = torch.empty((rows, I), dtype=torch.bfloat16, device=DEV)
+        y = torch.empty((rows, H), dtype=torch.bfloat16, device=DEV)
+        moe.moe_expert_ffn(s, 1, rows, x, None, None, *w, h, y,
+                           _ws(moe.moe_expert_ffn_workspace_size(s, 1, rows)))
+        check = np.unique(np.concatenate([np.arange(boundary - 40, boundary + 360),
+                                          np.arange(T - 330, T)]))
+        toks = check
+    else:
+        toks = np.unique(np.concatenate([np.arange(boundary - 8, boundary + 300),
+                                         np.arange(T - 300, T)])).astype(np.int32)
+        rows = len(toks)
+        r2s = torch.from_numpy(toks).to(DEV)  # k = 1: slot id = token
+        off = torch.tensor([0, rows], dtype=torch.int32, device=DEV)
+        h = torch.empty((rows, I), dtype=torch.bfloat16, device=DEV)
+        y = torch.empty((rows, H), dtype=torch.bfloat16, device=DEV)
+        moe.moe_expert_ffn(s, 1, rows, x, r2s, off, *w, h, y,
+                           _ws(moe.moe_expert_ffn_workspace_size(s, 1, rows)))
+        check = np.arange(rows)
+    torch.cuda.synchronize()
+    assert P.kernel_of(rows, 1) == "tiled"
+    sel = torch.from_numpy(check.astype(np.int64)).to(DEV)
+    x_rows = as_u16(x[torch.from_numpy(toks.astype(np.int64)).to(DEV)])
+    w3 = tuple(as_u16(t[0]) for t in w)
+    stats = P.Stats()
+    P.check_ffn_rows(case, x_rows, w3, 10.0, P.CHAINS["tiled"], as_u16(h[sel]), as_u16(y[sel]),
+                     stats=stats)
+    print("[parity] %s: %s" % (case, stats.line()), flush=True)
