@@ -3,11 +3,16 @@
 
 One step = one moe_layer_forward (router GEMM + softmax/top-k/renorm/scale, dispatch, routed and
 shared SwiGLU expert FFNs, combine) over one batch of synthetic, seeded inputs already resident
-in HBM. Default workload: the Hy4-shape decode batch (T=64, H=6144, 256 experts, top-8, one
-shared expert, intermediate 2048, bf16); ``--workload hy4_decode_t64_fp8`` runs the same batch
-with FP8 E4M3 expert weights (per-row fp32 scales). Prints one JSON line.
+in HBM. The headline workload (``value``) is the Hy4-shape decode batch (T=64, H=6144, 256
+experts, top-8, one shared expert, intermediate 2048, bf16); the same JSON line also carries,
+under ``workloads``, the other workloads of the layer's configuration list, each timed in a
+region of its own: the tiny layer, the Hy4 prefill batch (T=8192), the capacity-limited top-2
+layer and the long skewed prefill (T=65536), the last three bound by the matrix cores. Every
+workload reports its roofline fractions and the CPU oracle timed on a bounded token sample
+(all host threads; the tiny and decode layers also on one thread). ``--workload NAME`` changes
+the headline (e.g. ``hy4_decode_t64_fp8``), ``--extra ''`` drops the other workloads.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra A,B] [--no-cpu-baseline]
   python bench.py --copy-calibration     # plain device copy, for scaling HBM counters
 """
 from __future__ import annotations
@@ -22,6 +27,11 @@ METRIC = "MoE-layer tokens/s at Hy4 shape; % of bf16 MFMA or HBM roofline"
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_MFMA_FP8_TFLOPS = 5000.0  # MI355X dense FP8 MFMA, TFLOP/s (the W8A8 expert products)
+# the other workloads of the layer's configuration list, timed after the headline
+EXTRA = ("tiny_t128_h512_e32_k2", "hy4_prefill_t8192", "capacity_t4096_h7168_e32_k2",
+         "hy4_skew_t65536")
+# workloads whose CPU baseline also runs on one thread
+SINGLE_THREAD = ("tiny_t128_h512_e32_k2", "hy4_decode_t64")
 
 
 def parse():
@@ -30,6 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="hy4_decode_t64")
+    ap.add_argument("--extra", default=",".join(EXTRA),
+                    help="comma-separated workloads timed after the headline ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -95,11 +107,11 @@ def recorded_traffic(workload, kernel):
     return None
 
 
-def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
+def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50, threads=0):
     """The CPU oracle, timed on a bounded sample of the workload's tokens (every step of the
     layer for those tokens: router logits, routing, their routed and shared expert FFNs, combine),
     repeated until at least min_seconds have passed. Weights are copied to host memory before the
-    clock starts."""
+    clock starts. threads: OpenMP threads (0 = all the host offers)."""
     import numpy as np
     import torch
 
@@ -132,6 +144,10 @@ def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
            oracle.expert_ffn_rows_fp8 if wl.fp8 else oracle.expert_ffn_rows)
     W = {e: tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down")) for e in experts}
     SW = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
+    all_threads = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    cores = oracle.num_threads()
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -148,11 +164,13 @@ def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
         dt = time.perf_counter() - t0
         if dt >= min_seconds or reps >= max_reps:
             break
+    oracle.set_num_threads(all_threads)
     return {"value": round(reps * len(toks) / dt, 3), "unit": "tokens/s",
-            "cores": oracle.num_threads(), "kind": "oracle", "seconds": round(dt, 3),
+            "cores": cores, "kind": "oracle", "seconds": round(dt, 3),
             "sample": "%d of the workload's %d tokens, %d pass(es): all steps of the layer for them "
-                      "(%d distinct routed experts + shared), fp64 C++ oracle"
-                      % (len(toks), wl.T, reps, len(experts))}
+                      "(%d distinct routed experts%s), fp64 C++ oracle, %d thread(s)"
+                      % (len(toks), wl.T, reps, len(experts), " + shared" if wl.n_shared else "",
+                         cores)}
 
 
 def copy_calibration():
@@ -166,33 +184,22 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "reads_bytes": n, "writes_bytes": n}))
 
 
-def main():
-    args = parse()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X, so "
-              "--gpus %d (WORLD_SIZE=%d) is not supported" % (args.gpus, world), file=sys.stderr)
-        sys.exit(2)
-    if args.copy_calibration:
-        copy_calibration()
-        return
+def measure(wl, args):
+    """Generate the workload's inputs in HBM, run W warm-up steps, time K plain forward steps
+    between two events, then K more with an event between the phases for the per-kernel split.
+    Returns the step time, the phase times, the roofline objects and the layer's fractions."""
+    import ctypes
 
     import numpy as np
     import torch
 
     import sparse_moe_layer_softmax_amd as moe
-    from sparse_moe_layer_softmax_amd.workloads import WORKLOADS
 
-    wl = WORKLOADS[args.workload]
-    torch.cuda.set_device(0)
     dev = generate_inputs(wl)
     shape = moe.Shape.of(wl)
     layer = moe.MoELayer.from_inputs(shape, dev)
-    if args.mode == "train":
-        return train_step(args, wl, dev, layer)
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
-
     for _ in range(args.warmup):
         layer.forward(dev["x"], out)
     torch.cuda.synchronize()
@@ -203,7 +210,6 @@ def main():
     for row in evs:
         for e in row:
             e.record(stream)
-    import ctypes
     handles = [(ctypes.c_void_p * nph)(*[e.cuda_event for e in row]) for row in evs]
     torch.cuda.synchronize()
 
@@ -232,58 +238,133 @@ def main():
     rf = roofline(alg["gu_flops"], alg["gu_bytes"], gu_s, peak_mfma)
     # the tiled MFMA kernel runs when the groups hold at least 64 rows each on average (bf16 or
     # FP8 weights alike); below that the weights stream through the skinny kernel
-    tiled = wl.T * wl.K + wl.n_shared * wl.T >= 64 * (wl.E + wl.n_shared)
-    if tiled:
-        kname = "ffn_tiled_kernel<%s>" % ("kEpiSwiglu88" if wl.act_fp8 else
-                                          "kEpiSwiglu8" if wl.fp8 else "kEpiSwiglu")
+    rows = wl.T * wl.K + wl.n_shared * wl.T
+    groups = wl.E + wl.n_shared
+    if rows >= 64 * groups:
+        gu, dn = (("kEpiSwiglu88", "kEpiBf16_88") if wl.act_fp8 else
+                  ("kEpiSwiglu8", "kEpiBf16_8") if wl.fp8 else ("kEpiSwiglu", "kEpiBf16"))
+        kname, dname = "ffn_tiled_kernel<%s>" % gu, "ffn_tiled_kernel<%s>" % dn
     else:
-        # the weight-streaming kernel: <gated, FP8 weights, FP8 activations, 16-row sub-blocks per
-        # tile>; 16-row tiles (one sub-block) when the groups average at most 16 rows
-        rows = wl.T * wl.K + wl.n_shared * wl.T
-        maxns = 1 if rows <= 16 * (wl.E + wl.n_shared) else 4
-        kname = "ffn_skinny_kernel<true, %s, %s, %d>" % ("true" if wl.fp8 else "false",
-                                                         "true" if wl.act_fp8 else "false", maxns)
+        # the weight-streaming kernel: <gated, FP8 weights, FP8 activations, 16-row sub-blocks
+        # per tile>; 16-row tiles (one sub-block) when the groups average at most 16 rows
+        maxns = 1 if rows <= 16 * groups else 4
+        fl = ("true" if wl.fp8 else "false", "true" if wl.act_fp8 else "false", maxns)
+        kname = "ffn_skinny_kernel<true, %s, %s, %d>" % fl
+        dname = "ffn_skinny_kernel<false, %s, %s, %d>" % fl
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
     rf["algorithmic_flops"] = alg["gu_flops"]
     rf["avg_launch_ms"] = round(phase_ms["gate_up_gemm"], 4)
+    dn = roofline(alg["dn_flops"], alg["dn_bytes"], dn_s, peak_mfma)
+    dn["traffic"] = recorded_traffic(wl.name, dname)
+    dn["kernel"] = dname + " (routed+shared down grouped GEMM)"
+    dn["avg_launch_ms"] = round(phase_ms["down_gemm"], 4)
     layer_s = ms / 1e3
+    layer_obj = {"algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"],
+                 "hbm_GBs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
+                 "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS, 4),
+                 "mfma_TFLOPs": round(alg["layer_flops"] / layer_s / 1e12, 2),
+                 "mfma_frac": round(alg["layer_flops"] / layer_s / 1e12 / peak_mfma, 4),
+                 "routed_rows": alg["R"], "touched_experts": alg["touched"],
+                 "max_rows_per_expert": int(counts.max())}
+    config = {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I,
+              "n_shared": wl.n_shared, "routed_scaling": wl.scale, "swiglu_limit": wl.limit,
+              "capacity": wl.capacity, "router_bias": "zipf %.1f" % wl.zipf if wl.zipf else "none",
+              "parallelism": "none (1 GPU)",
+              "expert_weights": "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16",
+              "expert_activations": ("fp8_e4m3 + fp32 row scale (dynamic)" if wl.act_fp8
+                                     else "bf16")}
+    return dict(dev=dev, ms=ms, tokens_per_s=wl.T / layer_s, roofline=rf, down_gemm=dn,
+                layer=layer_obj, phases_ms={k: round(v, 4) for k, v in phase_ms.items()},
+                config=config)
+
+
+def cpu_baselines(wl, dev, args, min_seconds):
+    """The oracle's timing on the workload's token sample: all host threads, and one thread for
+    the tiny and decode layers."""
+    if args.no_cpu_baseline:
+        return None, None
+    n_tok = args.cpu_tokens or min(wl.T, 64)
+    full = cpu_baseline(wl, dev, n_tok, min_seconds=min_seconds)
+    one = cpu_baseline(wl, dev, n_tok, min_seconds=min_seconds, threads=1) \
+        if wl.name in SINGLE_THREAD else None
+    return full, one
+
+
+def release(m):
+    import torch
+    m.pop("dev", None)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the MoE layer here runs on a single MI355X, so "
+              "--gpus %d (WORLD_SIZE=%d) is not supported" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+
+    from sparse_moe_layer_softmax_amd.workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    if args.mode == "train":
+        import sparse_moe_layer_softmax_amd as moe
+        dev = generate_inputs(wl)
+        layer = moe.MoELayer.from_inputs(moe.Shape.of(wl), dev)
+        return train_step(args, wl, dev, layer)
+    m = measure(wl, args)
     res = {
         "metric": METRIC,
-        "value": round(wl.T / layer_s, 1),
+        "value": round(m["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(m["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3" if wl.act_fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I,
-                   "n_shared": wl.n_shared, "routed_scaling": wl.scale, "swiglu_limit": wl.limit,
-                   "capacity": wl.capacity, "parallelism": "none (1 GPU)",
-                   "expert_weights": "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16",
-                   "expert_activations": ("fp8_e4m3 + fp32 row scale (dynamic)" if wl.act_fp8
-                                          else "bf16")},
-        "roofline": rf,
-        "layer": {"algorithmic_bytes": alg["layer_bytes"], "algorithmic_flops": alg["layer_flops"],
-                  "hbm_GBs": round(alg["layer_bytes"] / layer_s / 1e9, 1),
-                  "hbm_frac": round(alg["layer_bytes"] / layer_s / 1e9 / PEAK_HBM_GBS, 4),
-                  "mfma_TFLOPs": round(alg["layer_flops"] / layer_s / 1e12, 2),
-                  "mfma_frac": round(alg["layer_flops"] / layer_s / 1e12 / peak_mfma, 4),
-                  "routed_rows": alg["R"], "touched_experts": alg["touched"],
-                  "max_rows_per_expert": int(counts.max())},
-        "down_gemm": roofline(alg["dn_flops"], alg["dn_bytes"], dn_s, peak_mfma),
-        "phases_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "config": m["config"],
+        "roofline": m["roofline"],
+        "layer": m["layer"],
+        "down_gemm": m["down_gemm"],
+        "phases_ms": m["phases_ms"],
     }
-    if not args.no_cpu_baseline:
-        n_tok = args.cpu_tokens or min(wl.T, 64)
-        res["cpu_baseline"] = cpu_baseline(wl, dev, n_tok)
-    else:
-        res["cpu_baseline"] = None
+    full, one = cpu_baselines(wl, m["dev"], args, 10.0)
+    res["cpu_baseline"] = full
+    if one is not None:
+        res["cpu_baseline_single_thread"] = one
+    release(m)
+    extra = [n for n in args.extra.split(",") if n and n != wl.name]
+    if extra:
+        res["workloads"] = {}
+    for name in extra:
+        w2 = WORKLOADS[name]
+        m2 = measure(w2, args)
+        obj = {"ms_per_step": round(m2["ms"], 4), "value": round(m2["tokens_per_s"], 1),
+               "unit": "tokens/s", "steps": args.steps, "warmup": args.warmup,
+               "config": m2["config"], "roofline": m2["roofline"], "down_gemm": m2["down_gemm"],
+               "layer": m2["layer"], "phases_ms": m2["phases_ms"]}
+        full, one = cpu_baselines(w2, m2["dev"], args, 6.0)
+        obj["cpu_baseline"] = full
+        if one is not None:
+            obj["cpu_baseline_single_thread"] = one
+        res["workloads"][name] = obj
+        release(m2)
+        print("[bench] %s: %.4f ms/step, %.1f tokens/s, gate/up %.1f%% of %s peak"
+              % (name, m2["ms"], m2["tokens_per_s"], 100 * m2["roofline"]["frac"],
+                 m2["roofline"]["bound"]), file=sys.stderr, flush=True)
     print(json.dumps(res), flush=True)
 
 
@@ -326,6 +407,10 @@ def cpu_baseline_train(wl, dev, n_tok, min_seconds=10.0, max_reps=50):
     SW = tuple(as_u16(dev[n]) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
     f64 = oracle.bf16_to_f64
     Ts, K, H = len(toks), wl.K, wl.H
+    all_threads = oracle.num_threads()
+    if threads:
+        oracle.set_num_threads(threads)
+    cores = oracle.num_threads()
     reps = 0
     t0 = time.perf_counter()
     while True:

@@ -76,6 +76,8 @@ def _declare(L):
     L.oracle_router_bwd.argtypes = [_I, _I, _I, _I, _D, _P, _P, _P, _D, _P]
     L.oracle_layer_backward.argtypes = [_I] * 6 + [_D, _D, _I] + [_P] * 16 + [_D] + [_P] * 15
     L.oracle_num_threads.restype = _I
+    L.oracle_set_num_threads.argtypes = [_I]
+    L.oracle_set_num_threads.restype = None
     L.oracle_e4m3_from_float_array.argtypes = [ctypes.c_long, _P, _P]
     L.oracle_quant_rows_e4m3.argtypes = [_I, _I, _P, _P, _P]
     L.oracle_gateup_rows_w8a8.argtypes = [_I, _I, _I, _D] + [_P] * 7
@@ -105,6 +107,11 @@ def _i32(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the following oracle calls (its results do not depend on the count)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def bf16_from_double(v: float) -> int:

@@ -293,6 +293,14 @@ int oracle_num_threads(void) {
 #endif
 }
 
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 void oracle_router_logits(int T, int H, int E, const uint16_t* x, const uint16_t* wr,
                           const float* bias, const int32_t* tokens, int n_tok, float* logits) {
   const int n = tokens ? n_tok : T;

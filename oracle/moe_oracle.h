@@ -228,6 +228,8 @@ void oracle_layer_backward(int T, int H, int E, int K, int I, int norm_topk, dou
 
 /* Number of OpenMP threads the oracle's parallel loops use. */
 int oracle_num_threads(void);
+/* Threads of the following oracle calls (OpenMP; results do not depend on it). */
+void oracle_set_num_threads(int n);
 
 #ifdef __cplusplus
 }
