@@ -61,6 +61,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2) /* shape outside the supported set listed above          */
 #define MOE_ERR_WORKSPACE (-3)   /* ws_bytes smaller than the matching *_workspace_size     */
 #define MOE_ERR_HIP (-4)         /* a kernel launch failed (hipGetLastError)                */
+#define MOE_ERR_SCRATCH (-5)     /* moe_layer_forward_noalloc: workspace over its scratch   */
 
 /* Layer shape and constants (Hy4 config walkthrough, section "MoE routed experts"). */
 typedef struct moe_shape {
@@ -342,6 +343,27 @@ int moe_layer_backward(const moe_shape* shape, const uint16_t* x, const uint16_t
                        float* d_w_gate, float* d_w_up, float* d_w_down, float* d_s_gate,
                        float* d_s_up, float* d_s_down, float* d_topk_w, float* d_logits, void* ws,
                        size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It takes no workspace: the
+ * layer's workspace lives in a static device array of moe_layer_noalloc_scratch_bytes() bytes
+ * (64 MiB) that the library holds on every GPU it runs on until the process ends (the Hy4 decode
+ * batch, T = 64, needs about 12 MiB; T up to 416 fits at the Hy4 shape). Arguments, layout
+ * and results as moe_layer_forward (the same kernels, so the same bits). The call allocates and
+ * frees nothing; its first call on a device looks up that device's array address
+ * (hipGetSymbolAddress) once. It uses the array of the CURRENT device: a non-null stream must
+ * belong to it (else MOE_ERR_INVALID_ARG). MOE_ERR_SCRATCH when moe_layer_workspace_size(shape)
+ * exceeds the array. Nothing in the array needs to start at zero, and each call overwrites what
+ * the previous one left. Every call on one GPU shares its array: calls that overlap in time on
+ * one GPU (different streams, or host threads) race and give undefined results; serialise them
+ * (one stream, or events).                                                                        */
+size_t moe_layer_noalloc_scratch_bytes(void);
+int moe_layer_forward_noalloc(const moe_shape* shape, const uint16_t* x,
+                              const uint16_t* w_router, const float* bias,
+                              const uint16_t* w_gate, const uint16_t* w_up,
+                              const uint16_t* w_down, const uint16_t* s_gate,
+                              const uint16_t* s_up, const uint16_t* s_down, uint16_t* out,
+                              hipStream_t stream);
 
 /* The forward of a training step: moe_layer_forward, which also stores for moe_layer_backward
  * the fp32 gate and up sums g = x Wg^T, u = x Wu^T of every layer row (the pre-activation

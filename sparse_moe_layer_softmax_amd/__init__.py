@@ -21,6 +21,7 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
 
 EXPORTED = (
     "moe_strerror", "moe_route_workspace_size", "moe_route", "moe_permute_workspace_size",
@@ -30,6 +31,7 @@ EXPORTED = (
     "moe_route_train_workspace_size", "moe_route_train", "moe_layer_backward_workspace_size",
     "moe_layer_backward_workspace_layout", "moe_layer_backward", "moe_quantize_rows_e4m3",
     "moe_layer_w8a8_workspace_size", "moe_layer_w8a8_workspace_layout", "moe_layer_forward_w8a8",
+    "moe_layer_noalloc_scratch_bytes", "moe_layer_forward_noalloc",
 )
 MOE_LAYER_PHASE_EVENTS = 7
 
@@ -118,6 +120,8 @@ def _load():
         "moe_layer_w8a8_workspace_size": ([sp], S),
         "moe_layer_w8a8_workspace_layout": ([sp, ctypes.POINTER(moe_layer_a8_ws_layout)], ctypes.c_int),
         "moe_layer_forward_w8a8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
+        "moe_layer_noalloc_scratch_bytes": ([], S),
+        "moe_layer_forward_noalloc": ([sp] + [P] * 11, ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -255,6 +259,18 @@ def moe_expert_ffn(shape: Shape, n_groups: int, rows_max: int, x, row_to_slot, g
 def moe_combine(shape: Shape, y_routed, topk_w, slot_to_row, y_shared, out, stream=None):
     _check(library().moe_combine(ctypes.byref(shape.c()), _p(y_routed), _p(topk_w), _p(slot_to_row),
                            _p(y_shared), _p(out), _stream(stream)), "moe_combine")
+
+
+def moe_layer_noalloc_scratch_bytes() -> int:
+    return library().moe_layer_noalloc_scratch_bytes()
+
+
+def moe_layer_forward_noalloc(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,
+                              s_down, out, stream=None):
+    """moe_layer_forward on the library's static per-device scratch (no workspace argument)."""
+    _check(library().moe_layer_forward_noalloc(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_up), _p(w_down),
+        _p(s_gate), _p(s_up), _p(s_down), _p(out), _stream(stream)), "moe_layer_forward_noalloc")
 
 
 def moe_layer_forward_train(shape: Shape, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,

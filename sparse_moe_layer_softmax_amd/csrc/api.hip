@@ -4,6 +4,7 @@
 // stream untouched. The library allocates nothing and never synchronises.
 #include <cmath>
 #include <climits>
+#include <mutex>
 
 #include "moe.h"
 #include "ffn_kernels.h"
@@ -313,6 +314,31 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
   return rc;
 }
 
+// ----- the no-allocation entry point's scratch: one static device array per GPU, holding the
+// layer's workspace. Host code reaches it only through the address hipGetSymbolAddress returns
+// for the current device (the array's name is a host-side stand-in, not a device address).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device, set once under g_scratch_mu
+
+// The scratch address on the current device, looked up on the first call there.
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +350,7 @@ const char* moe_strerror(int code) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "shape needs more than the library's static scratch";
     default: return "unknown error";
   }
 }
@@ -473,6 +500,30 @@ int moe_layer_forward(const moe_shape* s, const uint16_t* x, const uint16_t* w_r
                       hipStream_t stream) {
   return moe_layer_forward_profiled(s, x, w_router, bias, w_gate, w_up, w_down, s_gate, s_up,
                                     s_down, out, ws, ws_bytes, stream, nullptr);
+}
+
+size_t moe_layer_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int moe_layer_forward_noalloc(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                              const float* bias, const uint16_t* w_gate, const uint16_t* w_up,
+                              const uint16_t* w_down, const uint16_t* s_gate,
+                              const uint16_t* s_up, const uint16_t* s_down, uint16_t* out,
+                              hipStream_t stream) {
+  const int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (layer_ws(*s).pub.total > kScratchBytes) return MOE_ERR_SCRATCH;
+  if (stream) {  // the scratch is the current device's: the stream must run there
+    int cur = -1;
+    hipDevice_t sd = -1;
+    if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sd) != hipSuccess)
+      return MOE_ERR_HIP;
+    if (sd != cur) return MOE_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  const int rs = current_scratch(&ws);
+  if (rs != MOE_OK) return rs;
+  return layer_impl(s, x, w_router, bias, Weights::bf16(w_gate, w_up, w_down),
+                    Weights::bf16(s_gate, s_up, s_down), out, ws, kScratchBytes, stream, nullptr);
 }
 
 int moe_layer_forward_train(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,

@@ -45,7 +45,7 @@ void* const PW = reinterpret_cast<void*>(uintptr_t(1) << 20);
 }  // namespace
 
 int main() {
-  for (int code = -5; code <= 1; ++code)
+  for (int code = -6; code <= 1; ++code)
     if (!moe_strerror(code)) ++failures;
 
   // sizes and layouts over a range of shapes, including the extremes the checks accept
@@ -94,6 +94,9 @@ int main() {
     expect(moe_layer_forward(&bad[i], P16, P16, nullptr, P16, P16, P16, P16, P16, P16, P16, PW,
                              size_t(1) << 40, nullptr),
            want[i], "moe_layer_forward bad shape");
+    expect(moe_layer_forward_noalloc(&bad[i], P16, P16, nullptr, P16, P16, P16, P16, P16, P16,
+                                     P16, nullptr),
+           want[i], "moe_layer_forward_noalloc bad shape");
     expect(moe_combine(&bad[i], P16, PF, PI, nullptr, P16, nullptr), want[i], "moe_combine bad shape");
   }
 
@@ -149,6 +152,12 @@ int main() {
                             nullptr, P16, 0.f, P16, PF, PF, PF, PF, PF, PF, PF, nullptr, nullptr, PW,
                             size_t(1) << 60, nullptr),
          MOE_ERR_UNSUPPORTED, "backward operands past 64 GiB");
+  for (int T : {417, 8192}) {  // 416 tokens is the largest Hy4 batch the 64 MiB scratch holds
+    moe_shape pre = hy4(T);
+    expect(moe_layer_forward_noalloc(&pre, P16, P16, nullptr, P16, P16, P16, P16, P16, P16, P16,
+                                     nullptr),
+           MOE_ERR_SCRATCH, "noalloc past its scratch");
+  }
   std::printf("abi driver: %d failure(s)\n", failures);
   return failures ? 1 : 0;
 }
