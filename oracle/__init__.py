@@ -15,7 +15,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRCS = [os.path.join(_HERE, "moe_oracle.cpp"), os.path.join(_HERE, "moe_oracle_bwd.cpp"),
-         os.path.join(_HERE, "moe_oracle_w8a8.cpp")]
+         os.path.join(_HERE, "moe_oracle_w8a8.cpp"), os.path.join(_HERE, "moe_oracle_mx.cpp")]
 _LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
 _lib = None
 
@@ -84,6 +84,14 @@ def _declare(L):
     L.oracle_down_rows_w8a8.argtypes = [_I, _I, _I] + [_P] * 5
     L.oracle_layer_forward_w8a8.argtypes = ([_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 15 + [_I]
                                             + [_P] * 14)
+    L.oracle_mx_scale_of_amax.argtypes = [_D]
+    L.oracle_mx_scale_of_amax.restype = ctypes.c_uint8
+    L.oracle_mx_quant_rows.argtypes = [_I, _I, _P, _P, _P]
+    L.oracle_mx_dequant.argtypes = [_I, _I, _P, _P, _P]
+    L.oracle_gateup_rows_mx.argtypes = [_I, _I, _I, _D] + [_P] * 7
+    L.oracle_down_rows_mx.argtypes = [_I, _I, _I] + [_P] * 5
+    L.oracle_layer_forward_mx.argtypes = ([_I, _I, _I, _I, _I, _I, _D, _D, _I] + [_P] * 15 + [_I]
+                                          + [_P] * 14)
 
 
 def _ptr(a):
@@ -424,6 +432,120 @@ def layer_forward_w8a8(x, wr, wg: Fp8, wu: Fp8, wd: Fp8, K, *, bias=None, sg=Non
     lib().oracle_layer_forward_w8a8(
         T, H, E, K, I, int(bool(norm_topk)), float(scale), float(limit), int(capacity),
         _ptr(x), _ptr(wr), _ptr(_f32(bias)), *_fp8_ptrs(wg, wu, wd, sg, su, sd), int(use_logits),
+        _ptr(lg), _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
+        _ptr(r["row_to_slot"]), _ptr(r["slot_to_row"]), _ptr(r["xq"]), _ptr(r["x_scale"]),
+        _ptr(r["h_routed"]), _ptr(r["y_routed"]), _ptr(r.get("h_shared")), _ptr(r.get("y_shared")),
+        _ptr(r["out"]))
+    return r
+
+
+# ------------------------------------------------------ MX block-scaled FP8 (MXFP8) operands
+MX_BLOCK = 32
+
+
+class Mx:
+    """An MX matrix (or stack of matrices): E4M3 codes ``q`` (uint8, [..., rows, cols]) and E8M0
+    scale bytes ``s`` (uint8, [..., rows, cols / 32]); value = e4m3(q) * 2^(s - 127), one scale per
+    32 consecutive elements of a row."""
+
+    def __init__(self, q, s):
+        self.q = np.ascontiguousarray(np.asarray(q, dtype=np.uint8))
+        self.s = np.ascontiguousarray(np.asarray(s, dtype=np.uint8))
+        assert self.q.shape[-1] % MX_BLOCK == 0
+        assert self.s.shape == self.q.shape[:-1] + (self.q.shape[-1] // MX_BLOCK,)
+
+    @property
+    def shape(self):
+        return self.q.shape
+
+
+def mx_scale_of_amax(amax: float) -> int:
+    """E8M0 scale byte of a block whose largest magnitude is amax."""
+    return int(lib().oracle_mx_scale_of_amax(float(amax)))
+
+
+def mx_quant_rows(v):
+    """MX quantisation of bf16 rows [rows, cols] -> (codes uint8 [rows, cols], scale bytes uint8
+    [rows, cols / 32])."""
+    v = _u16(v)
+    rows, cols = v.shape
+    codes = np.zeros((rows, cols), dtype=np.uint8)
+    scales = np.zeros((rows, cols // MX_BLOCK), dtype=np.uint8)
+    if rows:
+        lib().oracle_mx_quant_rows(rows, cols, _ptr(v), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def mx_dequant(codes, scales):
+    """Values (float64 [rows, cols]) of MX data."""
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    scales = np.ascontiguousarray(np.asarray(scales, dtype=np.uint8))
+    rows, cols = codes.shape
+    out = np.zeros((rows, cols), dtype=np.float64)
+    if rows:
+        lib().oracle_mx_dequant(rows, cols, _ptr(codes), _ptr(scales), _ptr(out))
+    return out
+
+
+def gateup_rows_mx(xq, xs, wg: Mx, wu: Mx, limit):
+    xq = np.ascontiguousarray(np.asarray(xq, dtype=np.uint8))
+    xs = np.ascontiguousarray(np.asarray(xs, dtype=np.uint8))
+    n, H = xq.shape
+    I = wg.q.shape[0]
+    h = np.zeros((n, I), dtype=np.uint16)
+    if n:
+        lib().oracle_gateup_rows_mx(n, H, I, float(limit), _ptr(xq), _ptr(xs), _ptr(wg.q), _ptr(wg.s),
+                                    _ptr(wu.q), _ptr(wu.s), _ptr(h))
+    return h
+
+
+def down_rows_mx(hq, hs, wd: Mx):
+    hq = np.ascontiguousarray(np.asarray(hq, dtype=np.uint8))
+    hs = np.ascontiguousarray(np.asarray(hs, dtype=np.uint8))
+    n, I = hq.shape
+    H = wd.q.shape[0]
+    y = np.zeros((n, H), dtype=np.uint16)
+    if n:
+        lib().oracle_down_rows_mx(n, H, I, _ptr(hq), _ptr(hs), _ptr(wd.q), _ptr(wd.s), _ptr(y))
+    return y
+
+
+def _mx_ptrs(*ws):
+    out = []
+    for w in ws:
+        out += [None, None] if w is None else [_ptr(w.q), _ptr(w.s)]
+    return out
+
+
+def layer_forward_mx(x, wr, wg: Mx, wu: Mx, wd: Mx, K, *, bias=None, sg=None, su=None, sd=None,
+                     scale=1.0, limit=10.0, capacity=0, norm_topk=True, logits=None):
+    """The layer with MX expert weights and MX activations; returns the dict of layer_forward_w8a8
+    with x_scale the block scale bytes [T, H / 32]."""
+    x, wr = _u16(x), _u16(wr)
+    T, H = x.shape
+    E, I = wg.q.shape[0], wg.q.shape[1]
+    use_logits = logits is not None
+    lg = _f32(logits).copy() if use_logits else np.zeros((T, E), dtype=np.float32)
+    r = dict(
+        logits=lg,
+        topk_idx=np.zeros((T, K), dtype=np.int32),
+        topk_w=np.zeros((T, K), dtype=np.float32),
+        counts=np.zeros(E, dtype=np.int32),
+        offsets=np.zeros(E + 1, dtype=np.int32),
+        row_to_slot=np.zeros(T * K, dtype=np.int32),
+        slot_to_row=np.zeros(T * K, dtype=np.int32),
+        xq=np.zeros((T, H), dtype=np.uint8),
+        x_scale=np.zeros((T, H // MX_BLOCK), dtype=np.uint8),
+        h_routed=np.zeros((T * K, I), dtype=np.uint16),
+        y_routed=np.zeros((T * K, H), dtype=np.uint16),
+        out=np.zeros((T, H), dtype=np.uint16),
+    )
+    if sg is not None:
+        r["h_shared"] = np.zeros((T, I), dtype=np.uint16)
+        r["y_shared"] = np.zeros((T, H), dtype=np.uint16)
+    lib().oracle_layer_forward_mx(
+        T, H, E, K, I, int(bool(norm_topk)), float(scale), float(limit), int(capacity),
+        _ptr(x), _ptr(wr), _ptr(_f32(bias)), *_mx_ptrs(wg, wu, wd, sg, su, sd), int(use_logits),
         _ptr(lg), _ptr(r["topk_idx"]), _ptr(r["topk_w"]), _ptr(r["counts"]), _ptr(r["offsets"]),
         _ptr(r["row_to_slot"]), _ptr(r["slot_to_row"]), _ptr(r["xq"]), _ptr(r["x_scale"]),
         _ptr(r["h_routed"]), _ptr(r["y_routed"]), _ptr(r.get("h_shared")), _ptr(r.get("y_shared")),

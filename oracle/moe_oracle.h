@@ -172,6 +172,30 @@ void oracle_layer_forward_w8a8(int T, int H, int E, int K, int I, int norm_topk,
                                uint16_t* h_routed, uint16_t* y_routed, uint16_t* h_shared,
                                uint16_t* y_shared, uint16_t* out);
 
+// ---- MX block-scaled FP8 weights and activations (MXFP8), moe_oracle_mx.cpp. One E8M0 scale
+// byte s (value 2^(s - 127)) per 32 consecutive elements along the reduction dimension, OCP E4M3
+// elements; activations quantised per block by the OCP Microscaling conversion rule (shared
+// exponent floor(log2(amax)) - 8, clamped to [-127, 127]; elements nearest-even, saturating).
+uint8_t oracle_mx_scale_of_amax(double amax);
+void oracle_mx_quant_rows(int rows, int cols, const uint16_t* v, uint8_t* codes, uint8_t* scales);
+void oracle_mx_dequant(int rows, int cols, const uint8_t* codes, const uint8_t* scales, double* out);
+void oracle_gateup_rows_mx(int n, int H, int I, double limit, const uint8_t* xq, const uint8_t* xs,
+                           const uint8_t* qg, const uint8_t* sg, const uint8_t* qu, const uint8_t* su,
+                           uint16_t* h);
+void oracle_down_rows_mx(int n, int H, int I, const uint8_t* hq, const uint8_t* hs, const uint8_t* qd,
+                         const uint8_t* sd, uint16_t* y);
+void oracle_layer_forward_mx(int T, int H, int E, int K, int I, int norm_topk, double scale,
+                             double limit, int capacity, const uint16_t* x, const uint16_t* wr,
+                             const float* bias, const uint8_t* qg, const uint8_t* sg,
+                             const uint8_t* qu, const uint8_t* su, const uint8_t* qd,
+                             const uint8_t* sd, const uint8_t* sqg, const uint8_t* ssg,
+                             const uint8_t* squ, const uint8_t* ssu, const uint8_t* sqd,
+                             const uint8_t* ssd, int use_logits, float* logits, int32_t* topk_idx,
+                             float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* row_to_slot, int32_t* slot_to_row, uint8_t* xq, uint8_t* xs,
+                             uint16_t* h_routed, uint16_t* y_routed, uint16_t* h_shared,
+                             uint16_t* y_shared, uint16_t* out);
+
 /* Training-side router statistics (Hy3 deep-dive, SparseMoERouter training branch and its
  * load-balancing loss): from fp32 logits [T,E] (bias and noise already added) and the top-k
  * indices [T,K]:

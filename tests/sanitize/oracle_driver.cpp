@@ -125,6 +125,30 @@ void run_layer(int T, int H, int E, int K, int I, int capacity, bool shared) {
                             hr.data(), yr.data(), shared ? hs.data() : nullptr,
                             shared ? ys.data() : nullptr, out8.data());
 
+  // MX block-scaled FP8 weights and activations (scales one byte per 32 elements)
+  auto mxs = [&](size_t n) {
+    std::uniform_int_distribution<int> ud(112, 132);
+    std::vector<uint8_t> v(n);
+    for (auto& c : v) c = static_cast<uint8_t>(ud(rng));
+    return v;
+  };
+  if (H % 32 == 0 && I % 32 == 0) {
+    auto mg = mxs(size_t(E) * I * H / 32), mu = mxs(size_t(E) * I * H / 32), md = mxs(size_t(E) * H * I / 32);
+    auto smg = mxs(size_t(I) * H / 32), smu = mxs(size_t(I) * H / 32), smd = mxs(size_t(H) * I / 32);
+    std::vector<uint8_t> xs(size_t(T) * H / 32);
+    Routing rm = r;
+    oracle_layer_forward_mx(T, H, E, K, I, 1, 2.827, 10.0, capacity, x.data(), wr.data(), bias.data(),
+                            qg.data(), mg.data(), qu.data(), mu.data(), qd.data(), md.data(),
+                            shared ? sqg.data() : nullptr, smg.data(), shared ? squ.data() : nullptr,
+                            smu.data(), shared ? sqd.data() : nullptr, smd.data(), 1, r.logits.data(),
+                            rm.idx.data(), rm.topk_w.data(), rm.counts.data(), rm.offsets.data(),
+                            rm.r2s.data(), rm.s2r.data(), xq.data(), xs.data(), hr.data(), yr.data(),
+                            shared ? hs.data() : nullptr, shared ? ys.data() : nullptr, out8.data());
+    std::vector<double> deq(size_t(T) * H);
+    oracle_mx_dequant(T, H, xq.data(), xs.data(), deq.data());
+    for (double d : deq) check(std::isfinite(d), "finite MX value");
+  }
+
   // backward, rounded and exact
   auto dout = bf16s(size_t(T) * H, 1.0);
   const size_t R = size_t(r.offsets[E]);
