@@ -57,8 +57,10 @@ def algorithmic(wl, counts):
     R = int(counts.sum())
     touched = int((counts > 0).sum())
     # bytes of one expert's gate+up and down weights: bf16, or one-byte E4M3 codes plus one fp32
-    # scale per weight row
-    if wl.fp8:
+    # scale per weight row, or (MX) plus one scale byte per 32 codes
+    if wl.mx:
+        w_gu, w_dn = 2 * H * I + 2 * H * I // 32, H * I + H * I // 32
+    elif wl.fp8:
         w_gu, w_dn = 2 * H * I + 4 * 2 * I, H * I + 4 * H
     else:
         w_gu, w_dn = 4 * H * I, 2 * H * I
@@ -66,8 +68,14 @@ def algorithmic(wl, counts):
     layer_bytes = (touched + S) * (w_gu + w_dn) + 2 * E * H + 2 * 2 * T * H + 4 * T * E + 8 * T * K
     # gate/up grouped GEMM launch: its weights, x in, h out
     gu_flops = 4 * H * I * (R + S * T)
-    # activations read by the projections: bf16, or E4M3 codes plus one fp32 scale per row
-    a_x, a_h = (T * (H + 4), (R + S * T) * (I + 4)) if wl.act_fp8 else (2 * T * H, 2 * (R + S * T) * I)
+    # activations read by the projections: bf16, or E4M3 codes plus one fp32 scale per row, or
+    # (MX) plus one scale byte per 32 codes of each GEMM row
+    if wl.mx:
+        a_x, a_h = T * H + (R + S * T) * H // 32, (R + S * T) * (I + I // 32)
+    elif wl.act_fp8:
+        a_x, a_h = T * (H + 4), (R + S * T) * (I + 4)
+    else:
+        a_x, a_h = 2 * T * H, 2 * (R + S * T) * I
     gu_bytes = (touched + S) * w_gu + a_x + 2 * (R + S * T) * I
     # down grouped GEMM launch: its weights, h in, y out
     dn_flops = 2 * H * I * (R + S * T)
@@ -129,6 +137,9 @@ def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50, threads=0):
     experts = sorted(set(int(e) for e in idx.ravel()))
     def host_w(name, e=None):
         t = dev[name] if e is None else dev[name][e]
+        if wl.mx:
+            sc = dev[name + "_mx"] if e is None else dev[name + "_mx"][e]
+            return oracle.Mx(t.cpu().numpy(), sc.cpu().numpy())
         if wl.fp8:
             sc = dev[name + "_scale"] if e is None else dev[name + "_scale"][e]
             return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
@@ -140,7 +151,13 @@ def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50, threads=0):
         hq, sh = oracle.quant_rows_e4m3(h)
         return h, oracle.down_rows_w8a8(hq, sh, wd)
 
-    ffn = (ffn_w8a8 if wl.act_fp8 else
+    def ffn_mx(x_rows, wg, wu, wd, limit):
+        xq, xs = oracle.mx_quant_rows(x_rows)
+        h = oracle.gateup_rows_mx(xq, xs, wg, wu, limit)
+        hq, hs = oracle.mx_quant_rows(h)
+        return h, oracle.down_rows_mx(hq, hs, wd)
+
+    ffn = (ffn_mx if wl.mx else ffn_w8a8 if wl.act_fp8 else
            oracle.expert_ffn_rows_fp8 if wl.fp8 else oracle.expert_ffn_rows)
     W = {e: tuple(host_w(n, e) for n in ("w_gate", "w_up", "w_down")) for e in experts}
     SW = tuple(host_w(n) for n in ("s_gate", "s_up", "s_down")) if wl.n_shared else None
@@ -241,9 +258,17 @@ def measure(wl, args):
     rows = wl.T * wl.K + wl.n_shared * wl.T
     groups = wl.E + wl.n_shared
     if rows >= 64 * groups:
-        gu, dn = (("kEpiSwiglu88", "kEpiBf16_88") if wl.act_fp8 else
+        gu, dn = (("kEpiSwigluMx", "kEpiBf16Mx") if wl.mx else
+                  ("kEpiSwiglu88", "kEpiBf16_88") if wl.act_fp8 else
                   ("kEpiSwiglu8", "kEpiBf16_8") if wl.fp8 else ("kEpiSwiglu", "kEpiBf16"))
-        kname, dname = "ffn_tiled_kernel<%s>" % gu, "ffn_tiled_kernel<%s>" % dn
+        # second template argument: the buffer-descriptor form, which the library picks when the
+        # activation operand and each weight matrix hold at most 4 GiB
+        ab, wb = (1 if wl.act_fp8 else 2), (1 if wl.fp8 else 2)
+        lim = 0xFFFFFFFF
+        gu_buf = wl.T * wl.H * ab <= lim and wl.I * wl.H * wb <= lim
+        dn_buf = (wl.T + wl.T * wl.K) * wl.I * ab <= lim and wl.H * wl.I * wb <= lim
+        kname = "ffn_tiled_kernel<%s,%s>" % (gu, str(gu_buf).lower())
+        dname = "ffn_tiled_kernel<%s,%s>" % (dn, str(dn_buf).lower())
     else:
         # the weight-streaming kernel: <gated, FP8 weights, FP8 activations, 16-row sub-blocks
         # per tile>; 16-row tiles (one sub-block) when the groups average at most 16 rows
@@ -251,6 +276,8 @@ def measure(wl, args):
         fl = ("true" if wl.fp8 else "false", "true" if wl.act_fp8 else "false", maxns)
         kname = "ffn_skinny_kernel<true, %s, %s, %d>" % fl
         dname = "ffn_skinny_kernel<false, %s, %s, %d>" % fl
+        if wl.mx:  # fifth template argument: the MX form
+            kname, dname = kname[:-1] + ", true>", dname[:-1] + ", true>"
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
@@ -272,8 +299,10 @@ def measure(wl, args):
               "n_shared": wl.n_shared, "routed_scaling": wl.scale, "swiglu_limit": wl.limit,
               "capacity": wl.capacity, "router_bias": "zipf %.1f" % wl.zipf if wl.zipf else "none",
               "parallelism": "none (1 GPU)",
-              "expert_weights": "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16",
-              "expert_activations": ("fp8_e4m3 + fp32 row scale (dynamic)" if wl.act_fp8
+              "expert_weights": ("mxfp8: fp8_e4m3 + e8m0 scale per 32" if wl.mx else
+                                 "fp8_e4m3 + fp32 row scale" if wl.fp8 else "bf16"),
+              "expert_activations": ("mxfp8: fp8_e4m3 + e8m0 scale per 32 (dynamic)" if wl.mx else
+                                     "fp8_e4m3 + fp32 row scale (dynamic)" if wl.act_fp8
                                      else "bf16")}
     return dict(dev=dev, ms=ms, tokens_per_s=wl.T / layer_s, roofline=rf, down_gemm=dn,
                 layer=layer_obj, phases_ms={k: round(v, 4) for k, v in phase_ms.items()},

@@ -295,6 +295,54 @@ int moe_layer_forward_w8a8(const moe_shape* shape, const uint16_t* x, const uint
                            const float* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
                            hipStream_t stream, hipEvent_t const* phase_events);
 
+/* ---------------------------------------------------- MX block-scaled FP8 weights and activations
+ * The same FP8 deployment with per-block scales, in the OCP Microscaling (MX v1.0) MXFP8 form
+ * that the gfx950 scaled FP8 matrix instructions apply natively: one E8M0 scale byte s (value
+ * 2^(s - 127), s = 255 not allowed) per 32 consecutive elements along the reduction dimension,
+ * elements OCP E4M3. Scale arrays are K-tile-major: for a matrix [N][K] (K a multiple of 128)
+ * the byte of row n, block b is at  ((b / 4) * N + n) * 4 + b % 4,  i.e. [K/128][N][4] (routed
+ * experts: E such arrays back to back, like the codes).
+ * The activations entering each expert projection are quantised per row and block on the fly:
+ *   shared = floor(log2(amax)) - 8 clamped to [-127, 127] (amax: the block's largest |v|; an
+ *   all-zero block takes -127), s = shared + 127,  code = E4M3_RNE(clamp(v / 2^shared, +-448)).
+ * A projection is sum_k e4m3(a)2^(sa-127) e4m3(w)2^(sw-127) with fp32 accumulation, rounded
+ * where the bf16 path rounds (h, y, out). The weight-streaming path (few rows per expert) decodes
+ * each code times its scale to bf16, exact for scale bytes 10..245.
+ *
+ * moe_quantize_rows_mx: that quantisation on its own.
+ *   x [rows, cols] bf16 (16-byte aligned), codes [rows, cols] uint8 (8-byte aligned),
+ *   scales [cols/128][rows][4] bytes (4-byte aligned); rows >= 1, cols a positive multiple of 128.
+ * Returns MOE_ERR_INVALID_ARG for a NULL pointer, bad sizes or bad alignment.
+ *
+ * moe_layer_forward_mx: moe_layer_forward_fp8 with MX weights (each fp32 scale array replaced by
+ * its E8M0 byte array) and MX activations; outputs as moe_layer_forward.
+ * ws: moe_layer_mx_workspace_size(shape) bytes, 256-byte aligned. Its first part has the layout
+ * moe_layer_workspace_layout gives; the quantised activations follow at the offsets of
+ * moe_layer_mx_workspace_layout. Their scales are planes [K/128][scale_rows][4] indexed by the
+ * row of the projection's grouped GEMM (shared-expert rows [0, T) first when n_shared = 1, then
+ * the routed rows in slot_to_row order).                                                       */
+typedef struct moe_layer_mx_ws_layout {
+  size_t xq;         /* [T,H] E4M3 codes of x (token order)                              */
+  size_t x_scale;    /* [H/128][scale_rows][4] E8M0 bytes of x, by gate/up GEMM row      */
+  size_t hq;         /* [T + T*K, I] E4M3 codes of h, rows as in h (valid rows only)     */
+  size_t h_scale;    /* [I/128][scale_rows][4] E8M0 bytes of h, by row of h              */
+  size_t scale_rows; /* rows of a scale plane: T*K (+ T with a shared expert) + 320       */
+  size_t total;      /* bytes of the whole workspace                                     */
+} moe_layer_mx_ws_layout;
+
+int moe_quantize_rows_mx(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes,
+                         uint8_t* scales, hipStream_t stream);
+size_t moe_layer_mx_workspace_size(const moe_shape* shape);
+int moe_layer_mx_workspace_layout(const moe_shape* shape, moe_layer_mx_ws_layout* layout);
+int moe_layer_forward_mx(const moe_shape* shape, const uint16_t* x, const uint16_t* w_router,
+                         const float* bias, const uint8_t* w_gate, const uint8_t* w_gate_scale,
+                         const uint8_t* w_up, const uint8_t* w_up_scale, const uint8_t* w_down,
+                         const uint8_t* w_down_scale, const uint8_t* s_gate,
+                         const uint8_t* s_gate_scale, const uint8_t* s_up,
+                         const uint8_t* s_up_scale, const uint8_t* s_down,
+                         const uint8_t* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t const* phase_events);
+
 /* ================================================================ backward pass (training)
  * The routers on the pages are trained (Hy3 deep-dive `SparseMoERouter`: training branch with a
  * load-balancing loss and count EMAs; Hy4 deep-dive `MoERouter`: noise on the scores in

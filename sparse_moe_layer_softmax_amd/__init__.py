@@ -31,7 +31,8 @@ EXPORTED = (
     "moe_route_train_workspace_size", "moe_route_train", "moe_layer_backward_workspace_size",
     "moe_layer_backward_workspace_layout", "moe_layer_backward", "moe_quantize_rows_e4m3",
     "moe_layer_w8a8_workspace_size", "moe_layer_w8a8_workspace_layout", "moe_layer_forward_w8a8",
-    "moe_layer_noalloc_scratch_bytes", "moe_layer_forward_noalloc",
+    "moe_layer_noalloc_scratch_bytes", "moe_layer_forward_noalloc", "moe_quantize_rows_mx",
+    "moe_layer_mx_workspace_size", "moe_layer_mx_workspace_layout", "moe_layer_forward_mx",
 )
 MOE_LAYER_PHASE_EVENTS = 7
 
@@ -56,6 +57,10 @@ class moe_layer_ws_layout(ctypes.Structure):
 
 class moe_layer_a8_ws_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in ("xq", "x_scale", "hq", "h_scale", "total")]
+
+
+class moe_layer_mx_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("xq", "x_scale", "hq", "h_scale", "scale_rows", "total")]
 
 
 class moe_bwd_ws_layout(ctypes.Structure):
@@ -122,6 +127,10 @@ def _load():
         "moe_layer_forward_w8a8": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
         "moe_layer_noalloc_scratch_bytes": ([], S),
         "moe_layer_forward_noalloc": ([sp] + [P] * 11, ctypes.c_int),
+        "moe_quantize_rows_mx": ([P, I32, I32, P, P, P], ctypes.c_int),
+        "moe_layer_mx_workspace_size": ([sp], S),
+        "moe_layer_mx_workspace_layout": ([sp, ctypes.POINTER(moe_layer_mx_ws_layout)], ctypes.c_int),
+        "moe_layer_forward_mx": ([sp] + [P] * 17 + [S, P, P], ctypes.c_int),
     }
     for name, (argtypes, restype) in sig.items():
         fn = getattr(L, name)
@@ -353,6 +362,37 @@ def moe_layer_forward_w8a8(shape: Shape, x, w_router, bias, w_gate, w_gate_scale
         "moe_layer_forward_w8a8")
 
 
+def moe_quantize_rows_mx(x, codes, scales, stream=None):
+    """MX block quantisation: x [rows, cols] bf16 -> codes uint8 [rows, cols], scale bytes
+    [cols/128][rows][4] (K-tile-major)."""
+    rows, cols = x.shape
+    _check(library().moe_quantize_rows_mx(_p(x), rows, cols, _p(codes), _p(scales), _stream(stream)),
+           "moe_quantize_rows_mx")
+
+
+def moe_layer_mx_workspace_size(shape: Shape) -> int:
+    return library().moe_layer_mx_workspace_size(ctypes.byref(shape.c()))
+
+
+def moe_layer_mx_workspace_layout(shape: Shape) -> dict:
+    lay = moe_layer_mx_ws_layout()
+    _check(library().moe_layer_mx_workspace_layout(ctypes.byref(shape.c()), ctypes.byref(lay)),
+           "moe_layer_mx_workspace_layout")
+    return {n: getattr(lay, n) for n, _ in moe_layer_mx_ws_layout._fields_}
+
+
+def moe_layer_forward_mx(shape: Shape, x, w_router, bias, w_gate, w_gate_scale, w_up, w_up_scale,
+                         w_down, w_down_scale, s_gate, s_gate_scale, s_up, s_up_scale, s_down,
+                         s_down_scale, out, ws, phase_events=None, stream=None):
+    """The layer with MX block-scaled FP8 weights and activations (scale bytes K-tile-major)."""
+    _check(library().moe_layer_forward_mx(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(w_gate), _p(w_gate_scale),
+        _p(w_up), _p(w_up_scale), _p(w_down), _p(w_down_scale), _p(s_gate), _p(s_gate_scale),
+        _p(s_up), _p(s_up_scale), _p(s_down), _p(s_down_scale), _p(out), _p(ws),
+        ws.numel() if ws is not None else 0, _stream(stream), phase_events),
+        "moe_layer_forward_mx")
+
+
 # ----------------------------------------------------------------------------- conveniences
 _WEIGHTS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 
@@ -361,15 +401,29 @@ class MoELayer:
     """Holds device weights and a workspace; ``forward(x)`` runs moe_layer_forward (bf16 expert
     weights) or moe_layer_forward_fp8 (uint8 E4M3 expert weights; ``scales`` then maps each weight
     name of _WEIGHTS to its fp32 per-row scale tensor); with ``act_fp8`` (FP8 weights only)
-    moe_layer_forward_w8a8, which quantises the expert activations per row as well."""
+    moe_layer_forward_w8a8, which quantises the expert activations per row as well; with
+    ``mx_scales`` (E8M0 block-scale bytes [..., rows, cols / 32] per weight name) instead of
+    ``scales``, moe_layer_forward_mx, which takes them K-tile-major ([..., cols / 128, rows, 4],
+    a layout change made here once)."""
 
     def __init__(self, shape: Shape, w_router, w_gate, w_up, w_down, s_gate=None, s_up=None,
-                 s_down=None, router_bias=None, scales=None, act_fp8=False):
+                 s_down=None, router_bias=None, scales=None, act_fp8=False, mx_scales=None):
         self.shape = shape
         self.w = (w_router, router_bias, w_gate, w_up, w_down, s_gate, s_up, s_down)
         self.fp8 = w_gate.dtype == torch.uint8
+        self.mx = mx_scales is not None
         self.scales = scales or {}
-        if self.fp8:
+        if self.mx:
+            self.scales = {}
+            for n, t in zip(_WEIGHTS, (w_gate, w_up, w_down, s_gate, s_up, s_down)):
+                m = mx_scales.get(n)
+                if t is not None and m is None:
+                    raise ValueError("MX weight %s needs its block scales" % n)
+                if m is not None:  # [..., rows, cols/32] -> [..., cols/128, rows, 4]
+                    r, nb = m.shape[-2], m.shape[-1]
+                    self.scales[n] = m.reshape(*m.shape[:-2], r, nb // 4, 4).transpose(-3, -2).contiguous()
+            act_fp8 = True
+        elif self.fp8:
             for n, t in zip(_WEIGHTS, (w_gate, w_up, w_down, s_gate, s_up, s_down)):
                 if t is not None and self.scales.get(n) is None:
                     raise ValueError("FP8 weight %s needs a scale tensor" % n)
@@ -378,7 +432,11 @@ class MoELayer:
         self.act_fp8 = act_fp8
         self.device = w_router.device
         self.layout = moe_layer_workspace_layout(shape)
-        if act_fp8:
+        if self.mx:
+            self.layout.update({k: v for k, v in moe_layer_mx_workspace_layout(shape).items()
+                                if k != "total"})
+            self.ws = _ws(moe_layer_mx_workspace_size(shape), self.device)
+        elif act_fp8:
             self.layout.update({k: v for k, v in moe_layer_w8a8_workspace_layout(shape).items()
                                 if k != "total"})
             self.ws = _ws(moe_layer_w8a8_workspace_size(shape), self.device)
@@ -389,8 +447,10 @@ class MoELayer:
     def from_inputs(cls, shape: Shape, d: dict):
         """Build from a ``workloads.generate`` dict (bf16 or FP8 expert weights)."""
         scales = {n: d.get(n + "_scale") for n in _WEIGHTS}
+        mx = {n: d.get(n + "_mx") for n in _WEIGHTS} if d.get("mx") else None
         return cls(shape, d["w_router"], d["w_gate"], d["w_up"], d["w_down"], d["s_gate"], d["s_up"],
-                   d["s_down"], d["router_bias"], scales=scales, act_fp8=bool(d.get("act_fp8")))
+                   d["s_down"], d["router_bias"], scales=scales, act_fp8=bool(d.get("act_fp8")),
+                   mx_scales=mx)
 
     def forward(self, x, out=None, stream=None, phase_events=None, train=False):
         """The layer's output. train=True: moe_layer_forward_train, keeping the fp32 gate/up sums
@@ -411,7 +471,8 @@ class MoELayer:
             self._gu = self.gu
         elif self.fp8:
             sc = self.scales
-            fwd = moe_layer_forward_w8a8 if self.act_fp8 else moe_layer_forward_fp8
+            fwd = (moe_layer_forward_mx if self.mx else
+                   moe_layer_forward_w8a8 if self.act_fp8 else moe_layer_forward_fp8)
             fwd(self.shape, x, wr, b, wg, sc["w_gate"], wu, sc["w_up"], wd, sc["w_down"], sg,
                 sc.get("s_gate"), su, sc.get("s_up"), sd, sc.get("s_down"), out, self.ws,
                 phase_events, stream)

@@ -120,12 +120,14 @@ inline bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 25
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
-// One set of expert weights (gate, up, down): bf16, or FP8 E4M3 codes with per-row scales.
+// One set of expert weights (gate, up, down): bf16, or FP8 E4M3 codes with per-row scales, or
+// E4M3 codes with MX block scales (E8M0 bytes, [K/128][N][4] per matrix).
 struct Weights {
-  bool w8;
+  bool w8, mx;
   const uint16_t *gate, *up, *down;
   const uint8_t *qgate, *qup, *qdown;
   const float *sgate, *sup, *sdown;
+  const uint8_t *xgate, *xup, *xdown;
   static Weights bf16(const uint16_t* g, const uint16_t* u, const uint16_t* d) {
     Weights w{};
     w.gate = g;
@@ -145,13 +147,27 @@ struct Weights {
     w.sdown = ds;
     return w;
   }
+  static Weights mxfp8(const uint8_t* g, const uint8_t* gs, const uint8_t* u, const uint8_t* us,
+                       const uint8_t* d, const uint8_t* ds) {
+    Weights w{};
+    w.w8 = w.mx = true;
+    w.qgate = g;
+    w.xgate = gs;
+    w.qup = u;
+    w.xup = us;
+    w.qdown = d;
+    w.xdown = ds;
+    return w;
+  }
   // every pointer of the set given
   bool complete() const {
+    if (mx) return qgate && xgate && qup && xup && qdown && xdown;
     return w8 ? (qgate && sgate && qup && sup && qdown && sdown) : (gate && up && down);
   }
   // no pointer of the set given
   bool empty() const {
-    return !gate && !up && !down && !qgate && !sgate && !qup && !sup && !qdown && !sdown;
+    return !gate && !up && !down && !qgate && !sgate && !qup && !sup && !qdown && !sdown && !xgate &&
+           !xup && !xdown;
   }
 };
 
@@ -167,6 +183,9 @@ void set_weights(moe::FfnProblem& p, const Weights& w, bool a) {
   (a ? p.sgate_a : p.sgate_b) = w.sgate;
   (a ? p.sup_a : p.sup_b) = w.sup;
   (a ? p.sdown_a : p.sdown_b) = w.sdown;
+  (a ? p.xgate_a : p.xgate_b) = w.xgate;
+  (a ? p.xup_a : p.xup_b) = w.xup;
+  (a ? p.xdown_a : p.xdown_b) = w.xdown;
 }
 
 int expert_ffn_impl(const moe_shape* s, int32_t n_groups, int32_t rows_max, const uint16_t* x,
@@ -229,6 +248,30 @@ A8Ws a8_ws(const moe_shape& s) {
   return w;
 }
 
+// The MX workspace: the layer's own layout, then the block-quantised activations with their
+// scale planes (one dword of 4 E8M0 bytes per GEMM row and 128-element K-tile; kTiledRows spare
+// rows so that a row tile's scale load never leaves the plane).
+struct MxWs {
+  moe_layer_mx_ws_layout pub;
+};
+MxWs mx_ws(const moe_shape& s) {
+  MxWs w{};
+  const size_t rows = static_cast<size_t>(s.T) * s.K + (s.n_shared ? s.T : 0);
+  size_t o = layer_ws(s).pub.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  w.pub.scale_rows = rows + moe::kTiledRows;
+  w.pub.xq = take(static_cast<size_t>(s.T) * s.H);
+  w.pub.x_scale = take(static_cast<size_t>(s.H / 128) * w.pub.scale_rows * 4);
+  w.pub.hq = take(rows * s.I);
+  w.pub.h_scale = take(static_cast<size_t>(s.I / 128) * w.pub.scale_rows * 4);
+  w.pub.total = o;
+  return w;
+}
+
 int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, const float* bias,
                const Weights& routed, const Weights& shared_w, uint16_t* out, void* ws,
                size_t ws_bytes, hipStream_t stream, hipEvent_t const* ev, bool a8 = false,
@@ -245,7 +288,11 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
   if (reinterpret_cast<uintptr_t>(out) & 15u) return MOE_ERR_INVALID_ARG;
   const LayerWs w = layer_ws(*s);
   const A8Ws wa = a8_ws(*s);
-  if (ws_bytes < (a8 ? wa.pub.total : w.pub.total) || !aligned(ws)) return MOE_ERR_WORKSPACE;
+  const MxWs wm = mx_ws(*s);
+  const bool mx = routed.mx;
+  if (mx != shared_w.mx && shared) return MOE_ERR_INVALID_ARG;
+  const size_t need = mx ? wm.pub.total : a8 ? wa.pub.total : w.pub.total;
+  if (ws_bytes < need || !aligned(ws)) return MOE_ERR_WORKSPACE;
 
   float* logits = reinterpret_cast<float*>(at(ws, w.pub.logits));
   float* topk_w = reinterpret_cast<float*>(at(ws, w.pub.topk_w));
@@ -297,7 +344,15 @@ int layer_impl(const moe_shape* s, const uint16_t* x, const uint16_t* w_router, 
   p.y = y;
   p.tiles = reinterpret_cast<int32_t*>(at(ws, w.tiles));
   p.gu = gu;
-  if (a8) {
+  if (mx) {
+    p.a8 = p.mx = true;
+    p.xq = reinterpret_cast<uint8_t*>(at(ws, wm.pub.xq));
+    p.xs = reinterpret_cast<uint8_t*>(at(ws, wm.pub.x_scale));
+    p.hq = reinterpret_cast<uint8_t*>(at(ws, wm.pub.hq));
+    p.hs = reinterpret_cast<uint8_t*>(at(ws, wm.pub.h_scale));
+    p.mx_rows = static_cast<int32_t>(wm.pub.scale_rows);
+    p.s2r = s2r;
+  } else if (a8) {
     p.a8 = true;
     p.xq = reinterpret_cast<uint8_t*>(at(ws, wa.pub.xq));
     p.sx = reinterpret_cast<float*>(at(ws, wa.pub.x_scale));
@@ -594,6 +649,43 @@ int moe_layer_forward_w8a8(const moe_shape* s, const uint16_t* x, const uint16_t
                     Weights::fp8(w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale),
                     Weights::fp8(s_gate, s_gate_scale, s_up, s_up_scale, s_down, s_down_scale),
                     out, ws, ws_bytes, stream, ev, true);
+}
+
+size_t moe_layer_mx_workspace_size(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  return mx_ws(*s).pub.total;
+}
+
+int moe_layer_mx_workspace_layout(const moe_shape* s, moe_layer_mx_ws_layout* layout) {
+  const int rc = check_shape(s);
+  if (rc != MOE_OK) return rc;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  *layout = mx_ws(*s).pub;
+  return MOE_OK;
+}
+
+int moe_layer_forward_mx(const moe_shape* s, const uint16_t* x, const uint16_t* w_router,
+                         const float* bias, const uint8_t* w_gate, const uint8_t* w_gate_scale,
+                         const uint8_t* w_up, const uint8_t* w_up_scale, const uint8_t* w_down,
+                         const uint8_t* w_down_scale, const uint8_t* s_gate,
+                         const uint8_t* s_gate_scale, const uint8_t* s_up,
+                         const uint8_t* s_up_scale, const uint8_t* s_down,
+                         const uint8_t* s_down_scale, uint16_t* out, void* ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t const* ev) {
+  return layer_impl(s, x, w_router, bias,
+                    Weights::mxfp8(w_gate, w_gate_scale, w_up, w_up_scale, w_down, w_down_scale),
+                    Weights::mxfp8(s_gate, s_gate_scale, s_up, s_up_scale, s_down, s_down_scale),
+                    out, ws, ws_bytes, stream, ev, true);
+}
+
+int moe_quantize_rows_mx(const uint16_t* x, int32_t rows, int32_t cols, uint8_t* codes,
+                         uint8_t* scales, hipStream_t stream) {
+  if (!x || !codes || !scales || rows < 1 || cols < 1 || cols % 128 != 0) return MOE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(x) & 15u) || (reinterpret_cast<uintptr_t>(codes) & 7u) ||
+      (reinterpret_cast<uintptr_t>(scales) & 3u))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_quant_mx(x, rows, cols, nullptr, codes, scales, rows, nullptr, 0, 0,
+                                         stream));
 }
 
 namespace {

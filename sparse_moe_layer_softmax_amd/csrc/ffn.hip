@@ -123,7 +123,11 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   // gate/up + clamped SwiGLU -> h. W8A8: x quantised per row first; the tiled kernel then
   // moves the codes as pairs (Kd = H / 2), the skinny kernel reads them as bytes.
   hipError_t e = hipSuccess;
-  if (q.a8) {
+  if (q.mx) {
+    e = launch_quant_mx(q.x, q.T, q.H, nullptr, q.xq, q.xs, q.mx_rows, q.s2r, q.topk, q.n_ident,
+                        stream);
+    if (e != hipSuccess) return e;
+  } else if (q.a8) {
     e = launch_quant_rows(q.x, q.T, q.H, nullptr, q.xq, q.sx, stream);
     if (e != hipSuccess) return e;
   }
@@ -148,22 +152,35 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
     p.W1a = reinterpret_cast<const uint16_t*>(q.qup_a);
     p.W1b = reinterpret_cast<const uint16_t*>(q.qup_b);
   }
+  if (q.mx) {
+    p.X0a = q.xgate_a;
+    p.X0b = q.xgate_b;
+    p.X1a = q.xup_a;
+    p.X1b = q.xup_b;
+    p.a_mx = q.xs;
+    p.a_mx_rows = q.mx_rows;
+  }
   p.out = q.h;
   p.N = q.I;
   p.Kd = q.a8 && tiled ? q.H / 2 : q.H;
   p.gu = q.gu;
   if (q.gu && (q.w8 || q.a8)) return hipErrorInvalidValue;
   if (tiled)
-    e = launch_tiled(q.a8 ? kEpiSwiglu88 : (q.w8 ? kEpiSwiglu8 : (q.gu ? kEpiSwigluSave : kEpiSwiglu)),
+    e = launch_tiled(q.mx ? kEpiSwigluMx
+                          : q.a8 ? kEpiSwiglu88 : (q.w8 ? kEpiSwiglu8 : (q.gu ? kEpiSwigluSave : kEpiSwiglu)),
                      p, max_tiles, stream);
   else
-    e = launch_skinny(true, q.w8, q.a8, p, max_tiles, bm, stream);
+    e = launch_skinny(true, q.w8, q.a8, p, max_tiles, bm, stream, q.mx);
   if (e != hipSuccess) return e;
   mark(1);
 
   // down -> y (h rows are already in row order: identity gather); W8A8: the valid h rows
   // (offsets[G] of them) quantised per row first
-  if (q.a8) {
+  if (q.mx) {
+    e = launch_quant_mx(q.h, q.rows_max, q.I, q.offsets + q.n_groups, q.hq, q.hs, q.mx_rows,
+                        nullptr, 0, 0, stream);
+    if (e != hipSuccess) return e;
+  } else if (q.a8) {
     e = launch_quant_rows(q.h, q.rows_max, q.I, q.offsets + q.n_groups, q.hq, q.sh, stream);
     if (e != hipSuccess) return e;
   }
@@ -185,13 +202,20 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
     p.W0a = reinterpret_cast<const uint16_t*>(q.qdown_a);
     p.W0b = reinterpret_cast<const uint16_t*>(q.qdown_b);
   }
+  if (q.mx) {
+    p.X0a = q.xdown_a;
+    p.X0b = q.xdown_b;
+    p.X1a = p.X1b = nullptr;
+    p.a_mx = q.hs;
+  }
   p.out = q.y;
   p.N = q.H;
   p.Kd = q.a8 && tiled ? q.I / 2 : q.I;
   if (tiled)
-    e = launch_tiled(q.a8 ? kEpiBf16_88 : (q.w8 ? kEpiBf16_8 : kEpiBf16), p, max_tiles, stream);
+    e = launch_tiled(q.mx ? kEpiBf16Mx : q.a8 ? kEpiBf16_88 : (q.w8 ? kEpiBf16_8 : kEpiBf16), p,
+                     max_tiles, stream);
   else
-    e = launch_skinny(false, q.w8, q.a8, p, max_tiles, bm, stream);
+    e = launch_skinny(false, q.w8, q.a8, p, max_tiles, bm, stream, q.mx);
   if (e != hipSuccess) return e;
   mark(2);
   return hipGetLastError();

@@ -52,6 +52,15 @@ struct GroupedParams {
   int32_t k_w0;
   // kEpiSwigluSave: [rows, 2N] fp32, the gate sums in columns [0, N) and the up sums in [N, 2N)
   float* gu;
+  // MX block scales (kEpiSwigluMx / kEpiBf16Mx and the skinny kernel's MX form), one E8M0 byte
+  // per 32 codes along K. Weights: like Q*, one [K/128][N][4] array per matrix (K in codes), the
+  // *b arrays stacked per group. Activations: planes [K/128][a_mx_rows][4] indexed by GEMM row.
+  const uint8_t* X0a;
+  const uint8_t* X0b;
+  const uint8_t* X1a;
+  const uint8_t* X1b;
+  const uint8_t* a_mx;
+  int32_t a_mx_rows;
 };
 
 
@@ -64,8 +73,9 @@ constexpr int kSkinnyRowsSmall = 16;
 // gated: gate/up + SwiGLU over N = I columns (64 per workgroup); else down (128 per workgroup).
 // w8: the weights are the FP8 Q*/S* operands. a8 (with w8): A holds E4M3 codes [rows, Kd] with
 // one fp32 scale per row in a_scale.
+// mx (with a8): MX block scales (X*, a_mx) in place of the per-row ones.
 hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
-                         int tile_rows, hipStream_t stream);
+                         int tile_rows, hipStream_t stream, bool mx = false);
 
 // LDS-tiled MFMA kernel for many rows per group (ffn_tiled.hip): row tiles of kTiledRows.
 constexpr int kTiledRows = 320;
@@ -82,9 +92,12 @@ constexpr int kTiledRows = 320;
 // in LDS as it lies in memory and the MFMA operands are read from it with the LDS transpose read.
 // kEpiSwigluSave: kEpiSwiglu that also stores the fp32 gate and up sums (gu), which the
 // backward pass then reads instead of recomputing them.
+// kEpiSwigluMx / kEpiBf16Mx: the W8A8 forms with MX block scales (X*, a_mx) in place of the
+// per-row ones: each MFMA applies the E8M0 scales of its 32-code blocks, so the fp32 sums need
+// no scale in the epilogue.
 enum Epilogue { kEpiSwiglu = 0, kEpiBf16 = 1, kEpiF32 = 2, kEpiSwigluBwd = 3, kEpiSwiglu8 = 4,
                 kEpiBf16_8 = 5, kEpiSwiglu88 = 6, kEpiBf16_88 = 7, kEpiBf16T = 8,
-                kEpiSwigluSave = 9 };
+                kEpiSwigluSave = 9, kEpiSwigluMx = 10, kEpiBf16Mx = 11 };
 hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hipStream_t stream);
 
 }  // namespace moe

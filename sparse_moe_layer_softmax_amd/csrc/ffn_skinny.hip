@@ -59,10 +59,11 @@ __device__ __forceinline__ void exchange_line(const LineRaw& w, u32x4_t& f0, u32
   }
 }
 
-template <bool GATED, int NS, bool W8, bool A8>
+template <bool GATED, int NS, bool W8, bool A8, bool MX = false>
 __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r0, int r1,
                                             int col0) {
   static_assert(!A8 || W8, "FP8 activations come with FP8 weights");
+  static_assert(!MX || A8, "MX block scales come with FP8 activations");
   const int lane = threadIdx.x & 63;
   const int lr = lane & 15;
   const int lk = W8 ? (lane >> 4) * 16 : (lane >> 4) * 8;  // this lane's first K element
@@ -128,6 +129,20 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
   const uint8_t* w0 = M0 + static_cast<size_t>(col0 + lo8) * rowb + cb;
   const uint8_t* w1 = M1 + static_cast<size_t>(GATED ? col0 + lo8 : col0 + 16 + lo8) * rowb + cb;
   const size_t hoff = 8 * rowb;
+  // MX: this lane's weight-scale dwords (4 E8M0 bytes per 128-code K-tile) of its gate (or down
+  // column col0 + lr) row and its up (or down column col0 + 16 + lr) row, planes of N dwords
+  const uint32_t* xs0 = nullptr;
+  const uint32_t* xs1 = nullptr;
+  if constexpr (MX) {
+    const size_t xst = static_cast<size_t>(Kd / 128) * p.N;  // dwords per matrix
+    const uint32_t* X0 = reinterpret_cast<const uint32_t*>(g < p.g_split ? p.X0a : p.X0b) +
+                         (g < p.g_split ? g : g - p.g_split) * xst;
+    const uint32_t* X1 = GATED ? reinterpret_cast<const uint32_t*>(g < p.g_split ? p.X1a : p.X1b) +
+                                     (g < p.g_split ? g : g - p.g_split) * xst
+                               : X0;
+    xs0 = X0 + col0 + lr;
+    xs1 = X1 + (GATED ? col0 + lr : col0 + 16 + lr);
+  }
 
   f32x4_t acc0[NS], acc1[NS];
 #pragma unroll
@@ -148,6 +163,11 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
     r0w[ln] = load_line(w0 + 128 * ln, hoff);
     r1w[ln] = load_line(w1 + 128 * ln, hoff);
   }
+  uint32_t c0s = 0, c1s = 0;  // MX: the current K-tile's weight-scale dwords
+  if constexpr (MX) {
+    c0s = xs0[0];
+    c1s = xs1[0];
+  }
   for (int k = 0; k < Kd; k += 128) {
     const size_t kb = W8 ? static_cast<size_t>(k) : 2 * static_cast<size_t>(k);
     const size_t kn = k + 128 < Kd ? kb + KB : kb;
@@ -157,10 +177,31 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
       n0w[ln] = load_line(w0 + kn + 128 * ln, hoff);
       n1w[ln] = load_line(w1 + kn + 128 * ln, hoff);
     }
+    uint32_t n0s = 0, n1s = 0;  // MX: the next K-tile's weight-scale dwords
+    if constexpr (MX) {
+      const size_t kt1 = static_cast<size_t>(k + 128 < Kd ? k / 128 + 1 : k / 128) * p.N;
+      n0s = xs0[kt1];
+      n1s = xs1[kt1];
+    }
+    // MX: chunk G of a row is block G / 2 of the K-tile, chunk G + 4 block 2 + G / 2
+    const int gb = (lane >> 4) >> 1;
     // activations at the same K elements as the weight operands of MFMA u; rows past the tile
     // read a valid row and are masked to zero, so the loads need no branch
     u32x4_t aa[NS][U];
-    if (A8) {  // 16 codes per load: elements 16g + 64c + [0, 16) feed MFMAs 2c and 2c + 1
+    if (MX) {  // as A8, each 16-code chunk decoded with its block's scale byte
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int r = av[s] ? r0 + 16 * s + lr : r0;
+        const uint32_t sd = reinterpret_cast<const uint32_t*>(p.a_mx)[static_cast<size_t>(k / 128) * p.a_mx_rows + r];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4_t t = *reinterpret_cast<const u32x4_t*>(ap8[s] + k + 64 * c);
+          const uint32_t sb = sd >> (8 * (gb + 2 * c));
+          aa[s][2 * c] = e4m3x8_to_bf16_mx(t[0], t[1], sb) & am[s];
+          aa[s][2 * c + 1] = e4m3x8_to_bf16_mx(t[2], t[3], sb) & am[s];
+        }
+      }
+    } else if (A8) {  // 16 codes per load: elements 16g + 64c + [0, 16) feed MFMAs 2c and 2c + 1
 #pragma unroll
       for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -190,7 +231,13 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
     u32x4_t bb0[U], bb1[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (W8) {  // MFMA u takes codes 8(u%2)..+8 of chunk half u/2
+      if (MX) {  // chunk half u/2 is block gb + 2 (u/2) of the K-tile
+        const u32x4_t& c = f0[u >> 1];
+        const u32x4_t& d = f1[u >> 1];
+        const int sh = 8 * (gb + 2 * (u >> 1));
+        bb0[u] = e4m3x8_to_bf16_mx(c[2 * (u & 1)], c[2 * (u & 1) + 1], c0s >> sh);
+        bb1[u] = e4m3x8_to_bf16_mx(d[2 * (u & 1)], d[2 * (u & 1) + 1], c1s >> sh);
+      } else if (W8) {  // MFMA u takes codes 8(u%2)..+8 of chunk half u/2
         const u32x4_t& c = f0[u >> 1];
         const u32x4_t& d = f1[u >> 1];
         bb0[u] = e4m3x8_to_bf16(c[2 * (u & 1)], c[2 * (u & 1) + 1]);
@@ -207,11 +254,15 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
         acc0[s] = mfma16x16x32(aa[s][u], bb0[u], acc0[s]);
         acc1[s] = mfma16x16x32(aa[s][u], bb1[u], acc1[s]);
       }
+    if constexpr (MX) {
+      c0s = n0s;
+      c1s = n1s;
+    }
   }
 
   // FP8: per-row weight scales of this lane's two output columns
   float sc0 = 1.f, sc1 = 1.f;
-  if (W8) {
+  if (W8 && !MX) {
     const size_t so = static_cast<size_t>(g < p.g_split ? g : g - p.g_split) * p.N;
     const float* S0 = (g < p.g_split ? p.S0a : p.S0b) + so;
     const float* S1 = S0;
@@ -228,7 +279,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
         uint16_t* o = p.out + static_cast<size_t>(r) * p.N;
         float a0 = W8 ? acc0[s][v] * sc0 : acc0[s][v];
         float a1 = W8 ? acc1[s][v] * sc1 : acc1[s][v];
-        if (A8) {  // the activation row's scale (rows of the tile hold their own source row)
+        if (A8 && !MX) {  // the activation row's scale (rows of the tile hold their own source row)
           const int sr = source(r);
           const float sa = sr >= 0 ? p.a_scale[sr] : 0.f;
           a0 *= sa;
@@ -247,7 +298,7 @@ __device__ __forceinline__ void skinny_tile(const GroupedParams& p, int g, int r
 // MAXNS: the most 16-row sub-blocks a tile may hold (the tile table's row tile is 16 * MAXNS).
 // The register count follows the largest sub-block count compiled in, so a table of 16-row tiles
 // with MAXNS = 1 runs at several times the occupancy of the 64-row form.
-template <bool GATED, bool W8, bool A8 = false, int MAXNS = 4>
+template <bool GATED, bool W8, bool A8 = false, int MAXNS = 4, bool MX = false>
 __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
   const int tile = blockIdx.x;
   if (tile >= p.tiles[0]) return;
@@ -258,10 +309,10 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
   const int wave = threadIdx.x >> 6;
   const int col0 = GATED ? blockIdx.y * 64 + wave * 16 : blockIdx.y * 128 + wave * 32;
   switch ((r1 - r0 + 15) >> 4) {
-    case 1: skinny_tile<GATED, 1, W8, A8>(p, g, r0, r1, col0); break;
-    case 2: if constexpr (MAXNS >= 2) skinny_tile<GATED, 2, W8, A8>(p, g, r0, r1, col0); break;
-    case 3: if constexpr (MAXNS >= 3) skinny_tile<GATED, 3, W8, A8>(p, g, r0, r1, col0); break;
-    case 4: if constexpr (MAXNS >= 4) skinny_tile<GATED, 4, W8, A8>(p, g, r0, r1, col0); break;
+    case 1: skinny_tile<GATED, 1, W8, A8, MX>(p, g, r0, r1, col0); break;
+    case 2: if constexpr (MAXNS >= 2) skinny_tile<GATED, 2, W8, A8, MX>(p, g, r0, r1, col0); break;
+    case 3: if constexpr (MAXNS >= 3) skinny_tile<GATED, 3, W8, A8, MX>(p, g, r0, r1, col0); break;
+    case 4: if constexpr (MAXNS >= 4) skinny_tile<GATED, 4, W8, A8, MX>(p, g, r0, r1, col0); break;
     default: break;
   }
 }
@@ -270,9 +321,13 @@ __global__ __launch_bounds__(256) void ffn_skinny_kernel(GroupedParams p) {
 }  // namespace
 
 template <int MAXNS>
-static void skinny_dispatch(bool gated, bool w8, bool a8, const GroupedParams& p, dim3 grid,
+static void skinny_dispatch(bool gated, bool w8, bool a8, bool mx, const GroupedParams& p, dim3 grid,
                             hipStream_t stream) {
-  if (a8 && gated)
+  if (mx && gated)
+    hipLaunchKernelGGL((ffn_skinny_kernel<true, true, true, MAXNS, true>), grid, dim3(256), 0, stream, p);
+  else if (mx)
+    hipLaunchKernelGGL((ffn_skinny_kernel<false, true, true, MAXNS, true>), grid, dim3(256), 0, stream, p);
+  else if (a8 && gated)
     hipLaunchKernelGGL((ffn_skinny_kernel<true, true, true, MAXNS>), grid, dim3(256), 0, stream, p);
   else if (a8)
     hipLaunchKernelGGL((ffn_skinny_kernel<false, true, true, MAXNS>), grid, dim3(256), 0, stream, p);
@@ -287,12 +342,12 @@ static void skinny_dispatch(bool gated, bool w8, bool a8, const GroupedParams& p
 }
 
 hipError_t launch_skinny(bool gated, bool w8, bool a8, const GroupedParams& p, int max_tiles,
-                         int tile_rows, hipStream_t stream) {
+                         int tile_rows, hipStream_t stream, bool mx) {
   const dim3 grid(max_tiles, gated ? p.N / 64 : p.N / 128);
   if (tile_rows == 16)
-    skinny_dispatch<1>(gated, w8, a8, p, grid, stream);
+    skinny_dispatch<1>(gated, w8, a8, mx, p, grid, stream);
   else
-    skinny_dispatch<4>(gated, w8, a8, p, grid, stream);
+    skinny_dispatch<4>(gated, w8, a8, mx, p, grid, stream);
   return hipGetLastError();
 }
 

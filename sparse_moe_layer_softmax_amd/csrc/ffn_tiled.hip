@@ -64,7 +64,10 @@ constexpr int kStageA = kBM * kBK, kStageB = kTN * kBK;  // bf16 elements per st
 constexpr int kStageB8 = kTN * kBK;                      // bytes per FP8 weight stage
 constexpr int kStagesB8 = 3;  // FP8 weight stages: K-tile kt+2 is fetched during K-tile kt
 constexpr size_t kSmemRing = sizeof(uint16_t) * kStages * (kStageA + kStageB);
-constexpr size_t kSmem = kSmemRing + sizeof(float) * kBM;  // + W8A8 row scales of the tile
+// MX scale stages: per K-tile one dword (4 E8M0 bytes) per tile row and per weight row
+constexpr int kScaleStage = kBM + kTN;
+// after the ring: the W8A8 row scales of the tile, or the two MX scale stages
+constexpr size_t kSmem = kSmemRing + sizeof(uint32_t) * (2 * kScaleStage > kBM ? 2 * kScaleStage : kBM);
 constexpr int kDmaB = kTN / 8 / 8;  // weight-tile DMA instructions per wavefront per K-tile
 
 // LDS element offset of (row, k) in a [rows][64] bf16 stage. The eight 16-byte chunks of a row
@@ -156,10 +159,11 @@ template <int EPI, int MIV, bool BUF>
 __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1,
                                            int kb, int nk, int split) {
   constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;     // FP8 weights, bf16 activations
-  constexpr bool A8 = EPI == kEpiSwiglu88 || EPI == kEpiBf16_88;  // FP8 weights and activations
+  constexpr bool MX = EPI == kEpiSwigluMx || EPI == kEpiBf16Mx;     // ... with MX block scales
+  constexpr bool A8 = EPI == kEpiSwiglu88 || EPI == kEpiBf16_88 || MX;  // FP8 weights and activations
   constexpr bool BT = EPI == kEpiBf16T;  // weights [Kd][N], read with the LDS transpose read
   constexpr bool GATED = EPI == kEpiSwiglu || EPI == kEpiSwigluBwd || EPI == kEpiSwiglu8 ||
-                         EPI == kEpiSwiglu88 || EPI == kEpiSwigluSave;
+                         EPI == kEpiSwiglu88 || EPI == kEpiSwigluSave || EPI == kEpiSwigluMx;
   constexpr int MV = MIV > 0 ? MIV : 1;  // array extent
   // DMA instructions of this wavefront that may still be in flight when a K-tile's operands
   // must have landed: FP8 weight tiles run one K-tile further ahead (the next-but-one tile's)
@@ -174,7 +178,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = wave >> 2;    // rows 160*half .. +160 of the tile; also the ping-pong group
   const int quarter = wave & 3;  // weight rows 64*quarter .. +64 of the tile
-  if constexpr (A8) {  // the activation-row scale of every tile row (0 past the group's end)
+  if constexpr (A8 && !MX) {  // the activation-row scale of every tile row (0 past the group's end)
     float* srow = reinterpret_cast<float*>(smem + kSmemRing / sizeof(uint16_t));
     if (tid < kBM) {
       const int r = r0 + tid;
@@ -326,6 +330,37 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     }
   };
 
+  // MX: the K-tile's scale dwords into scale stage `stage` (after the ring): tile rows (wavefront
+  // 0: rows 0-255, wavefront 1: rows 256-319, 16 lanes) and weight rows (wavefront 2; gate/up:
+  // gate rows in lanes 0-31, up rows in lanes 32-63). Each lane moves the dwords of 4 rows.
+  uint32_t* sS = reinterpret_cast<uint32_t*>(smem + kSmemRing / sizeof(uint16_t));
+  const uint8_t* Xg = nullptr;
+  const uint8_t* Xu = nullptr;
+  if constexpr (MX) {
+    const size_t xst = static_cast<size_t>(Kd / kBK) * p.N * sizeof(uint32_t);  // bytes per matrix
+    Xg = g < p.g_split ? p.X0a + g * xst : p.X0b + (g - p.g_split) * xst;
+    Xu = GATED ? (g < p.g_split ? p.X1a + g * xst : p.X1b + (g - p.g_split) * xst) : Xg;
+  }
+  auto dma_s = [&](int kt, int stage) {
+    if constexpr (MX) {
+      const size_t kk = static_cast<size_t>(kb + kt);
+      uint32_t* dst = sS + stage * kScaleStage;
+      if (wave == 0 || (wave == 1 && lane < (kBM - 256) / 4)) {
+        const uint8_t* src = p.a_mx + ((kk * p.a_mx_rows + r0 + 256 * wave) * 4 + lane * 16);
+        lds_dma16(reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst + 256 * wave));
+      } else if (wave == 2) {
+        const size_t plane = kk * p.N;
+        const uint8_t* src = GATED ? (lane < 32 ? Xg : Xu) + (plane + nb * 128 + (lane & 31) * 4) * 4
+                                   : Xg + (plane + nb * kTN + lane * 4) * 4;
+        lds_dma16(reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst + kBM));
+      }
+    }
+  };
+  // MX: this K-tile's scale dwords of the lane's A rows and weight rows, shifted so that byte 0
+  // holds the scale the lane supplies in the current slice h: lane half q gives the scale of the
+  // slice's block q, block 2h + q of the K-tile
+  uint32_t dsa[MV], dsb[2];
+
   f32x16_t acc[MV][2];
 #pragma unroll
   for (int i = 0; i < MV; ++i)
@@ -373,6 +408,9 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       // h is not a compile-time constant here (the slice loop is not unrolled): the two offsets
       // (those of K-steps 2h and 2h + 1) are computed, not looked up in lds_off, whose dynamic
       // indexing would put it in scratch memory and which would hold four more registers
+      // lane half q: bytes 0-15 = codes 64h + 16q + [0, 16), bytes 16-31 = codes 64h + 32 + 16q +
+      // [0, 16); the MFMA's first 32-code block is bytes 0-15 of both halves, its second bytes
+      // 16-31 (the layout of its MX block scales)
       const int o0 = swz(fr, 32 * h + fk), o1 = swz(fr, 32 * h + 16 + fk);
 #pragma unroll
       for (int i = 0; i < MIV; ++i) {
@@ -432,6 +470,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   if (nk > 0) {
     dma_a(0, 0);
     dma_b(0, 0);
+    dma_s(0, 0);
     if (W8) dma_b(min(1, nk - 1), 1);
     wait_vmcnt<kLead>();
     barrier_no_fence();
@@ -440,18 +479,40 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
     auto phase = [&](int kt, int h) {
       // ---- memory phase
       if (MIV > 0) fetch(kt & 1, W8 ? kt % kStagesB8 : kt & 1, h);
+      if (MX && MIV > 0) {  // the K-tile's scale dwords, read with the slice-0 fragments
+        if (h == 0) {
+          const uint32_t* ss = sS + (kt & 1) * kScaleStage;
+#pragma unroll
+          for (int i = 0; i < MIV; ++i) dsa[i] = ss[half * 160 + i * 32 + fr];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dsb[j] = ss[kBM + (GATED ? j * 128 + quarter * 32 + fr : quarter * 64 + j * 32 + fr)];
+        }
+      }
       if (h == 0) {
+        dma_s(min(kt + 1, nk - 1), (kt + 1) & 1);
         dma_a(min(kt + 1, nk - 1), (kt + 1) & 1);
         if (W8) dma_b(min(kt + 2, nk - 1), (kt + 2) % kStagesB8);
         else dma_b(min(kt + 1, nk - 1), (kt + 1) & 1);
       }
       if (half == 1 && h == 1) wait_vmcnt<kLead>();
       wait_lgkmcnt0();
+      if (MX && MIV > 0) {  // byte 0 <- the scale of block 2h + (lane half) of the K-tile
+        const int sh = h == 0 ? 8 * (lane >> 5) : 16;
+#pragma unroll
+        for (int i = 0; i < MIV; ++i) dsa[i] >>= sh;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dsb[j] >>= sh;
+      }
       barrier_no_fence();
       // ---- compute phase
       if (MIV > 0) {
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (A8) {  // one FP8 MFMA covers the slice's 64 codes
+        if constexpr (MX) {  // one scaled FP8 MFMA covers the slice's two blocks
+#pragma unroll
+          for (int i = 0; i < MIV; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x64_fp8_mx(af8[i], bf8[j], acc[i][j], dsa[i], dsb[j]);
+        } else if constexpr (A8) {  // one FP8 MFMA covers the slice's 64 codes
 #pragma unroll
           for (int i = 0; i < MIV; ++i)
 #pragma unroll
@@ -484,7 +545,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
 
   // ---- epilogue: lane holds rows 8*(v/4) + 4*(lane/32) + v%4 of each 32x32 block, column lane%32
   const int rbase = r0 + half * 160;
-  if (W8 || A8) {  // per-row weight scales of this lane's two columns multiply the fp32 sums
+  if (W8 || (A8 && !MX)) {  // per-row weight scales of this lane's two columns multiply the fp32 sums
     const size_t so = static_cast<size_t>(g < p.g_split ? g : g - p.g_split) * p.N;
     const float* S0 = (g < p.g_split ? p.S0a : p.S0b) + so;
     const float* S1 = GATED ? (g < p.g_split ? p.S1a : p.S1b) + so : S0;
@@ -574,7 +635,7 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
   auto eoff = [&](int row, int col) { return row * C + ((((col >> 3) ^ row) & (CH - 1)) << 3) + (col & 7); };
 #pragma unroll
   for (int i = 0; i < MIV; ++i) {
-    if constexpr (A8) {  // the scale of each output row's activation row (staged in LDS)
+    if constexpr (A8 && !MX) {  // the scale of each output row's activation row (staged in LDS)
       const float* srow = reinterpret_cast<const float*>(smem + kSmemRing / sizeof(uint16_t));
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -761,6 +822,8 @@ hipError_t launch_tiled(Epilogue epi, const GroupedParams& p, int max_tiles, hip
     case kEpiBf16_8: return tiled_launch<kEpiBf16_8>(p, p.N / kTN, max_tiles, stream);
     case kEpiSwiglu88: return tiled_launch<kEpiSwiglu88>(p, p.N / 128, max_tiles, stream);
     case kEpiBf16_88: return tiled_launch<kEpiBf16_88>(p, p.N / kTN, max_tiles, stream);
+    case kEpiSwigluMx: return tiled_launch<kEpiSwigluMx>(p, p.N / 128, max_tiles, stream);
+    case kEpiBf16Mx: return tiled_launch<kEpiBf16Mx>(p, p.N / kTN, max_tiles, stream);
     case kEpiBf16: return tiled_launch<kEpiBf16>(p, p.N / kTN, max_tiles, stream);
     case kEpiBf16T: return tiled_launch<kEpiBf16T>(p, p.N / kTN, max_tiles, stream);
     default: return tiled_launch<kEpiF32>(p, p.N / kTN, max_tiles, stream);

@@ -73,6 +73,18 @@ __device__ __forceinline__ f32x16_t mfma32x32x64_fp8(u32x8_t a, u32x8_t b, f32x1
                                                          0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
 }
 
+// The same product with MX block scales. The instruction's first 32-code block of row r (of A;
+// column r of B) is bytes 0-15 of lanes r and r + 32, its second block bytes 16-31 of both; lane
+// r supplies the first block's E8M0 byte and lane r + 32 the second's, in bits 7:0 of sa (A) and
+// sb (B). A probe on the GPU fixed this layout (one-hot codes against distinct per-lane scales).
+__device__ __forceinline__ f32x16_t mfma32x32x64_fp8_mx(u32x8_t a, u32x8_t b, f32x16_t c, uint32_t sa,
+                                                       uint32_t sb) {
+  typedef int i32x8_t __attribute__((ext_vector_type(8)));
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(__builtin_bit_cast(i32x8_t, a),
+                                                         __builtin_bit_cast(i32x8_t, b), c, 0, 0, 0,
+                                                         static_cast<int>(sa), 0, static_cast<int>(sb));
+}
+
 // Eight OCP E4M3 codes (two dwords, code 0 in the low byte) -> the eight bf16 of one MFMA
 // operand. Exact: every E4M3 value is a bf16 value (the gfx950 scaled convert, scale 1).
 __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -81,6 +93,19 @@ __device__ __forceinline__ u32x4_t e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
   r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  return r;
+}
+
+// The same with an MX block scale: the eight bf16 of e4m3(code) * 2^(s - 127) for the E8M0 byte
+// s, exact while the product stays within bf16's normal range (s from 10 to 245 for any code).
+__device__ __forceinline__ u32x4_t e4m3x8_to_bf16_mx(uint32_t lo, uint32_t hi, uint32_t s) {
+  const uint32_t b = s & 0xFFu;
+  const float sc = __uint_as_float(b ? b << 23 : 0x00400000u);  // 2^(b - 127)
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, sc, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, sc, true));
   return r;
 }
 

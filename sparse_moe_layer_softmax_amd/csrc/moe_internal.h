@@ -79,6 +79,17 @@ struct FfnProblem {
   float* sx;
   uint8_t* hq;
   float* sh;
+  // MX block scales (mx, with w8 and a8): the weights' E8M0 bytes in place of the fp32 row
+  // scales, one [K/128][N][4] array per matrix (xgate_* etc., stacked per group as the codes);
+  // x and h quantised per 32-element block into xq / hq with their scale planes xs
+  // ([H/128][mx_rows][4]) and hs ([I/128][mx_rows][4]) indexed by GEMM row, mx_rows at least
+  // rows_max + kTiledRows. s2r: slot_to_row, which places the x scales of a token's slots.
+  bool mx;
+  const uint8_t *xgate_a, *xgate_b, *xup_a, *xup_b, *xdown_a, *xdown_b;
+  uint8_t* xs;
+  uint8_t* hs;
+  int32_t mx_rows;
+  const int32_t* s2r;
   // bf16 weights only: when set, the gate/up projection also stores its fp32 gate and up sums,
   // [rows_max, 2I] (gate in columns [0, I), up in [I, 2I)), and both projections take the tiled
   // kernel, whatever the rows per group, so that the sums are the ones the backward's recompute
@@ -93,6 +104,13 @@ hipError_t launch_ffn(const FfnProblem& p, hipStream_t stream, hipEvent_t const*
 // past *rows_dev (when given) are left untouched. cols a multiple of 8.
 hipError_t launch_quant_rows(const uint16_t* v, int rows, int cols, const int32_t* rows_dev,
                              uint8_t* codes, float* scales, hipStream_t stream);
+// MX block quantisation (quant.hip): codes [rows, cols] in source row order; one E8M0 byte per
+// 32 elements, stored as planes [cols / 128][plane_rows][4] indexed by GEMM row: source row r
+// itself (s2r NULL), or for tokens: row t when n_ident > 0 and n_ident + s2r[t*K + k] for each
+// kept slot. cols a multiple of 128; rows at or past *rows_dev (when given) are skipped.
+hipError_t launch_quant_mx(const uint16_t* v, int rows, int cols, const int32_t* rows_dev,
+                           uint8_t* codes, uint8_t* scales, int plane_rows, const int32_t* s2r,
+                           int K, int n_ident, hipStream_t stream);
 
 // Dense C[rows, N] (fp32) = A[rows, Kd] . W[N, Kd]^T on the tiled MFMA kernel (router logits
 // at large T). Supported when N == 256 and Kd % 64 == 0. The reduction is split into

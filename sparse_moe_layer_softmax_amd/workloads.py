@@ -22,6 +22,12 @@ codes with one fp32 scale per row: the row is drawn as above in float32, its sca
 max|w| / 448 (448 being the largest finite E4M3 value), and the codes are torch's round-to-nearest
 conversion of w / scale. This is checkpoint preparation, not part of the layer: the layer only
 ever reads the codes and scales.
+
+MX workloads (``mx=True``, with ``fp8`` and ``act_fp8``) store every expert weight matrix as E4M3
+codes with one power-of-two scale per 32 consecutive elements of a row (E8M0 bytes, bias 127,
+``<name>_mx`` of shape [..., rows, cols / 32]): per block, the smallest power of two 2^e with
+max|w| / 2^e <= 448 (so no code saturates), and codes torch's round-to-nearest conversion of
+w / 2^e. Checkpoint preparation again; the activations' block quantisation is the layer's own.
 """
 from __future__ import annotations
 
@@ -55,6 +61,7 @@ class Workload:
     seed: int = 0
     fp8: bool = False           # expert weights as FP8 E4M3 codes + per-row fp32 scales
     act_fp8: bool = False       # with fp8: expert activations quantised per row to E4M3 (W8A8)
+    mx: bool = False            # with fp8 and act_fp8: MX block scales (32 elements) instead
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -105,6 +112,17 @@ WORKLOADS = {
     "hy4_skew_t65536_w8a8": Workload(
         "hy4_skew_t65536_w8a8", T=65536, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
         w_std=0.006, router_std=0.006, zipf=1.2, seed=10, fp8=True, act_fp8=True),
+    # the FP8 deployment with MX block scales (one power of two per 32 elements, OCP MXFP8) on
+    # weights and activations
+    "hy4_decode_t64_mx": Workload(
+        "hy4_decode_t64_mx", T=64, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, seed=11, fp8=True, act_fp8=True, mx=True),
+    "hy4_prefill_t8192_mx": Workload(
+        "hy4_prefill_t8192_mx", T=8192, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, seed=12, fp8=True, act_fp8=True, mx=True),
+    "hy4_skew_t65536_mx": Workload(
+        "hy4_skew_t65536_mx", T=65536, H=6144, E=256, K=8, I=2048, scale=2.827, limit=10.0,
+        w_std=0.006, router_std=0.006, zipf=1.2, seed=13, fp8=True, act_fp8=True, mx=True),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -136,6 +154,17 @@ def _randn_fp8(shape, std, gen, device):
     return q, scale
 
 
+def _randn_mx(shape, std, gen, device):
+    """(E4M3 codes as uint8, E8M0 scale bytes [rows, cols / 32]) of a float32 N(0, std^2) matrix."""
+    w = torch.randn(*shape, generator=gen, device=device, dtype=torch.float32) * std
+    blk = w.view(*shape[:-1], shape[-1] // 32, 32)
+    amax = blk.abs().amax(dim=-1)
+    e = torch.ceil(torch.log2(torch.clamp(amax, min=2.0 ** -100) / 448.0))
+    e = torch.clamp(e, -127, 127)
+    q = (blk / torch.exp2(e).unsqueeze(-1)).to(torch.float8_e4m3fn).view(torch.uint8).view(*shape)
+    return q, (e + 127).to(torch.uint8)
+
+
 def generate(wl: Workload, device="cpu", shared: bool = True):
     """Return a dict of torch tensors on ``device``:
     x [T,H], w_router [E,H], router_bias [E] fp32 or None, w_gate/w_up [E,I,H], w_down [E,H,I],
@@ -150,7 +179,13 @@ def generate(wl: Workload, device="cpu", shared: bool = True):
     out["router_bias"] = None if b is None else b.to(dev)
     for name, shp in (("w_gate", (wl.I, wl.H)), ("w_up", (wl.I, wl.H)), ("w_down", (wl.H, wl.I))):
         g = _gen(wl, name, dev)
-        if wl.fp8:
+        if wl.mx:
+            w = torch.empty((wl.E,) + shp, dtype=torch.uint8, device=dev)
+            sc = torch.empty((wl.E, shp[0], shp[1] // 32), dtype=torch.uint8, device=dev)
+            for e in range(wl.E):
+                w[e], sc[e] = _randn_mx(shp, wl.w_std, g, dev)
+            out[name + "_mx"] = sc
+        elif wl.fp8:
             w = torch.empty((wl.E,) + shp, dtype=torch.uint8, device=dev)
             sc = torch.empty((wl.E, shp[0]), dtype=torch.float32, device=dev)
             for e in range(wl.E):
@@ -162,16 +197,21 @@ def generate(wl: Workload, device="cpu", shared: bool = True):
                 w[e] = _randn_bf16(shp, wl.w_std, g, dev)
         out[name] = w
     out["act_fp8"] = wl.act_fp8
+    out["mx"] = wl.mx
     for name, shp in (("s_gate", (wl.I, wl.H)), ("s_up", (wl.I, wl.H)), ("s_down", (wl.H, wl.I))):
         if shared and wl.n_shared:
             g = _gen(wl, name, dev)
-            if wl.fp8:
+            if wl.mx:
+                out[name], out[name + "_mx"] = _randn_mx(shp, wl.w_std, g, dev)
+            elif wl.fp8:
                 out[name], out[name + "_scale"] = _randn_fp8(shp, wl.w_std, g, dev)
             else:
                 out[name] = _randn_bf16(shp, wl.w_std, g, dev)
         else:
             out[name] = None
-            if wl.fp8:
+            if wl.mx:
+                out[name + "_mx"] = None
+            elif wl.fp8:
                 out[name + "_scale"] = None
     return out
 

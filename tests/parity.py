@@ -195,6 +195,12 @@ CHAINS = {
     # order). Both then multiply by the weight and row scales.
     "tiled_a8": Chain(64, 1, 64, group=64, guard=-5, scale_mults=2),
     "skinny_a8": Chain(128, 4, 32, scale_mults=2),
+    # MX: the tiled kernel's scaled FP8 MFMA applies the block scales inside the instruction, so
+    # the chain runs on the dequantised values with no scale multiply after it; its precision is
+    # charged as the W8A8 MFMA's (measured). The weight-streaming kernel decodes code * scale to
+    # bf16 exactly and runs the bf16 MFMA (W8 order).
+    "tiled_mx": Chain(64, 1, 64, group=64, guard=-5, scale_mults=0),
+    "skinny_mx": Chain(128, 4, 32, scale_mults=0),
 }
 
 
@@ -204,8 +210,8 @@ def kernel_of(rows_max: int, n_groups: int, train: bool = False) -> str:
     return "tiled" if train or rows_max >= 64 * n_groups else "skinny"
 
 
-def chain_for(kern: str, fp8: bool, act_fp8: bool) -> Chain:
-    return CHAINS[kern + ("_a8" if act_fp8 else "_w8" if fp8 else "")]
+def chain_for(kern: str, fp8: bool, act_fp8: bool, mx: bool = False) -> Chain:
+    return CHAINS[kern + ("_mx" if mx else "_a8" if act_fp8 else "_w8" if fp8 else "")]
 
 
 def _group_max(M, g):
@@ -436,6 +442,34 @@ def check_w8a8_rows(what, xq, sx, w3, limit, chain, h_gpu, hq_gpu, sh_gpu, y_gpu
                    "y", bare=True)
 
 
+def check_mx_rows(what, xq, xs, w3, limit, chain, h_gpu, hq_gpu, hs_gpu, y_gpu, h_orc, hq_orc,
+                  hs_orc, y_orc, stats=None):
+    """check_w8a8_rows for the MX form: xq, xs the rows' x codes and block-scale bytes [n, H/32]
+    (the same on both sides, checked bit for bit first); w3 three oracle.Mx weights; hq/hs the h
+    codes and scale bytes of each side. The projections run on the dequantised values (every
+    product exact), so the sums and their absolute terms are plain float64 matrix products."""
+    deq = oracle.mx_dequant
+    wg, wu, wd = (deq(w.q, w.s) for w in w3)
+    A = deq(xq, xs)
+    Sg, dg, Ag = chain_sums(A, wg, chain)
+    Su, du, Au = chain_sums(A, wu, chain)
+    vh, th = h_reference(Sg, Ag, Su, Au, limit)
+    check_reconstruction(vh, h_orc, what + " h", th)
+    dh = swiglu_bound(fl32(Sg), fl32(Su), dg + U * np.abs(Sg), du + U * np.abs(Su), limit)
+    check_interval(h_gpu, vh, dh, what + " h", h_orc, stats, "h", bare=True)
+    Ag8 = deq(hq_gpu, hs_gpu)
+    Syc, dyc, _ = chain_sums(Ag8, wd, chain)
+    check_interval(y_gpu, Syc, dyc, what + " y (chained)")
+    Ao8 = deq(hq_orc, hs_orc)
+    Syo, _, Ayo = chain_sums(Ao8, wd, chain)
+    vy = fl32(Syo)
+    check_reconstruction(vy, y_orc, what + " y", sum_tol(Syo, Ayo))
+    diff = np.abs(Ag8 - Ao8)
+    prop = diff @ np.abs(wd).T if diff.any() else 0.0
+    check_interval(y_gpu, vy, dyc + U * np.abs(Syo) + prop, what + " y (end to end)", y_orc, stats,
+                   "y", bare=True)
+
+
 def combine_value(w, rows_of_slots, y_rows_f64, ys_f64):
     """sum_j w_j y_j + y_shared in float64 (slot order, kept slots only), the fp32 running-sum
     bound of the GPU's combine, and the sum of the absolute terms. w [T, K] fp32 weights,
@@ -542,6 +576,11 @@ def host(wts: dict) -> dict:
     return out
 
 
+def mx_planes_to_rows(planes, rows):
+    """MX scale planes [K/128][plane_rows][4] -> per-row scale bytes [rows][K/32]."""
+    return np.ascontiguousarray(planes[:, :rows, :].transpose(1, 0, 2).reshape(rows, -1))
+
+
 def run_layer_gpu(wl, dev: dict, train: bool = False):
     """moe_layer_forward (train: moe_layer_forward_train) on the GPU; returns host copies of out
     and every intermediate."""
@@ -566,7 +605,15 @@ def run_layer_gpu(wl, dev: dict, train: bool = False):
     y = layer.intermediate("y", torch.int16, (rows, H)).cpu().numpy().view(np.uint16)
     g["h_shared"], g["h_routed"] = (h[:n_id], h[n_id:]) if n_id else (None, h)
     g["y_shared"], g["y_routed"] = (y[:n_id], y[n_id:]) if n_id else (None, y)
-    if layer.act_fp8:  # the quantised activations (W8A8)
+    if layer.mx:  # the block-quantised activations: codes, and scale planes by GEMM row
+        sr = layer.layout["scale_rows"]
+        g["xq"] = layer.intermediate("xq", torch.uint8, (T, H)).cpu().numpy()
+        g["hq"] = layer.intermediate("hq", torch.uint8, (rows, I)).cpu().numpy()
+        g["x_scale"] = mx_planes_to_rows(
+            layer.intermediate("x_scale", torch.uint8, (H // 128, sr, 4)).cpu().numpy(), rows)
+        g["h_scale"] = mx_planes_to_rows(
+            layer.intermediate("h_scale", torch.uint8, (I // 128, sr, 4)).cpu().numpy(), rows)
+    elif layer.act_fp8:  # the quantised activations (W8A8)
         g["xq"] = layer.intermediate("xq", torch.uint8, (T, H)).cpu().numpy()
         g["x_scale"] = layer.intermediate("x_scale", torch.float32, (T,)).cpu().numpy()
         g["hq"] = layer.intermediate("hq", torch.uint8, (rows, I)).cpu().numpy()

@@ -67,6 +67,12 @@ int main() {
     moe_layer_a8_ws_layout l8{};
     (void)moe_layer_w8a8_workspace_layout(&s, &l8);
     (void)moe_layer_backward_workspace_size(&s);
+    moe_layer_mx_ws_layout lm{};
+    if ((moe_layer_mx_workspace_layout(&s, &lm) == MOE_OK) != (moe_layer_mx_workspace_size(&s) > 0) ||
+        (lm.total && lm.total != moe_layer_mx_workspace_size(&s))) {
+      std::fprintf(stderr, "FAILED: MX layout of T=%d\n", T);
+      ++failures;
+    }
     moe_bwd_ws_layout lb{};
     (void)moe_layer_backward_workspace_layout(&s, &lb);
   }
@@ -98,6 +104,9 @@ int main() {
                                      P16, nullptr),
            want[i], "moe_layer_forward_noalloc bad shape");
     expect(moe_combine(&bad[i], P16, PF, PI, nullptr, P16, nullptr), want[i], "moe_combine bad shape");
+    expect(moe_layer_forward_mx(&bad[i], P16, P16, nullptr, P8, P8, P8, P8, P8, P8, P8, P8, P8, P8, P8,
+                                P8, P16, PW, size_t(1) << 40, nullptr, nullptr),
+           want[i], "moe_layer_forward_mx bad shape");
   }
 
   // argument errors on a valid shape
@@ -139,6 +148,14 @@ int main() {
                                 PF, P16, PW, 1024, nullptr, nullptr),
          MOE_ERR_WORKSPACE, "w8a8 small ws");
   expect(moe_quantize_rows_e4m3(P16, 4, 60, P8, PF, nullptr), MOE_ERR_INVALID_ARG, "quant cols");
+  expect(moe_quantize_rows_mx(P16, 4, 192, P8, P8, nullptr), MOE_ERR_INVALID_ARG, "mx quant cols");
+  expect(moe_quantize_rows_mx(P16, 4, 256, P8, P8 + 1, nullptr), MOE_ERR_INVALID_ARG, "mx quant scales align");
+  expect(moe_layer_forward_mx(&s, P16, P16, nullptr, P8, P8, P8, nullptr, P8, P8, P8, P8, P8, P8, P8, P8,
+                              P16, PW, size_t(1) << 40, nullptr, nullptr),
+         MOE_ERR_INVALID_ARG, "mx layer missing scale");
+  expect(moe_layer_forward_mx(&s, P16, P16, nullptr, P8, P8, P8, P8, P8, P8, P8, P8, P8, P8, P8, P8, P16,
+                              PW, 1024, nullptr, nullptr),
+         MOE_ERR_WORKSPACE, "mx layer small ws");
   expect(moe_layer_backward(&s, P16, P16, P16, P16, P16, P16, P16, P16, PW, size_t(1) << 40, nullptr,
                             P16, 0.f, P16, PF, PF, PF, PF, PF, PF, nullptr, nullptr, nullptr, PW,
                             size_t(1) << 40, nullptr),
