@@ -183,7 +183,8 @@ def cpu_baseline(wl, dev, n_tok, min_seconds=10.0, max_reps=50, threads=0):
             break
     oracle.set_num_threads(all_threads)
     return {"value": round(reps * len(toks) / dt, 3), "unit": "tokens/s",
-            "cores": cores, "kind": "oracle", "seconds": round(dt, 3),
+            "cores": cores, "nproc": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "seconds": round(dt, 3),
             "sample": "%d of the workload's %d tokens, %d pass(es): all steps of the layer for them "
                       "(%d distinct routed experts%s), fp64 C++ oracle, %d thread(s)"
                       % (len(toks), wl.T, reps, len(experts), " + shared" if wl.n_shared else "",
@@ -270,14 +271,14 @@ def measure(wl, args):
         kname = "ffn_tiled_kernel<%s,%s>" % (gu, str(gu_buf).lower())
         dname = "ffn_tiled_kernel<%s,%s>" % (dn, str(dn_buf).lower())
     else:
-        # the weight-streaming kernel: <gated, FP8 weights, FP8 activations, 16-row sub-blocks
-        # per tile>; 16-row tiles (one sub-block) when the groups average at most 16 rows
+        # the weight-streaming kernel; 16-row tiles (one sub-block) when the groups average at
+        # most 16 rows
         maxns = 1 if rows <= 16 * groups else 4
-        fl = ("true" if wl.fp8 else "false", "true" if wl.act_fp8 else "false", maxns)
-        kname = "ffn_skinny_kernel<true, %s, %s, %d>" % fl
-        dname = "ffn_skinny_kernel<false, %s, %s, %d>" % fl
-        if wl.mx:  # fifth template argument: the MX form
-            kname, dname = kname[:-1] + ", true>", dname[:-1] + ", true>"
+        # <gated, FP8 weights, FP8 activations, 16-row sub-blocks per tile, MX scales>
+        fl = ("true" if wl.fp8 else "false", "true" if wl.act_fp8 else "false", maxns,
+              "true" if wl.mx else "false")
+        kname = "ffn_skinny_kernel<true, %s, %s, %d, %s>" % fl
+        dname = "ffn_skinny_kernel<false, %s, %s, %d, %s>" % fl
     rf["traffic"] = recorded_traffic(wl.name, kname)
     rf["kernel"] = kname + " (routed+shared gate/up grouped GEMM, clamped SwiGLU epilogue)"
     rf["algorithmic_bytes"] = alg["gu_bytes"]
