@@ -93,6 +93,8 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restric
   if (r >= n) return;
   const uint16_t* vr = v + static_cast<size_t>(r) * cols;
   uint8_t* cr = codes + static_cast<size_t>(r) * cols;
+  // the token's GEMM rows of its K slots (K <= 64), one per lane, loaded once for all columns
+  const int slot_row = s2r && lane < K ? s2r[static_cast<size_t>(r) * K + lane] : -1;
   for (int c = lane * 8; c < cols; c += 512) {
     const u32x4_t t = ld16(vr + c);
     float amax = 0.f;
@@ -117,7 +119,7 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restric
     } else {
       if ((lane & 15) == 0 && n_ident > 0) scales[plane + r] = dw;
       for (int k = 0; k < K; ++k) {  // the token's kept slots (row -1: dropped)
-        const int j = s2r[static_cast<size_t>(r) * K + k];
+        const int j = __shfl(slot_row, k);
         if ((lane & 15) == 0 && j >= 0) scales[plane + n_ident + j] = dw;
       }
     }
@@ -130,6 +132,7 @@ hipError_t launch_quant_mx(const uint16_t* v, int rows, int cols, const int32_t*
                            uint8_t* codes, uint8_t* scales, int plane_rows, const int32_t* s2r,
                            int K, int n_ident, hipStream_t stream) {
   if (rows < 1) return hipSuccess;
+  if (s2r && (K < 1 || K > 64)) return hipErrorInvalidValue;  // one slot per lane of a wavefront
   hipLaunchKernelGGL(quant_mx_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, v, rows, cols,
                      rows_dev, codes, reinterpret_cast<uint32_t*>(scales), plane_rows, s2r, K, n_ident);
   return hipGetLastError();
