@@ -122,8 +122,9 @@ __device__ __forceinline__ void barrier_no_fence() {
 }
 
 // Global->LDS DMA of 16 bytes per lane. STREAM marks the load non-temporal (cache policy NT): used
-// for weight tiles, which few workgroups share and which otherwise displace the activation rows
-// that the n-blocks of a band re-read from L2.
+// for the weight tiles of a group with a single row tile, which no other workgroup reads and
+// which would otherwise displace the activation rows that the group's column blocks re-read from
+// L2.
 template <bool STREAM = false>
 __device__ __forceinline__ void lds_dma16(const uint16_t* g, uint16_t* l) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -157,7 +158,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uin
 // through 64-bit addresses.
 template <int EPI, int MIV, bool BUF>
 __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb, int r0, int r1,
-                                           int kb, int nk, int split) {
+                                           int kb, int nk, int split, bool b_shared) {
   constexpr bool W8 = EPI == kEpiSwiglu8 || EPI == kEpiBf16_8;     // FP8 weights, bf16 activations
   constexpr bool MX = EPI == kEpiSwigluMx || EPI == kEpiBf16Mx;     // ... with MX block scales
   constexpr bool A8 = EPI == kEpiSwiglu88 || EPI == kEpiBf16_88 || MX;  // FP8 weights and activations
@@ -310,23 +311,45 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         uint16_t* dst = reinterpret_cast<uint16_t*>(sB8 + stage * kStageB8 + (wave + 8 * i) * 1024);
-        if constexpr (BUF)
-          lds_dma16_buf<true>(rQ[i], qoff8[i], static_cast<uint32_t>((kb + kt) * kBK), dst);
-        else
-          lds_dma16<true>(reinterpret_cast<const uint16_t*>(bsrc8[i] + kt * kBK), dst);
+        if constexpr (BUF) {
+          if (b_shared)
+            lds_dma16_buf(rQ[i], qoff8[i], static_cast<uint32_t>((kb + kt) * kBK), dst);
+          else
+            lds_dma16_buf<true>(rQ[i], qoff8[i], static_cast<uint32_t>((kb + kt) * kBK), dst);
+        } else {
+          if (b_shared)
+            lds_dma16(reinterpret_cast<const uint16_t*>(bsrc8[i] + kt * kBK), dst);
+          else
+            lds_dma16<true>(reinterpret_cast<const uint16_t*>(bsrc8[i] + kt * kBK), dst);
+        }
       }
     } else if constexpr (BUF) {
       const uint32_t k2 = static_cast<uint32_t>((kb + kt) * kBK) * sizeof(uint16_t);
+      if (b_shared) {
 #pragma unroll
-      for (int i = 0; i < kDmaB; ++i)
-        lds_dma16_buf<true>(rB, b16 * 16u, static_cast<uint32_t>(i * bstep * sizeof(uint16_t)) + k2,
-                            sB + stage * kStageB + (wave + 8 * i) * 512);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kDmaB; ++i)
-        lds_dma16<true>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const u32x4_t*>(Wb + i * bstep) + b16) +
-                            (kb + kt) * kBK,
+        for (int i = 0; i < kDmaB; ++i)
+          lds_dma16_buf(rB, b16 * 16u, static_cast<uint32_t>(i * bstep * sizeof(uint16_t)) + k2,
                         sB + stage * kStageB + (wave + 8 * i) * 512);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kDmaB; ++i)
+          lds_dma16_buf<true>(rB, b16 * 16u, static_cast<uint32_t>(i * bstep * sizeof(uint16_t)) + k2,
+                              sB + stage * kStageB + (wave + 8 * i) * 512);
+      }
+    } else {
+      if (b_shared) {
+#pragma unroll
+        for (int i = 0; i < kDmaB; ++i)
+          lds_dma16(reinterpret_cast<const uint16_t*>(reinterpret_cast<const u32x4_t*>(Wb + i * bstep) + b16) +
+                        (kb + kt) * kBK,
+                    sB + stage * kStageB + (wave + 8 * i) * 512);
+      } else {
+#pragma unroll
+        for (int i = 0; i < kDmaB; ++i)
+          lds_dma16<true>(reinterpret_cast<const uint16_t*>(reinterpret_cast<const u32x4_t*>(Wb + i * bstep) + b16) +
+                              (kb + kt) * kBK,
+                          sB + stage * kStageB + (wave + 8 * i) * 512);
+      }
     }
   };
 
@@ -757,17 +780,20 @@ __global__ __launch_bounds__(kThreads, 1) void ffn_tiled_kernel(GroupedParams p,
   if (r0 < 0 || r1 <= r0) return;
 
   const int half = (threadIdx.x >> 6) >> 2;
+  // weight tiles that several row tiles of the group read stay in L2 under the default policy; a group with one row tile streams its weights past L2 (non-temporal), so that they do
+  // not evict the activation rows its column blocks share
+  const bool b_shared = mt > 1;
   // 32-row fragments of this wavefront that hold rows of the group (uniform per wavefront); the
   // main loop is specialised on it so that no branch sits between the MFMAs. Every
   // specialisation passes the same barriers.
   const int miv = min(kMI, max(0, (r1 - (r0 + half * 160) + 31) / 32));
   switch (miv) {
-    case 0: tiled_main<EPI, 0, BUF>(p, g, nb, r0, r1, kb, nk, split); break;
-    case 1: tiled_main<EPI, 1, BUF>(p, g, nb, r0, r1, kb, nk, split); break;
-    case 2: tiled_main<EPI, 2, BUF>(p, g, nb, r0, r1, kb, nk, split); break;
-    case 3: tiled_main<EPI, 3, BUF>(p, g, nb, r0, r1, kb, nk, split); break;
-    case 4: tiled_main<EPI, 4, BUF>(p, g, nb, r0, r1, kb, nk, split); break;
-    default: tiled_main<EPI, 5, BUF>(p, g, nb, r0, r1, kb, nk, split); break;
+    case 0: tiled_main<EPI, 0, BUF>(p, g, nb, r0, r1, kb, nk, split, b_shared); break;
+    case 1: tiled_main<EPI, 1, BUF>(p, g, nb, r0, r1, kb, nk, split, b_shared); break;
+    case 2: tiled_main<EPI, 2, BUF>(p, g, nb, r0, r1, kb, nk, split, b_shared); break;
+    case 3: tiled_main<EPI, 3, BUF>(p, g, nb, r0, r1, kb, nk, split, b_shared); break;
+    case 4: tiled_main<EPI, 4, BUF>(p, g, nb, r0, r1, kb, nk, split, b_shared); break;
+    default: tiled_main<EPI, 5, BUF>(p, g, nb, r0, r1, kb, nk, split, b_shared); break;
   }
 }
 
