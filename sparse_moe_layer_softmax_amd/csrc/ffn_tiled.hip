@@ -24,9 +24,11 @@ namespace {
 //    register file of two wavefronts per SIMD allows. 320 rows also fit a whole expert at the
 //    prefill shape (about T*k/E = 256 rows each, never more than ~310) in one row tile.
 //  - K is staged 64 at a time through a two-stage LDS ring (2 x 72 KB) filled by direct
-//    global->LDS loads (global_load_lds_dwordx4, no VGPR staging; non-temporal for the weights).
-//    One such instruction moves 1 KB: 8 rows of 128 bytes, whole L2 lines. The DMA of K-tile kt+1 is issued at the start of
-//    K-tile kt, so it has a whole K-tile of compute to land.
+//    global->LDS loads (global_load_lds_dwordx4, no VGPR staging). Weight tiles load
+//    non-temporal when their group has a single row tile and under the default cache policy when
+//    several row tiles read them. One such instruction moves 1 KB: 8 rows of 128 bytes, whole L2
+//    lines. The DMA of K-tile kt+1 is issued at the start of K-tile kt, so it has a whole K-tile
+//    of compute to land.
 //  - Each wavefront loads the activation rows of its own live 32-row fragments (one instruction
 //    per fragment) and an eighth of the weight tile, so rows past the end of a group cost neither
 //    DMA nor MFMA: ragged expert tails are cheap.
