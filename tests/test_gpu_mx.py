@@ -315,3 +315,56 @@ def test_mx_full_size_sampled(name):
     P.check_out("tokens %s" % toks.tolist(), g_w[toks], r_w[toks], loc, yg, yo, ysg, yso,
                 as_u16(out[torch.from_numpy(toks).to(DEV)]), out_orc, stats)
     print("[parity] %s: %s" % (name, stats.line()), flush=True)
+
+
+# ----------------------------------------------------------------------------- operands past 4 GiB
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case", ["h_codes_past_4gib", "x_codes_past_4gib"])
+def test_mx_operands_past_4_gib(case):
+    """An FP8 operand of more than 4 GiB takes the tiled kernel's 64-bit-address DMA form: the h
+    codes [2.2M, 2048] of the down projection, or the x codes [2.2M, 2048] of gate/up (E = 1,
+    k = 1, no shared expert, so GEMM row t is token t). Checked against the oracle on the rows
+    around the 2^32-byte boundary of that operand and on the last rows."""
+    _require_gpu()
+    T = 2_200_000
+    H, I = (256, 2048) if case.startswith("h_") else (2048, 256)
+    width = I if case.startswith("h_") else H  # bytes per row of the large operand
+    assert T * width > (1 << 32)
+    wl = Workload(case, T=T, H=H, E=1, K=1, I=I, n_shared=0, scale=1.0, limit=10.0, seed=95,
+                  fp8=True, act_fp8=True, mx=True)
+    print("\n[large] mx %s T=%d H=%d I=%d" % (case, T, H, I), flush=True)
+    dev = generate(wl, DEV)
+    layer = moe.MoELayer.from_inputs(moe.Shape.of(wl), dev)
+    out = layer.forward(dev["x"])
+    torch.cuda.synchronize()
+    boundary = (1 << 32) // width  # first row that starts past 2^32 bytes
+    rows = np.unique(np.concatenate([np.arange(boundary - 40, boundary + 300), np.arange(T - 300, T)]))
+    sel = torch.from_numpy(rows.astype(np.int64)).to(DEV)
+    rd = lambda n, dt, shp: layer.intermediate(n, dt, shp)
+    np.testing.assert_array_equal(rd("slot_to_row", torch.int32, (T,))[sel].cpu().numpy(), rows)
+    sr = layer.layout["scale_rows"]
+    plane_rows = lambda name, k: np.ascontiguousarray(
+        rd(name, torch.uint8, (k // 128, sr, 4))[:, sel, :].cpu().numpy().transpose(1, 0, 2)
+        .reshape(len(rows), -1))
+    xq, xs = oracle.mx_quant_rows(as_u16(dev["x"][sel]))
+    np.testing.assert_array_equal(rd("xq", torch.uint8, (T, H))[sel].cpu().numpy(), xq)
+    np.testing.assert_array_equal(plane_rows("x_scale", H), xs)
+    gh = as_u16(rd("h", torch.bfloat16, (T, I))[sel])
+    hq_g = rd("hq", torch.uint8, (T, I))[sel].cpu().numpy()
+    hs_g = plane_rows("h_scale", I)
+    hq_r, hs_r = oracle.mx_quant_rows(gh)  # the GPU's codes from its own h: bit-exact
+    np.testing.assert_array_equal(hq_g, hq_r)
+    np.testing.assert_array_equal(hs_g, hs_r)
+    w3 = tuple(oracle.Mx(dev[n][0].cpu().numpy(), dev[n + "_mx"][0].cpu().numpy())
+               for n in ("w_gate", "w_up", "w_down"))
+    h_o = oracle.gateup_rows_mx(xq, xs, w3[0], w3[1], wl.limit)
+    hq_o, hs_o = oracle.mx_quant_rows(h_o)
+    y_o = oracle.down_rows_mx(hq_o, hs_o, w3[2])
+    gy = as_u16(rd("y", torch.bfloat16, (T, H))[sel])
+    assert P.kernel_of(T, 1) == "tiled"
+    stats = P.Stats()
+    P.check_mx_rows(case, xq, xs, w3, wl.limit, P.chain_for("tiled", True, True, mx=True), gh, hq_g,
+                    hs_g, gy, h_o, hq_o, hs_o, y_o, stats)
+    # one expert, weight 1: the output rows are the y rows
+    np.testing.assert_array_equal(as_u16(out[sel]), gy)
+    print("[parity] mx %s: %s" % (case, stats.line()), flush=True)
