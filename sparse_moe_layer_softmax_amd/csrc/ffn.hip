@@ -163,6 +163,11 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   p.out = q.h;
   p.N = q.I;
   p.Kd = q.a8 && tiled ? q.H / 2 : q.H;
+  if (q.mx && tiled) {  // the tiled epilogue quantises h for the down projection itself
+    p.mx_hq = q.hq;
+    p.mx_hs = q.hs;
+    p.mx_h_rows = q.mx_rows;
+  }
   p.gu = q.gu;
   if (q.gu && (q.w8 || q.a8)) return hipErrorInvalidValue;
   if (tiled)
@@ -175,12 +180,15 @@ hipError_t launch_ffn(const FfnProblem& q, hipStream_t stream, hipEvent_t const*
   mark(1);
 
   // down -> y (h rows are already in row order: identity gather); W8A8: the valid h rows
-  // (offsets[G] of them) quantised per row first
-  if (q.mx) {
+  // (offsets[G] of them) quantised per row first; MX: quantised by blocks, in the tiled
+  // gate/up epilogue or here after the weight-streaming kernel
+  p.mx_hq = nullptr;
+  p.mx_hs = nullptr;
+  if (q.mx && !tiled) {
     e = launch_quant_mx(q.h, q.rows_max, q.I, q.offsets + q.n_groups, q.hq, q.hs, q.mx_rows,
                         nullptr, 0, 0, stream);
     if (e != hipSuccess) return e;
-  } else if (q.a8) {
+  } else if (q.a8 && !q.mx) {
     e = launch_quant_rows(q.h, q.rows_max, q.I, q.offsets + q.n_groups, q.hq, q.sh, stream);
     if (e != hipSuccess) return e;
   }

@@ -61,6 +61,11 @@ struct GroupedParams {
   const uint8_t* X1b;
   const uint8_t* a_mx;
   int32_t a_mx_rows;
+  // kEpiSwigluMx, when mx_hq is set: h also leaves the epilogue MX-quantised, as codes
+  // [rows, N] and scale bytes in planes [N/128][mx_h_rows][4] by row (the down GEMM's a_mx)
+  uint8_t* mx_hq;
+  uint8_t* mx_hs;
+  int32_t mx_h_rows;
 };
 
 

@@ -691,6 +691,19 @@ __device__ __forceinline__ void tiled_main(const GroupedParams& p, int g, int nb
       const u32x4_t val = *reinterpret_cast<const u32x4_t*>(&ep[row * C + (((ch ^ row) & (CH - 1)) << 3)]);
       const int r = rbase + i * 32 + row;
       if (r < r1) *reinterpret_cast<u32x4_t*>(p.out + static_cast<size_t>(r) * p.N + col0 + ch * 8) = val;
+      if constexpr (MX && GATED) {
+        // the four lanes of a row hold its 32 columns col0.. (block `quarter` of 128-column plane
+        // nb): h's MX codes and scale byte for the down projection, from the bf16 values just
+        // stored
+        if (p.mx_hq) {
+          uint2 codes;
+          const int sc = mx_quant8(val, &codes);
+          if (r < r1) {
+            *reinterpret_cast<uint2*>(p.mx_hq + static_cast<size_t>(r) * p.N + col0 + ch * 8) = codes;
+            if (ch == 0) p.mx_hs[(static_cast<size_t>(nb) * p.mx_h_rows + r) * 4 + quarter] = static_cast<uint8_t>(sc);
+          }
+        }
+      }
     }
     // one fragment row at a time: keeps the scheduler from reading every accumulator at once
     __builtin_amdgcn_sched_barrier(0);

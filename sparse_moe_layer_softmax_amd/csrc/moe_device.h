@@ -119,4 +119,36 @@ __device__ __forceinline__ float clamped_swiglu(float g, float u, float limit) {
   return g / (1.f + __expf(-g)) * u;
 }
 
+// ---- FP8 (OCP E4M3) encoding of bf16 values, shared by the quantisers and the fused epilogue
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float clamp448(float q) { return fminf(fmaxf(q, -448.f), 448.f); }
+
+// four codes (bytes 0..3 = a, b, c, d): E4M3 nearest-even of each value clamped to +-448
+// (v_cvt_pk_fp8_f32)
+__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// MX (OCP MXFP8) block quantisation, for a lane holding 8 of a 32-element block's bf16 values
+// (t: four dwords, element 0 in the low half of t[0]) in a group of 4 lanes (lane ^ 1, lane ^ 2)
+// that holds the block. Returns the block's E8M0 byte s = max(E(amax) - 8, 0), E the biased
+// fp32 exponent of the block's largest magnitude (a zero block: 0), and the lane's 8 codes
+// E4M3_RNE(clamp(v * 2^(127 - s), +-448)) in *codes; every step is exact but the final rounding.
+__device__ __forceinline__ int mx_quant8(const u32x4_t& t, uint2* codes) {
+  float amax = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(t[d])), fabsf(bf_hi(t[d]))));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int s = max(static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF) - 8, 0);
+  const float f = __uint_as_float(static_cast<uint32_t>(254 - s) << 23);  // 2^(127 - s)
+  codes->x = pack4(bf_lo(t[0]) * f, bf_hi(t[0]) * f, bf_lo(t[1]) * f, bf_hi(t[1]) * f);
+  codes->y = pack4(bf_lo(t[2]) * f, bf_hi(t[2]) * f, bf_lo(t[3]) * f, bf_hi(t[3]) * f);
+  return s;
+}
+
 }  // namespace moe

@@ -21,17 +21,6 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float clamp448(float q) { return fminf(fmaxf(q, -448.f), 448.f); }
-
-// four codes (bytes 0..3 = a, b, c, d)
-__device__ __forceinline__ uint32_t pack4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
-  return static_cast<uint32_t>(w);
-}
 
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ v, int rows,
                                                          int cols, const int32_t* __restrict__ rows_dev,
@@ -75,6 +64,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 // amax that is zero or subnormal. The codes are E4M3_RNE(clamp(v * 2^(127 - s), +-448)); the
 // power of two is a normal fp32 value (s <= 246 for bf16 input), so the product is exact unless
 // it falls below the fp32 normal range, where the E4M3 code is zero either way.
+// (The block step itself is mx_quant8, which the tiled gate/up epilogue also applies to h as it
+// writes it; this kernel quantises x, and h after the weight-streaming kernel.)
 // One wavefront per row; a lane takes 8 consecutive elements, so a block is 4 lanes and a
 // 128-element K-tile (one dword of 4 scale bytes) 16 lanes. The codes keep the source row
 // order; the scale dwords go to planes [cols / 128][plane_rows] of the GEMM that reads them:
@@ -97,16 +88,8 @@ __global__ __launch_bounds__(256) void quant_mx_kernel(const uint16_t* __restric
   const int slot_row = s2r && lane < K ? s2r[static_cast<size_t>(r) * K + lane] : -1;
   for (int c = lane * 8; c < cols; c += 512) {
     const u32x4_t t = ld16(vr + c);
-    float amax = 0.f;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(t[d])), fabsf(bf_hi(t[d]))));
-    amax = fmaxf(amax, __shfl_xor(amax, 1));
-    amax = fmaxf(amax, __shfl_xor(amax, 2));
-    const int s = max(static_cast<int>((__float_as_uint(amax) >> 23) & 0xFF) - 8, 0);
-    const float f = __uint_as_float(static_cast<uint32_t>(254 - s) << 23);  // 2^(127 - s)
     uint2 o;
-    o.x = pack4(bf_lo(t[0]) * f, bf_hi(t[0]) * f, bf_lo(t[1]) * f, bf_hi(t[1]) * f);
-    o.y = pack4(bf_lo(t[2]) * f, bf_hi(t[2]) * f, bf_lo(t[3]) * f, bf_hi(t[3]) * f);
+    const int s = mx_quant8(t, &o);
     *reinterpret_cast<uint2*>(cr + c) = o;
     // the K-tile's four scale bytes, blocks in order, from lanes 0, 4, 8, 12 of the 16-lane group
     const int g0 = lane & ~15;
