@@ -46,8 +46,34 @@ import oracle
 import sparse_moe_layer_softmax_amd as moe
 from sparse_moe_layer_softmax_amd.workloads import as_u16
 
-f64 = oracle.bf16_to_f64
 U = 2.0 ** -24  # fp32 unit roundoff
+
+
+def f64(u16) -> np.ndarray:
+    """bf16 bit patterns -> float64 values (exact; through torch, whose conversion runs on every
+    core: the weights of a full-size layer pass through here once per checked group)."""
+    a = np.ascontiguousarray(u16, np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+# ----------------------------------------------------------------------------- group checks
+def run_pipelined(prepare, check, items, workers: int = 6, window: int = 12):
+    """check(prepare(item)) for every item, results in item order. prepare runs here (it may
+    copy device tensors to the host); check runs on a thread pool (numpy, torch and the oracle's
+    C calls release the interpreter lock in their heavy parts). At most `window` prepared items
+    are held at once, which bounds the host memory of full-size layers."""
+    import collections
+    from concurrent.futures import ThreadPoolExecutor
+
+    out, pending = [], collections.deque()
+    with ThreadPoolExecutor(workers) as ex:
+        for it in items:
+            pending.append(ex.submit(check, prepare(it)))
+            while len(pending) >= window:
+                out.append(pending.popleft().result())
+        while pending:
+            out.append(pending.popleft().result())
+    return out
 
 
 # ----------------------------------------------------------------------------- bf16 rounding
@@ -91,6 +117,10 @@ class Stats:
         c[1] += cand
         c[2] += flips
         c[3] += bare_bad
+
+    def merge(self, other: "Stats") -> None:
+        for k, v in other.rows.items():
+            self.add(k, *v)
 
     def line(self) -> str:
         return "; ".join("%s: %d elements, %d candidates, %d flips%s"
@@ -214,11 +244,7 @@ def chain_for(kern: str, fp8: bool, act_fp8: bool, mx: bool = False) -> Chain:
     return CHAINS[kern + ("_mx" if mx else "_a8" if act_fp8 else "_w8" if fp8 else "")]
 
 
-def _group_max(M, g):
-    return np.abs(M).reshape(M.shape[0], -1, g).max(axis=2)
-
-
-def chain_sums(A, W, chain: Chain, rows_per_chunk: int = 0):
+def chain_sums(A, W, chain: Chain):
     """Exact sums S = A W^T (float64) and the a-priori bound on |fp32 chain - S| per element, for
     A [n, K], W [m, K] float64 values (dequantised for FP8 operands). With u = 2^-24 and the
     alignment granule gamma = 2^(1 - guard) u (relative to the largest aligned term):
@@ -228,12 +254,13 @@ def chain_sums(A, W, chain: Chain, rows_per_chunk: int = 0):
     last term is the rounding), summed over the chain. The largest |product| of a group is
     bounded by max|a| max|w| over the group; S_j, A_j are the running sum and the instruction's
     absolute products."""
-    A = np.ascontiguousarray(A, np.float64)
-    W = np.ascontiguousarray(W, np.float64)
+    A = torch.from_numpy(np.ascontiguousarray(A, np.float64))
+    W = torch.from_numpy(np.ascontiguousarray(W, np.float64))
     n, K = A.shape
     m = W.shape[0]
+    absW = W.abs()
     S = A @ W.T
-    Aabs = np.abs(A) @ np.abs(W).T
+    Aabs = A.abs() @ absW.T
     blk, per_block = chain.block, chain.per_block
     assert K % blk == 0 and blk % chain.group == 0, (K, blk, chain.group)
     # long reductions: running sums taken every c instructions only (each instruction's running
@@ -245,22 +272,18 @@ def chain_sums(A, W, chain: Chain, rows_per_chunk: int = 0):
     blk, per_block = blk * c, per_block * c
     nb = K // blk
     gamma = 2.0 ** (1 - chain.guard) * U
-    XW = _group_max(A, chain.group) @ _group_max(W, chain.group).T  # sum of group max products
+    # sum over groups of the largest |product| bound max|a| max|w|
+    g = chain.group
+    XW = A.abs().view(n, -1, g).amax(2) @ absW.view(m, -1, g).amax(2).T
     mg = chain.span // chain.group
-    # the running sums at block boundaries enter only as magnitudes summed over the chain, so
-    # float32 serves (its error is orders below the 5% margin of the bound)
-    Wt = torch.from_numpy(W.reshape(m, nb, blk)).permute(1, 2, 0).contiguous().float()  # [nb, blk, m]
-    before = np.empty((n, m))   # sum over blocks of |running sum at the block's start|
-    after = np.empty((n, m))    # sum over blocks of |running sum at the block's end|
-    step = rows_per_chunk or max(1, int(1.2e7 // max(1, nb * m)))
-    for r0 in range(0, n, step):
-        At = torch.from_numpy(A[r0:r0 + step].reshape(-1, nb, blk)).permute(1, 0, 2).float()
-        run = torch.bmm(At, Wt).cumsum_(0)           # running sums at block ends: [nb, c, m]
-        last = run[-1].abs().double()
-        run.abs_()
-        tot = run.sum(0, dtype=torch.float64)
-        after[r0:r0 + step] = tot.numpy()
-        before[r0:r0 + step] = (tot - last).numpy()   # starts: the ends shifted by one block
+    # running sums at block ends, one block product at a time
+    run = torch.zeros((n, m), dtype=torch.float64)
+    after = torch.zeros((n, m), dtype=torch.float64)  # sum over blocks of |running sum at its end|
+    for b in range(nb):
+        run += A[:, b * blk:(b + 1) * blk] @ W[:, b * blk:(b + 1) * blk].T
+        after += run.abs()
+    before = (after - run.abs()).numpy()  # sum over blocks of |running sum at the block's start|
+    S, Aabs, XW, after = S.numpy(), Aabs.numpy(), XW.numpy(), after.numpy()
     if per_block == 1:
         acc = gamma * ((chain.group - 1) * XW + mg * (before + Aabs)) + U * after
     else:  # every running sum inside block b is at most |S_{b-1}| + A_b
@@ -303,9 +326,12 @@ def e4m3_table():
 
 
 def weight_f64(w) -> np.ndarray:
-    """Float64 values of a weight matrix: bf16 bit patterns, or an oracle.Fp8 (scale * e4m3)."""
+    """Float64 values of a weight matrix: bf16 bit patterns, or an oracle.Fp8 (scale * e4m3;
+    the codes decode through torch's float8_e4m3fn, to which the oracle's own decoding is pinned
+    code by code)."""
     if isinstance(w, oracle.Fp8):
-        return e4m3_table()[w.q] * w.scale.astype(np.float64)[..., None]
+        q = torch.from_numpy(np.ascontiguousarray(w.q, np.uint8)).view(torch.float8_e4m3fn)
+        return (q.to(torch.float64) * torch.from_numpy(w.scale.astype(np.float64))[..., None]).numpy()
     return f64(w)
 
 

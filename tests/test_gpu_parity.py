@@ -440,25 +440,21 @@ def test_full_size_sampled(name):
         a, b = int(g_off[e]), int(g_off[e + 1])
         if a < b:
             groups.append(("expert %d" % e, e, n_id + a, g_r2s[a:b] // K))
-    cache = {}
 
     def weights(key):
-        if key not in cache:
-            names = ("s_gate", "s_up", "s_down") if key is None else ("w_gate", "w_up", "w_down")
+        names = ("s_gate", "s_up", "s_down") if key is None else ("w_gate", "w_up", "w_down")
 
-            def one(n):
-                t = dev[n] if key is None else dev[n][key]
-                if t.dtype == torch.uint8:
-                    sc = dev[n + "_scale"] if key is None else dev[n + "_scale"][key]
-                    return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
-                return as_u16(t)
-            cache[key] = tuple(one(n) for n in names)
-        return cache[key]
+        def one(n):
+            t = dev[n] if key is None else dev[n][key]
+            if t.dtype == torch.uint8:
+                sc = dev[n + "_scale"] if key is None else dev[n + "_scale"][key]
+                return oracle.Fp8(t.cpu().numpy(), sc.cpu().numpy())
+            return as_u16(t)
+        return tuple(one(n) for n in names)
 
-    stats = P.Stats()
-    y_rows = {}  # layer row -> (gpu y, oracle y) for the sampled tokens' rows
-    n_rows = 0
-    for label, key, r0, tok_of in groups:
+    def prepare(grp):
+        # the group's rows to check and every device-side input of them, copied to the host
+        label, key, r0, tok_of = grp
         n = len(tok_of)
         local = set()
         for t0 in range(0, n, bm):
@@ -469,16 +465,26 @@ def test_full_size_sampled(name):
         sel = torch.from_numpy(lrows.astype(np.int64)).to(DEV)
         gh, gy = as_u16(h_all[sel]), as_u16(y_all[sel])
         x_rows = as_u16(dev["x"][torch.from_numpy(tok_of[local].astype(np.int64)).to(DEV)])
-        w3 = weights(key)
+        return label, tok_of, local, lrows, gh, gy, x_rows, weights(key)
+
+    def check(prep):
+        label, tok_of, local, lrows, gh, gy, x_rows, w3 = prep
+        st = P.Stats()
         rh, ry = P.ffn_rows(x_rows, w3, wl.limit)
         P.check_ffn_rows("%s rows %s" % (label, local[:4].tolist()), x_rows, w3, wl.limit, chain,
-                         gh, gy, rh, ry, stats)
-        for i, lr in enumerate(lrows):
-            if int(tok_of[local[i]]) in tok_set:
-                y_rows[int(lr)] = (gy[i], ry[i])
-        n_rows += len(local)
-        if key in cache and key is not None and len(cache) > 8:
-            del cache[key]  # keep host copies of a few experts only
+                         gh, gy, rh, ry, st)
+        yr = {int(lr): (gy[i], ry[i]) for i, lr in enumerate(lrows)
+              if int(tok_of[local[i]]) in tok_set}
+        return len(local), yr, st
+
+    stats = P.Stats()
+    y_rows = {}  # layer row -> (gpu y, oracle y) for the sampled tokens' rows
+    n_rows = 0
+    for n_g, yr, st in P.run_pipelined(prepare, check, groups):
+        n_rows += n_g
+        y_rows.update(yr)
+        stats.merge(st)
+
     # the sampled tokens' outputs: chained and end to end
     s2r_t = g_s2r.reshape(T, K)[toks]
     rows_t = np.where(s2r_t >= 0, n_id + s2r_t, -1)
