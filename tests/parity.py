@@ -315,14 +315,11 @@ def swiglu_bound(g, u, dg, du, limit):
 
 
 # ----------------------------------------------------------------------------- weights
-_E4M3 = None
-
-
-def e4m3_table():
-    global _E4M3
-    if _E4M3 is None:
-        _E4M3 = np.array([oracle.double_from_e4m3(c) for c in range(256)])
-    return _E4M3
+def e4m3_f64(codes) -> np.ndarray:
+    """float64 values of E4M3 codes (torch's float8_e4m3fn, to which the oracle's own decoding is
+    pinned code by code; multithreaded, unlike a table gather)."""
+    q = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn)
+    return q.to(torch.float64).numpy()
 
 
 def weight_f64(w) -> np.ndarray:
@@ -427,8 +424,7 @@ def _code_sums(codes, row_scale, w):
     """The oracle's scaled W8A8 projection in float64, in its own order of operations: the exact
     sum of E4M3 code products (small dyadic numbers: exact in any order), times the weight-row
     scale, times the activation-row scale; and the absolute terms."""
-    e4 = e4m3_table()
-    A, Wc = e4[codes], e4[w.q]
+    A, Wc = e4m3_f64(codes), e4m3_f64(w.q)
     ws = w.scale.astype(np.float64)[None, :]
     rs = np.asarray(row_scale, np.float64)[:, None]
     return (A @ Wc.T) * ws * rs, (np.abs(A) @ np.abs(Wc).T) * ws * np.abs(rs)
@@ -443,9 +439,8 @@ def check_w8a8_rows(what, xq, sx, w3, limit, chain, h_gpu, hq_gpu, sh_gpu, y_gpu
     end-to-end interval widened by the difference of the dequantised h rows, which comes only
     from checked h flips (one flip can move the codes of its element, or the whole row's scale
     when it is the row maximum)."""
-    e4 = e4m3_table()
     wg, wu, wd = (weight_f64(w) for w in w3)
-    A = e4[xq] * np.asarray(sx, np.float64)[:, None]
+    A = e4m3_f64(xq) * np.asarray(sx, np.float64)[:, None]
     _, dg, _ = chain_sums(A, wg, chain)
     _, du, _ = chain_sums(A, wu, chain)
     Sg, Ag = _code_sums(xq, sx, w3[0])
@@ -454,14 +449,14 @@ def check_w8a8_rows(what, xq, sx, w3, limit, chain, h_gpu, hq_gpu, sh_gpu, y_gpu
     check_reconstruction(vh, h_orc, what + " h", th)
     dh = swiglu_bound(fl32(Sg), fl32(Su), dg + U * np.abs(Sg), du + U * np.abs(Su), limit)
     check_interval(h_gpu, vh, dh, what + " h", h_orc, stats, "h", bare=True)
-    Ag8 = e4[hq_gpu] * np.asarray(sh_gpu, np.float64)[:, None]
+    Ag8 = e4m3_f64(hq_gpu) * np.asarray(sh_gpu, np.float64)[:, None]
     _, dyc, _ = chain_sums(Ag8, wd, chain)
     Syc, _ = _code_sums(hq_gpu, sh_gpu, w3[2])
     check_interval(y_gpu, Syc, dyc, what + " y (chained)")
     Syo, Ayo = _code_sums(hq_orc, sh_orc, w3[2])
     vy = fl32(Syo)
     check_reconstruction(vy, y_orc, what + " y", sum_tol(Syo, Ayo))
-    Ao8 = e4[hq_orc] * np.asarray(sh_orc, np.float64)[:, None]
+    Ao8 = e4m3_f64(hq_orc) * np.asarray(sh_orc, np.float64)[:, None]
     diff = np.abs(Ag8 - Ao8)
     prop = diff @ np.abs(wd).T if diff.any() else 0.0
     check_interval(y_gpu, vy, dyc + U * np.abs(Syo) + prop, what + " y (end to end)", y_orc, stats,

@@ -256,36 +256,47 @@ def test_w8a8_full_size_sampled(name):
     chain = P.chain_for(kern, True, True)
     stats = P.Stats()
     yg_rows, yo_rows, ysg, yso = {}, {}, [], []
+    qs, items = {}, []
     for t in toks:
         t = int(t)
         x_t = as_u16(dev["x"][t:t + 1])
         q_t, s_t = oracle.quant_rows_e4m3(x_t)
         np.testing.assert_array_equal(xq_all[t:t + 1].cpu().numpy(), q_t, err_msg="xq token %d" % t)
         np.testing.assert_array_equal(sx_all[t:t + 1], s_t)
+        qs[t] = (q_t, s_t)
         rows = g_s2r[t * K:(t + 1) * K]
-        slots = [(j, int(g_idx[t, j]), n_id + int(rows[j])) for j in range(K) if rows[j] >= 0]
+        items += [(t, j, int(g_idx[t, j]), n_id + int(rows[j])) for j in range(K) if rows[j] >= 0]
         if n_id:
-            slots.append((-1, None, t))  # the shared row
-        for j, e, row in slots:
-            w3 = (w("s_gate"), w("s_up"), w("s_down")) if e is None else \
-                (w("w_gate", e), w("w_up", e), w("w_down", e))
-            gh = as_u16(h_all[row:row + 1])
-            hq_g = hq_all[row:row + 1].cpu().numpy()
-            sh_g = sh_all[row:row + 1]
-            hq_r, sh_r = oracle.quant_rows_e4m3(gh)  # the GPU's codes from its own h: bit-exact
-            np.testing.assert_array_equal(hq_g, hq_r, err_msg="hq row %d" % row)
-            np.testing.assert_array_equal(sh_g, sh_r)
-            h_o = oracle.gateup_rows_w8a8(q_t, s_t, w3[0], w3[1], wl.limit)
-            hq_o, sh_o = oracle.quant_rows_e4m3(h_o)
-            y_o = oracle.down_rows_w8a8(hq_o, sh_o, w3[2])
-            gy = as_u16(y_all[row:row + 1])
-            P.check_w8a8_rows("token %d slot %d" % (t, j), q_t, s_t, w3, wl.limit, chain, gh, hq_g,
-                              sh_g, gy, h_o, hq_o, sh_o, y_o, stats)
-            if e is None:
-                ysg.append(gy[0])
-                yso.append(y_o[0])
-            else:
-                yg_rows[row], yo_rows[row] = gy[0], y_o[0]
+            items.append((t, -1, None, t))  # the shared row
+
+    def prepare(it):
+        t, j, e, row = it
+        w3 = (w("s_gate"), w("s_up"), w("s_down")) if e is None else \
+            (w("w_gate", e), w("w_up", e), w("w_down", e))
+        return (t, j, e, row, w3, as_u16(h_all[row:row + 1]), hq_all[row:row + 1].cpu().numpy(),
+                sh_all[row:row + 1], as_u16(y_all[row:row + 1]))
+
+    def check(prep):
+        t, j, e, row, w3, gh, hq_g, sh_g, gy = prep
+        q_t, s_t = qs[t]
+        hq_r, sh_r = oracle.quant_rows_e4m3(gh)  # the GPU's codes from its own h: bit-exact
+        np.testing.assert_array_equal(hq_g, hq_r, err_msg="hq row %d" % row)
+        np.testing.assert_array_equal(sh_g, sh_r)
+        h_o = oracle.gateup_rows_w8a8(q_t, s_t, w3[0], w3[1], wl.limit)
+        hq_o, sh_o = oracle.quant_rows_e4m3(h_o)
+        y_o = oracle.down_rows_w8a8(hq_o, sh_o, w3[2])
+        st = P.Stats()
+        P.check_w8a8_rows("token %d slot %d" % (t, j), q_t, s_t, w3, wl.limit, chain, gh, hq_g,
+                          sh_g, gy, h_o, hq_o, sh_o, y_o, st)
+        return e, row, gy[0], y_o[0], st
+
+    for e, row, gy0, yo0, st in P.run_pipelined(prepare, check, items):
+        stats.merge(st)
+        if e is None:
+            ysg.append(gy0)
+            yso.append(yo0)
+        else:
+            yg_rows[row], yo_rows[row] = gy0, yo0
     # the sampled tokens' outputs against the oracle's combine of its own rows
     s2r_t = g_s2r.reshape(T, K)[toks]
     uniq = sorted(yg_rows)
