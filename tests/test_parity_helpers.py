@@ -90,3 +90,53 @@ def test_check_interval_accepts_and_rejects():
         pass
     else:
         raise AssertionError("an off-interval value must be rejected")
+
+
+def test_f64_and_e4m3_decodes_match_the_oracle():
+    """The parity helpers' own bf16 and E4M3 decodes (through torch) against the oracle's, on
+    every bit pattern (NaN patterns compared as NaN)."""
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        mine, ref = P.f64(b), oracle.bf16_to_f64(b)
+    np.testing.assert_array_equal(np.isnan(mine), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(mine[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(mine[ok]), np.signbit(ref[ok]))
+    c = np.arange(256, dtype=np.uint8)
+    mine8 = P.e4m3_f64(c)
+    ref8 = np.array([oracle.double_from_e4m3(int(v)) for v in c])
+    np.testing.assert_array_equal(np.isnan(mine8), np.isnan(ref8))
+    ok = ~np.isnan(ref8)
+    np.testing.assert_array_equal(mine8[ok], ref8[ok])
+    np.testing.assert_array_equal(np.signbit(mine8[ok]), np.signbit(ref8[ok]))
+
+
+def test_run_pipelined_keeps_order_and_raises():
+    """Results come back in item order whatever order the pool finishes them in, and a failing
+    check surfaces as its exception."""
+    import time
+
+    prepared = []
+
+    def prepare(i):
+        prepared.append(i)
+        return i
+
+    def check(i):
+        time.sleep(0.002 * ((7 * i) % 5))
+        return i * i
+
+    assert P.run_pipelined(prepare, check, range(40), workers=4, window=6) == [i * i for i in range(40)]
+    assert prepared == list(range(40))
+
+    def bad(i):
+        if i == 13:
+            raise AssertionError("item 13")
+        return i
+
+    try:
+        P.run_pipelined(lambda i: i, bad, range(30), workers=3, window=4)
+    except AssertionError as e:
+        assert "item 13" in str(e)
+    else:
+        raise AssertionError("the failing check did not raise")
