@@ -387,6 +387,16 @@ def h_reference(Sg, Ag, Su, Au, limit):
     return vh, tol
 
 
+def _mmT(a, w, absolute=False):
+    """a @ w.T in float64 (|a| @ |w|.T with absolute), through torch's multithreaded CPU
+    product."""
+    ta = torch.from_numpy(np.ascontiguousarray(a, np.float64))
+    tw = torch.from_numpy(np.ascontiguousarray(w, np.float64))
+    if absolute:
+        ta, tw = ta.abs(), tw.abs()
+    return (ta @ tw.T).numpy()
+
+
 def check_ffn_rows(what, x_rows, w3, limit, chain, h_gpu, y_gpu, h_orc=None, y_orc=None,
                    stats=None):
     """One group's rows of the expert FFN (bf16 or FP8 weights, bf16 activations).
@@ -411,10 +421,10 @@ def check_ffn_rows(what, x_rows, w3, limit, chain, h_gpu, y_gpu, h_orc=None, y_o
     check_interval(y_gpu, Syc, dyc, what + " y (chained)", stats=None)
     # y end to end: the oracle's y, widened only by the checked h flips
     ho = f64(h_orc)
-    Syo = ho @ wd.T
+    Syo = _mmT(ho, wd)
     vy = fl32(Syo)
-    check_reconstruction(vy, y_orc, what + " y", sum_tol(Syo, np.abs(ho) @ np.abs(wd).T))
-    prop = (np.abs(hg - ho) * fh) @ np.abs(wd).T if fh.any() else 0.0
+    check_reconstruction(vy, y_orc, what + " y", sum_tol(Syo, _mmT(ho, wd, absolute=True)))
+    prop = _mmT(np.abs(hg - ho) * fh, wd, absolute=True) if fh.any() else 0.0
     fy = check_interval(y_gpu, vy, dyc + U * np.abs(Syo) + prop, what + " y (end to end)", y_orc,
                         stats, "y", bare=True)
     return fh, fy
@@ -427,7 +437,7 @@ def _code_sums(codes, row_scale, w):
     A, Wc = e4m3_f64(codes), e4m3_f64(w.q)
     ws = w.scale.astype(np.float64)[None, :]
     rs = np.asarray(row_scale, np.float64)[:, None]
-    return (A @ Wc.T) * ws * rs, (np.abs(A) @ np.abs(Wc).T) * ws * np.abs(rs)
+    return _mmT(A, Wc) * ws * rs, _mmT(A, Wc, absolute=True) * ws * np.abs(rs)
 
 
 def check_w8a8_rows(what, xq, sx, w3, limit, chain, h_gpu, hq_gpu, sh_gpu, y_gpu, h_orc, hq_orc,
@@ -458,7 +468,7 @@ def check_w8a8_rows(what, xq, sx, w3, limit, chain, h_gpu, hq_gpu, sh_gpu, y_gpu
     check_reconstruction(vy, y_orc, what + " y", sum_tol(Syo, Ayo))
     Ao8 = e4m3_f64(hq_orc) * np.asarray(sh_orc, np.float64)[:, None]
     diff = np.abs(Ag8 - Ao8)
-    prop = diff @ np.abs(wd).T if diff.any() else 0.0
+    prop = _mmT(diff, wd, absolute=True) if diff.any() else 0.0
     check_interval(y_gpu, vy, dyc + U * np.abs(Syo) + prop, what + " y (end to end)", y_orc, stats,
                    "y", bare=True)
 
@@ -486,7 +496,7 @@ def check_mx_rows(what, xq, xs, w3, limit, chain, h_gpu, hq_gpu, hs_gpu, y_gpu, 
     vy = fl32(Syo)
     check_reconstruction(vy, y_orc, what + " y", sum_tol(Syo, Ayo))
     diff = np.abs(Ag8 - Ao8)
-    prop = diff @ np.abs(wd).T if diff.any() else 0.0
+    prop = _mmT(diff, wd, absolute=True) if diff.any() else 0.0
     check_interval(y_gpu, vy, dyc + U * np.abs(Syo) + prop, what + " y (end to end)", y_orc, stats,
                    "y", bare=True)
 
