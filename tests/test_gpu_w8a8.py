@@ -118,6 +118,11 @@ SMALL = {
         Workload("e", T=640, H=256, E=32, K=8, I=512, scale=2.827), "w8a8_midsize_t640_h256_e32_k8", 69),
     "w8a8_dense_ffn_t700_h512_i2304": _w8a8(
         Workload("f", T=700, H=512, E=1, K=1, I=2304, n_shared=0), "w8a8_dense_ffn_t700_h512_i2304", 70),
+    # the Hy4 width element by element on the tiled FP8 MFMA path (gate/up K-loop of 48 tiles of
+    # 128 codes, down of 16): 128 tokens, 4 experts of about 64 rows, top-2, the shared expert
+    "w8a8_hy4_width_t128_e4_k2": _w8a8(
+        Workload("w", T=128, H=6144, E=4, K=2, I=2048, scale=2.827, w_std=0.006, router_std=0.006),
+        "w8a8_hy4_width_t128_e4_k2", 71),
 }
 
 
