@@ -81,15 +81,38 @@ __global__ __launch_bounds__(256) void ktile_transpose_kernel(
   }
 }
 
-// kt[2g], kt[2g+1]: first K-tile and K-tile count of group g (the tile table's order).
-__global__ void group_ktiles_kernel(const int32_t* __restrict__ offsets, int G,
-                                    int32_t* __restrict__ kt) {
-  int acc = 0;
-  for (int g = 0; g < G; ++g) {
-    const int c = (offsets[g + 1] - offsets[g] + kKT - 1) / kKT;
-    kt[2 * g] = acc;
-    kt[2 * g + 1] = c;
-    acc += c;
+// kt[2g], kt[2g+1]: first K-tile and K-tile count of group g (the tile table's order). One
+// workgroup of 256 threads, four consecutive groups per thread (G <= 1024): counts, then an
+// exclusive integer scan (lanes by shuffles, wavefronts through LDS).
+__global__ __launch_bounds__(256) void group_ktiles_kernel(const int32_t* __restrict__ offsets, int G,
+                                                           int32_t* __restrict__ kt) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int c4[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    c4[i] = g < G ? (offsets[g + 1] - offsets[g] + kKT - 1) / kKT : 0;
+    sum += c4[i];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int b = inc - sum;
+  for (int j = 0; j < w; ++j) b += wsum[j];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int g = 4 * tid + i;
+    if (g < G) {
+      kt[2 * g] = b;
+      kt[2 * g + 1] = c4[i];
+    }
+    b += c4[i];
   }
 }
 
@@ -501,7 +524,7 @@ hipError_t launch_layer_backward(const BwdProblem& b, hipStream_t stream) {
     const int mtk = max_tiles_for(rows_max, G, kKT);
     const int ldk = mtk * kKT;
     if ((e = launch_build_tiles(b.grp_offsets, G, kKT, mtk, b.ktiles, stream)) != hipSuccess) return e;
-    hipLaunchKernelGGL(group_ktiles_kernel, dim3(1), dim3(1), 0, stream, b.grp_offsets, G, b.kt);
+    hipLaunchKernelGGL(group_ktiles_kernel, dim3(1), dim3(256), 0, stream, b.grp_offsets, G, b.kt);
     auto ktr = [&](const uint16_t* src, int C, const int32_t* gather, uint16_t* dst) {
       hipLaunchKernelGGL(ktile_transpose_kernel, dim3(C / kKtCols, mtk), dim3(256), 0, stream, src, C,
                          b.ktiles, mtk, b.grp_offsets, rows_max, gather, n_ident, K, ldk, dst);

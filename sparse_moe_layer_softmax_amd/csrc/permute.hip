@@ -44,27 +44,37 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(
     int32_t* __restrict__ row_to_slot, int32_t* __restrict__ ext_offsets, int n_ident, int nblk,
     int E, int TK, int capacity) {
   __shared__ int sk[kMaxE + 1];
-  const int e = threadIdx.x;
+  __shared__ int wsum[kMaxE / 64];
+  const int e = threadIdx.x;  // one expert per thread (blockDim = kMaxE >= E)
   int kept = 0;
   if (e < E) {
     int run = 0;
-    // block_counts reads are independent of the running sum, so they pipeline
+    // block_counts reads are independent of the running sum: unrolled, eight are in flight
+#pragma unroll 8
     for (int b = 0; b < nblk; ++b) {
       const int c = block_counts[static_cast<size_t>(b) * E + e];
       block_base[static_cast<size_t>(b) * E + e] = run;
       run += c;
     }
     kept = (capacity > 0 && run > capacity) ? capacity : run;
-    sk[e] = kept;
   }
+  // exclusive scan of the kept counts over the experts: lanes by shuffles, wavefronts through LDS
+  // (integer sums, so the result does not depend on the order)
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = kept;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(inc, d);
+    if (lane >= d) inc += o;
+  }
+  if (lane == 63) wsum[w] = inc;
   __syncthreads();
+  int excl = inc - kept;
+  for (int j = 0; j < w; ++j) excl += wsum[j];
+  if (e < E) sk[e] = excl;
   if (threadIdx.x == 0) {
     int acc = 0;
-    for (int i = 0; i < E; ++i) {
-      const int c = sk[i];
-      sk[i] = acc;
-      acc += c;
-    }
+    for (int j = 0; j < kMaxE / 64; ++j) acc += wsum[j];
     sk[E] = acc;
   }
   __syncthreads();
@@ -246,7 +256,7 @@ hipError_t launch_permute(const moe_shape& s, const int32_t* topk_idx, int32_t* 
   const int nblk = permute_blocks(TK);
   hipLaunchKernelGGL(permute_hist_kernel, dim3(nblk), dim3(256), 0, stream, topk_idx,
                      block_counts, TK, s.E, chunk);
-  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(256), 0, stream, block_counts, block_base,
+  hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kMaxE), 0, stream, block_counts, block_base,
                      counts, offsets, row_to_slot, ext_offsets, n_ident, nblk, s.E, TK,
                      s.capacity);
   hipLaunchKernelGGL(permute_scatter_kernel, dim3(nblk), dim3(64), 0, stream, topk_idx,
